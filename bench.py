@@ -1,0 +1,260 @@
+"""Benchmark: blockwise FP8 quantization throughput on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic weights:
+by default the 36-layer Qwen3-8B-shaped dense weight set (252 BF16 tensors,
+6.95e9 values, 13.9 GB), quantized at block [128,128] in ONE grouped launch
+(``fp8bq_quantize_many``), inputs already resident in HBM.
+
+Reported value: algorithmic GB/s = (2 B read + 1 B written per element +
+4 B per tile scale) / step time.  The JSON line also carries:
+  roofline      the grouped kernel's achieved bytes per launch / its mean
+                launch time (HIP events on the launch stream) vs 8 TB/s;
+                `traffic` is the HBM byte count (FETCH_SIZE + WRITE_SIZE,
+                scaled by a copy-kernel calibration) from the committed
+                counter profile, or null if that profile is for other code;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same
+                workload (one layer), on this host.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+                       [--workload dense|dense-layer|moe|ragged]
+                       [--no-cpu-baseline] [--calibrate-copy]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0
+METRIC = "blockwise FP8 quantize GB/s (bf16 in + fp8/scale out), % of HBM peak, 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_group_t128_dense36_traffic.md")
+KERNEL_SOURCES = ("fp8_blockwise_weight_amd/csrc/kernels.hpp", "fp8_blockwise_weight_amd/csrc/fp8bq.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(M, N, bm, bn):
+    TM, TN = -(-M // bm), -(-N // bn)
+    return 3 * M * N + 4 * TM * TN
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = None
+    with open(TRAFFIC_FILE, encoding="utf-8") as f:
+        for line in f:
+            if line.startswith("TRAFFIC_JSON "):
+                rec = json.loads(line[len("TRAFFIC_JSON "):])
+    if not rec or rec.get("kernel_sha") != kernel_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def build_workload(name, dev):
+    import torch  # noqa: F401
+    from fp8_blockwise_weight_amd import workloads as wl
+
+    if name == "dense":
+        groups = [wl.c3()]
+        block = (128, 128)
+        desc = "qwen3-8b-shaped dense stack, 36 layers x 7 linears (252 tensors)"
+    elif name == "dense-layer":
+        groups = [wl.c2()]
+        block = (128, 128)
+        desc = "one qwen3-8b-shaped decoder layer (7 tensors)"
+    elif name == "moe":
+        groups = [wl.c4_layer(layer) for layer in range(wl.MOE_LAYERS)]
+        block = (128, 128)
+        desc = "moe 48 layers x 128 experts (w13 1536x2048, down 2048x768), one launch per layer"
+    elif name == "ragged":
+        groups = [[sp] for sp in wl.c5()]
+        block = (128, 128)
+        desc = "ragged 1000x3000, 4097x11008, 151937x4096, 77x128, one launch each"
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    return groups, block, desc
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dense")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain device copy of known size (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(tiles are independent, so a multi-GPU run would shard rows on tile boundaries "
+              "with no exchange)", file=sys.stderr)
+        sys.exit(2)
+
+    import ctypes
+
+    import torch
+
+    import fp8_blockwise_weight_amd as fq
+
+    lib = fq.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    groups, (bm, bn), desc = build_workload(args.workload, dev)
+    from fp8_blockwise_weight_amd import workloads as wl
+
+    t0 = time.perf_counter()
+    calls = []       # (entries, count, workspace) per launch
+    keep = []        # tensors kept alive
+    total_bytes = 0
+    n_elems = 0
+    n_tensors = 0
+    for specs in groups:
+        xs = [wl.materialize(sp, dev) for sp in specs]
+        outs = [(torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=dev),
+                 torch.empty(fq.scale_shape(*x.shape, bm, bn), dtype=torch.float32, device=dev))
+                for x in xs]
+        ws = torch.empty(max(fq.workspace_bytes(len(xs)), 1), dtype=torch.uint8, device=dev)
+        arr = fq.make_entries(xs, outs)
+        calls.append((arr, len(xs), ws))
+        keep.append((xs, outs))
+        for sp in specs:
+            total_bytes += algorithmic_bytes(sp.M, sp.N, bm, bn)
+            n_elems += sp.M * sp.N
+        n_tensors += len(specs)
+    torch.cuda.synchronize()
+    log(f"generated {n_tensors} tensors, {n_elems / 1e9:.3f} G values in {time.perf_counter() - t0:.1f}s")
+
+    stream = torch.cuda.current_stream(dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def step():
+        for arr, count, ws in calls:
+            st = lib.fp8bq_quantize_many(arr, count, bm, bn, ws.data_ptr(), ws.numel(), sptr)
+            if st != 0:
+                raise RuntimeError(f"fp8bq_quantize_many failed: status {st}, "
+                                   f"hip error {lib.fp8bq_last_hip_error()}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Per-step HIP events on the launch stream, and the wall clock around all steps.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ev_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    launches = len(calls)
+    mean_launch_ms = sum(ev_ms) / len(ev_ms) / launches
+    bytes_per_launch = total_bytes / launches
+    achieved = bytes_per_launch / (mean_launch_ms * 1e-3) / 1e9
+    value = total_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"steps {args.steps}: wall {ms_per_step:.3f} ms/step, events mean {sum(ev_ms) / len(ev_ms):.3f} "
+        f"min {min(ev_ms):.3f} max {max(ev_ms):.3f} ms; {value:.1f} GB/s = {100 * value / HBM_PEAK_GBS:.1f}% of peak")
+
+    if args.calibrate_copy:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters
+        # calibrate the quantizer's counters (bytes per counted KiB).
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 3 x 1 GiB device-to-device")
+
+    traffic = committed_traffic()
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "kernel": f"fp8bq::quantize_group<kT128> ({'one launch' if launches == 1 else f'{launches} launches'} per step)",
+        "bytes_per_launch": bytes_per_launch,
+        "mean_launch_ms": round(mean_launch_ms, 4),
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(keep[0][0][:7], groups[0][:7], bm, bn)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": desc,
+            "tensors": n_tensors,
+            "elements": n_elems,
+            "block": [bm, bn],
+            "launches_per_step": launches,
+            "algorithmic_bytes_per_step": total_bytes,
+            "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(xs, specs, bm, bn):
+    """The CPU oracle (as it is, single process) on one layer of the workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    host = [x.view(torch.int16).cpu().numpy().view(np.uint16) for x in xs]
+    nbytes = sum(algorithmic_bytes(sp.M, sp.N, bm, bn) for sp in specs)
+    nel = sum(sp.M * sp.N for sp in specs)
+    t0 = time.perf_counter()
+    for h in host:
+        oracle.quantize(h, bm, bn)
+    dt = time.perf_counter() - t0
+    log(f"cpu oracle: {len(host)} tensors, {nel / 1e6:.1f} M values in {dt:.1f}s")
+    return {
+        "value": round(nbytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{len(host)} tensors ({nel} values) of the benchmarked workload "
+                  f"(first layer), numpy oracle in one process, {dt:.1f} s",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,222 @@
+"""Python binding of libfp8bq (blockwise FP8 e4m3fn weight quantization, gfx950).
+
+Argument marshalling only: every step of the quantization runs in the HIP
+kernels of ``libfp8bq.so``.  PyTorch supplies device memory and the current
+stream.  There is no fallback: if the library is missing or the device is
+not a gfx950, the calls raise.
+
+The entry point mirrors ``scaled_fp8_blockwise(data_hp, weight_block_size)``
+of the page "fp8_kernel.py — FP8 量化内核" (section 1): an [M, N] matrix
+and a [BLOCK_M, BLOCK_N] block size in, ``(fp8_data, descale)`` out, with the
+descale shaped [ceil(M/bm), ceil(N/bn)].  ``quantize_many`` is the grouped
+form of the per-weight loop of the page "vllm_fp8_utils.py" (section 3).
+"""
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8bq.so")
+
+# Status codes of include/fp8bq.h
+OK = 0
+ERR_INVALID_ARGUMENT = 1
+ERR_UNSUPPORTED_DEVICE = 2
+ERR_WORKSPACE = 3
+ERR_HIP = 4
+
+E4M3_MAX = 448.0
+EPS = 1e-10
+
+# Every symbol include/fp8bq.h declares.
+EXPORTS = (
+    "fp8bq_quantize",
+    "fp8bq_many_workspace_bytes",
+    "fp8bq_quantize_many",
+    "fp8bq_encode_e4m3",
+    "fp8bq_status_string",
+    "fp8bq_last_hip_error",
+)
+
+
+class TensorEntry(ctypes.Structure):
+    """``fp8bq_tensor`` of include/fp8bq.h."""
+
+    _fields_ = [
+        ("x", ctypes.c_void_p),
+        ("q", ctypes.c_void_p),
+        ("scale_inv", ctypes.c_void_p),
+        ("M", ctypes.c_int64),
+        ("N", ctypes.c_int64),
+    ]
+
+
+class Fp8bqError(RuntimeError):
+    def __init__(self, where: str, status: int, hip_error: int):
+        self.status = status
+        self.hip_error = hip_error
+        text = load_library().fp8bq_status_string(status).decode()
+        super().__init__(f"{where}: {text} (status {status}, hip error {hip_error})")
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libfp8bq.so (built in-tree by ``fp8_blockwise_weight_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m fp8_blockwise_weight_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback implementation")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_i32, c_i64, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    lib.fp8bq_quantize.argtypes = [c_vp, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp]
+    lib.fp8bq_quantize.restype = ctypes.c_int
+    lib.fp8bq_many_workspace_bytes.argtypes = [c_i32]
+    lib.fp8bq_many_workspace_bytes.restype = ctypes.c_size_t
+    lib.fp8bq_quantize_many.argtypes = [ctypes.POINTER(TensorEntry), c_i32, c_i32, c_i32, c_vp,
+                                        ctypes.c_size_t, c_vp]
+    lib.fp8bq_quantize_many.restype = ctypes.c_int
+    lib.fp8bq_encode_e4m3.argtypes = [c_vp, c_vp, c_i64, c_vp]
+    lib.fp8bq_encode_e4m3.restype = ctypes.c_int
+    lib.fp8bq_status_string.argtypes = [ctypes.c_int]
+    lib.fp8bq_status_string.restype = ctypes.c_char_p
+    lib.fp8bq_last_hip_error.argtypes = []
+    lib.fp8bq_last_hip_error.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(where: str, status: int) -> None:
+    if status != OK:
+        raise Fp8bqError(where, status, load_library().fp8bq_last_hip_error())
+
+
+def block_shape(block_size) -> Tuple[int, int]:
+    """Validate a block size: the SGLang loop raises when it is missing."""
+    if block_size is None:
+        raise ValueError("weight_block_size is required (got None)")
+    bm, bn = (int(v) for v in block_size)
+    if bm < 1 or bn < 1:
+        raise ValueError(f"block size must be positive, got {tuple(block_size)}")
+    return bm, bn
+
+
+def scale_shape(M: int, N: int, bm: int, bn: int) -> Tuple[int, int]:
+    return (-(-M // bm), -(-N // bn))
+
+
+def _check_input(x) -> None:
+    import torch
+
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise TypeError("x must be a 2-D torch.bfloat16 tensor")
+    if not x.is_cuda:
+        raise TypeError("x must be on a GPU (there is no CPU implementation)")
+    if not x.is_contiguous():
+        raise TypeError("x must be contiguous row-major")
+
+
+def _stream(device) -> int:
+    import torch
+
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def quantize(x, block_size=(128, 128), out=None):
+    """Quantize one BF16 [M, N] GPU tensor.
+
+    Returns ``(q, scale_inv)``: ``q`` is torch.float8_e4m3fn [M, N] and
+    ``scale_inv`` float32 [ceil(M/bm), ceil(N/bn)]; dequantize with
+    ``q.float() * scale_inv`` expanded over each block.  ``out`` may supply
+    preallocated ``(q, scale_inv)``.  Work is enqueued on the current stream.
+    """
+    import torch
+
+    bm, bn = block_shape(block_size)
+    _check_input(x)
+    M, N = x.shape
+    if out is None:
+        q = torch.empty((M, N), dtype=torch.float8_e4m3fn, device=x.device)
+        s = torch.empty(scale_shape(M, N, bm, bn), dtype=torch.float32, device=x.device)
+    else:
+        q, s = out
+    lib = load_library()
+    with torch.cuda.device(x.device):
+        _check("fp8bq_quantize",
+               lib.fp8bq_quantize(x.data_ptr(), M, N, bm, bn, q.data_ptr(), s.data_ptr(),
+                                  _stream(x.device)))
+    return q, s
+
+
+def workspace_bytes(count: int) -> int:
+    return int(load_library().fp8bq_many_workspace_bytes(int(count)))
+
+
+def make_entries(tensors: Sequence, outputs: Sequence) -> ctypes.Array:
+    arr = (TensorEntry * len(tensors))()
+    for i, (x, (q, s)) in enumerate(zip(tensors, outputs)):
+        arr[i].x = x.data_ptr()
+        arr[i].q = q.data_ptr()
+        arr[i].scale_inv = s.data_ptr()
+        arr[i].M, arr[i].N = x.shape
+    return arr
+
+
+def quantize_many(tensors: Sequence, block_size=(128, 128), outputs: Optional[Sequence] = None,
+                  workspace=None) -> List:
+    """Quantize a list of BF16 GPU tensors (same device, one block size) in one launch.
+
+    Returns a list of ``(q, scale_inv)`` pairs in input order.  ``outputs``
+    and ``workspace`` (a uint8 GPU tensor of at least ``workspace_bytes``)
+    may be preallocated.
+    """
+    import torch
+
+    bm, bn = block_shape(block_size)
+    tensors = list(tensors)
+    if not tensors:
+        return []
+    dev = tensors[0].device
+    for x in tensors:
+        _check_input(x)
+        if x.device != dev:
+            raise ValueError("all tensors of one grouped call must be on the same device")
+    if outputs is None:
+        outputs = [(torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=dev),
+                    torch.empty(scale_shape(*x.shape, bm, bn), dtype=torch.float32, device=dev))
+                   for x in tensors]
+    need = workspace_bytes(len(tensors))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    arr = make_entries(tensors, outputs)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _check("fp8bq_quantize_many",
+               lib.fp8bq_quantize_many(arr, len(tensors), bm, bn, workspace.data_ptr(),
+                                       workspace.numel(), _stream(dev)))
+    return list(outputs)
+
+
+def encode_e4m3(y):
+    """The final cast alone: float32 GPU tensor -> e4m3fn codes (uint8), clamped to +-448."""
+    import torch
+
+    if y.dtype != torch.float32 or not y.is_cuda or not y.is_contiguous():
+        raise TypeError("y must be a contiguous float32 GPU tensor")
+    q = torch.empty(y.shape, dtype=torch.uint8, device=y.device)
+    with torch.cuda.device(y.device):
+        _check("fp8bq_encode_e4m3",
+               load_library().fp8bq_encode_e4m3(y.data_ptr(), q.data_ptr(), y.numel(),
+                                                _stream(y.device)))
+    return q
+
+
+__all__ = [
+    "EXPORTS", "Fp8bqError", "TensorEntry", "block_shape", "encode_e4m3", "load_library",
+    "make_entries", "quantize", "quantize_many", "scale_shape", "workspace_bytes",
+]

@@ -1,0 +1,346 @@
+// Device code of fp8bq: blockwise BF16 -> OCP e4m3fn quantization for gfx950.
+//
+// The arithmetic is the blockwise cast of the page "fp8_kernel.py — FP8 量化内核"
+// (section 2, Triton implementation): per tile, a = max(max|x|, eps),
+// s = a/448 (stored), r = 1/s, q = e4m3fn(clamp(x*r, -448, 448)).
+//
+// Work decomposition (one 256-thread workgroup = 4 wave64s per work unit):
+//   * every thread owns 16-byte column chunks (8 BF16 values) of a unit that
+//     is 128 columns wide: 16 threads cover one 256-byte row segment, so a
+//     wave's load touches 4 rows x 256 contiguous bytes and its 8-byte FP8
+//     store writes 4 rows x 128 contiguous bytes (whole cache lines);
+//   * [128,128] blocks: unit = one tile (8 loads per thread, all held in
+//     registers: the tile is read from HBM exactly once);
+//   * [64,64] blocks: unit = 64 x 128 = two side-by-side tiles, so the FP8
+//     rows written are still full 128-byte lines;
+//   * [1,128] blocks: unit = 64 rows x 128 = 64 row-tiles; each tile's
+//     maximum is reduced inside one 16-lane DPP row, with no LDS and no
+//     barrier;
+//   * any other block size, N % 8 != 0 or a misaligned pointer: one tile per
+//     unit, element by element (two passes over the tile), same arithmetic.
+//
+// The tile maximum is an integer max over (bits & 0x7FFF): for finite BF16
+// values magnitude order equals bit-pattern order, so this is exact.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8bq {
+
+constexpr float kE4m3Max = 448.0f;
+constexpr float kEps = 1e-10f;
+constexpr int kThreads = 256;
+
+enum Kind : int { kT128 = 0, kT64 = 1, kR128 = 2, kGeneral = 3 };
+
+// Pointers into device memory, marked as global so loads and stores are
+// emitted as global_* (not flat_*) instructions.
+#define FP8BQ_GLOBAL __attribute__((address_space(1)))
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// One tensor as the kernels see it.
+struct Desc {
+  const uint16_t* x;  // BF16 [M, N]
+  uint8_t* q;         // e4m3fn [M, N]
+  float* s;           // fp32 [TM, TN]
+  int64_t M;
+  int64_t N;
+  int32_t TN;       // tile columns: row pitch of s
+  int32_t UN;       // work-unit columns
+  int32_t general;  // 1: this tensor takes the element-wise tile body
+  int32_t pad;
+  int64_t reserved;  // pads the entry to 64 bytes
+};
+static_assert(sizeof(Desc) == 64, "descriptor layout is part of the workspace format");
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  u16x2 x = __builtin_bit_cast(u16x2, a);
+  u16x2 y = __builtin_bit_cast(u16x2, b);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, y));
+}
+
+// Packed magnitudes of the 8 BF16 values of a chunk, folded to two u16 maxima.
+__device__ __forceinline__ uint32_t fold_abs(u32x4 w) {
+  constexpr uint32_t kMag = 0x7FFF7FFFu;
+  uint32_t a = pk_max_u16(w.x & kMag, w.y & kMag);
+  uint32_t b = pk_max_u16(w.z & kMag, w.w & kMag);
+  return pk_max_u16(a, b);
+}
+
+__device__ __forceinline__ uint32_t halves_max(uint32_t m) {
+  return max(m & 0xFFFFu, m >> 16);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
+  int o = __builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  return max(v, (uint32_t)o);
+}
+
+// Max over each aligned group of 8 lanes (quad swaps, then half-row mirror).
+__device__ __forceinline__ uint32_t max8(uint32_t v) {
+  v = dpp_max<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max<0x141>(v);  // row_half_mirror
+  return v;
+}
+
+// Max over each 16-lane DPP row.
+__device__ __forceinline__ uint32_t max16(uint32_t v) {
+  return dpp_max<0x140>(max8(v));  // row_mirror
+}
+
+// Max of lanes L, L+16, L+32, L+48 (one value per DPP row), as a uniform value.
+template <int L>
+__device__ __forceinline__ uint32_t rows_max(uint32_t v) {
+  uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, L);
+  uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, L + 16);
+  uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, L + 32);
+  uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, L + 48);
+  return max(max(a, b), max(c, d));
+}
+
+// Scale and reciprocal from the tile's maximum magnitude bits: two correctly
+// rounded binary32 divisions (this file is built without fast-math).
+__device__ __forceinline__ void tile_scale(uint32_t maxbits, float& s, float& r) {
+  const float amax = __uint_as_float(maxbits << 16);
+  const float a = fmaxf(amax, kEps);
+  s = a / kE4m3Max;
+  r = 1.0f / s;
+}
+
+__device__ __forceinline__ float clamp448(float y) {
+  return __builtin_amdgcn_fmed3f(y, -kE4m3Max, kE4m3Max);
+}
+
+// Four clamped values -> four e4m3fn bytes (byte i = value i).
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+  return (uint32_t)v;
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// 8 BF16 values (one 16-byte chunk) -> 8 e4m3fn bytes.
+__device__ __forceinline__ u32x2 quant8(u32x4 w, float r) {
+  u32x2 o;
+  o.x = cvt4(clamp448(bf_lo(w.x) * r), clamp448(bf_hi(w.x) * r),
+             clamp448(bf_lo(w.y) * r), clamp448(bf_hi(w.y) * r));
+  o.y = cvt4(clamp448(bf_lo(w.z) * r), clamp448(bf_hi(w.z) * r),
+             clamp448(bf_lo(w.w) * r), clamp448(bf_hi(w.w) * r));
+  return o;
+}
+
+// ---------------------------------------------------------------- unit bodies
+
+template <int KIND>
+struct UnitShape {
+  static constexpr int kRows = (KIND == kT128) ? 128 : 64;  // unit rows
+  static constexpr int kLoads = kRows / 16;                 // 16-byte loads per thread
+};
+
+// Vectorized unit (ur, uc) of a [128,128], [64,64] or [1,128] tensor.
+// CHECK = the unit crosses the bottom or right edge of the matrix.
+// Needs N % 8 == 0, x 16-byte and q 8-byte aligned.
+template <int KIND, bool CHECK>
+__device__ __forceinline__ void vec_unit(const Desc& d, int64_t ur, int64_t uc, uint32_t* red) {
+  constexpr int R = UnitShape<KIND>::kRows;
+  constexpr int L = UnitShape<KIND>::kLoads;
+  const int t = threadIdx.x;
+  const int chunk = t & 15;   // 16-byte column chunk within the unit
+  const int prow = t >> 4;    // row within a 16-row pass
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int64_t N = d.N;
+  const int64_t row0 = ur * R;
+  const int64_t col = uc * 128 + chunk * 8;
+  int rows_valid = R;
+  bool col_ok = true;
+  if (CHECK) {
+    const int64_t left = d.M - row0;
+    rows_valid = left < R ? (int)left : R;
+    col_ok = col < N;  // N % 8 == 0: a chunk is wholly inside or outside
+  }
+  const size_t base = (size_t)(row0 + prow) * (size_t)N + (size_t)col;
+  const FP8BQ_GLOBAL u32x4* xp = (const FP8BQ_GLOBAL u32x4*)(d.x + base);
+  const size_t pitch16 = (size_t)N * 16 / 8;  // 16 rows, in 16-byte chunks
+
+  u32x4 v[L];
+#pragma unroll
+  for (int k = 0; k < L; ++k) {
+    if (!CHECK || (col_ok && k * 16 + prow < rows_valid)) {
+      v[k] = xp[k * pitch16];
+    } else {
+      v[k] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  FP8BQ_GLOBAL u32x2* qp = (FP8BQ_GLOBAL u32x2*)(d.q + base);
+  FP8BQ_GLOBAL float* sp = (FP8BQ_GLOBAL float*)d.s;
+  const size_t qpitch16 = (size_t)N * 16 / 8;  // 16 rows, in 8-byte chunks
+
+  if constexpr (KIND == kR128) {
+    // Every 16-lane row holds one row-tile: reduce inside the DPP row.
+#pragma unroll
+    for (int k = 0; k < L; ++k) {
+      const uint32_t m = max16(halves_max(fold_abs(v[k])));
+      float s, r;
+      tile_scale(m, s, r);
+      const bool row_ok = !CHECK || k * 16 + prow < rows_valid;
+      if (row_ok && (!CHECK || col_ok)) qp[k * qpitch16] = quant8(v[k], r);
+      if (chunk == 0 && row_ok) sp[(size_t)(row0 + k * 16 + prow) * d.TN + uc] = s;
+    }
+  } else {
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < L; ++k) m = pk_max_u16(m, fold_abs(v[k]));
+    m = halves_max(m);
+    uint32_t tm;
+    if constexpr (KIND == kT128) {
+      m = max16(m);
+      const uint32_t wm = rows_max<0>(m);
+      if (lane == 0) red[wave] = wm;
+      __syncthreads();
+      tm = max(max(red[0], red[1]), max(red[2], red[3]));
+    } else {  // kT64: left tile = chunks 0..7, right tile = chunks 8..15
+      m = max8(m);
+      const uint32_t w0 = rows_max<0>(m);
+      const uint32_t w1 = rows_max<8>(m);
+      if (lane == 0) {
+        red[wave * 2] = w0;
+        red[wave * 2 + 1] = w1;
+      }
+      __syncthreads();
+      const int h = chunk >> 3;
+      tm = max(max(red[h], red[2 + h]), max(red[4 + h], red[6 + h]));
+    }
+    float s, r;
+    tile_scale(tm, s, r);
+#pragma unroll
+    for (int k = 0; k < L; ++k) {
+      if (!CHECK || (col_ok && k * 16 + prow < rows_valid)) qp[k * qpitch16] = quant8(v[k], r);
+    }
+    if constexpr (KIND == kT128) {
+      if (t == 0) sp[(size_t)ur * d.TN + uc] = s;
+    } else {
+      const int64_t tj = uc * 2 + (chunk >> 3);
+      if ((t == 0 || t == 8) && tj < d.TN) sp[(size_t)ur * d.TN + tj] = s;
+    }
+  }
+}
+
+// Element-wise tile body: any block size, any alignment.  Pass 1 takes the
+// maximum, pass 2 re-reads the tile and writes one byte per element.
+__device__ __forceinline__ void general_tile(const Desc& d, int32_t bm, int32_t bn, int64_t ti,
+                                             int64_t tj, uint32_t* red) {
+  const int t = threadIdx.x;
+  const int64_t r0 = ti * bm;
+  const int64_t c0 = tj * bn;
+  const int64_t rows = (d.M - r0) < bm ? (d.M - r0) : bm;
+  const int64_t cols = (d.N - c0) < bn ? (d.N - c0) : bn;
+  const int64_t n = rows * cols;
+  const FP8BQ_GLOBAL uint16_t* x = (const FP8BQ_GLOBAL uint16_t*)(d.x + (size_t)r0 * d.N + c0);
+  uint32_t m = 0;
+  for (int64_t e = t; e < n; e += kThreads) {
+    const int64_t rr = e / cols;
+    const int64_t cc = e - rr * cols;
+    m = max(m, (uint32_t)(x[(size_t)rr * d.N + cc] & 0x7FFFu));
+  }
+  m = max16(m);
+  const uint32_t wm = rows_max<0>(m);
+  if ((t & 63) == 0) red[t >> 6] = wm;
+  __syncthreads();
+  const uint32_t tm = max(max(red[0], red[1]), max(red[2], red[3]));
+  float s, r;
+  tile_scale(tm, s, r);
+  if (t == 0) ((FP8BQ_GLOBAL float*)d.s)[(size_t)ti * d.TN + tj] = s;
+  FP8BQ_GLOBAL uint8_t* q = (FP8BQ_GLOBAL uint8_t*)(d.q + (size_t)r0 * d.N + c0);
+  for (int64_t e = t; e < n; e += kThreads) {
+    const int64_t rr = e / cols;
+    const int64_t cc = e - rr * cols;
+    const size_t off = (size_t)rr * d.N + cc;
+    const float y = clamp448(__uint_as_float((uint32_t)x[off] << 16) * r);
+    q[off] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xFF);
+  }
+}
+
+template <int KIND>
+__device__ __forceinline__ void run_unit(const Desc& d, int32_t bm, int32_t bn, int64_t u,
+                                         uint32_t* red) {
+  // Units per tensor are < 2^31 (checked on the host): 32-bit division.
+  const uint32_t uu = (uint32_t)u;
+  const uint32_t un = (uint32_t)d.UN;
+  const uint32_t ur = uu / un;
+  const uint32_t uc = uu - ur * un;
+  if (KIND == kGeneral || d.general) {
+    general_tile(d, bm, bn, ur, uc, red);
+    return;
+  }
+  if constexpr (KIND != kGeneral) {
+    constexpr int R = UnitShape<KIND>::kRows;
+    const bool inside = (int64_t)(ur + 1) * R <= d.M && (int64_t)(uc + 1) * 128 <= d.N;
+    if (inside) {
+      vec_unit<KIND, false>(d, ur, uc, red);
+    } else {
+      vec_unit<KIND, true>(d, ur, uc, red);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- kernels
+
+// One tensor: unit u -> (unit row, unit column) of d.  Grid-stride, so any
+// grid size is correct; LDS scratch alternates between two slots so one
+// barrier per unit suffices.
+template <int KIND>
+__global__ __launch_bounds__(kThreads) void quantize_one(Desc d, int32_t bm, int32_t bn,
+                                                         int64_t total) {
+  __shared__ uint32_t red[2][8];
+  int it = 0;
+  for (int64_t u = blockIdx.x; u < total; u += gridDim.x, ++it) {
+    run_unit<KIND>(d, bm, bn, u, red[it & 1]);
+  }
+}
+
+// A list of tensors: start[t] is the first global unit of tensor t
+// (start[0] = 0, strictly increasing: empty tensors are not listed).
+template <int KIND>
+__global__ __launch_bounds__(kThreads) void quantize_group(const Desc* __restrict__ descs,
+                                                           const int64_t* __restrict__ start,
+                                                           int32_t count, int32_t bm, int32_t bn,
+                                                           int64_t total) {
+  __shared__ uint32_t red[2][8];
+  int it = 0;
+  for (int64_t u = blockIdx.x; u < total; u += gridDim.x, ++it) {
+    int lo = 0, hi = count - 1;  // largest t with start[t] <= u
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (start[mid] <= u) {
+        lo = mid;
+      } else {
+        hi = mid - 1;
+      }
+    }
+    const Desc d = descs[lo];
+    run_unit<KIND>(d, bm, bn, u - start[lo], red[it & 1]);
+  }
+}
+
+// The final cast alone: clamp and convert n floats.
+__global__ __launch_bounds__(kThreads) void encode_e4m3(const float* __restrict__ y,
+                                                        uint8_t* __restrict__ q, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
+    q[i] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(y[i]), 0.0f, 0, false) & 0xFF);
+  }
+}
+
+}  // namespace fp8bq

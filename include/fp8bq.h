@@ -1,0 +1,137 @@
+/*
+ * fp8bq — blockwise FP8 (OCP e4m3fn) weight quantization for AMD MI355X (gfx950).
+ *
+ * The operation is the blockwise cast on the documentation page
+ * "fp8_kernel.py — FP8 量化内核" (verl/utils/kernel/fp8_kernel.py):
+ *   - section 1, unified entry point: [M, N] high-precision data and a
+ *     [BLOCK_M, BLOCK_N] block size in, FP8 data and a descale per block out;
+ *   - section 2, Triton implementation: per block, amax = max(max|x|, eps),
+ *     s = amax / 448, q = clamp(x * (1/s), -448, 448) cast to float8_e4m3fn,
+ *     s stored as the descale.
+ * The grouped call serves the streaming loop of the page "vllm_fp8_utils.py"
+ * (section 3, quant_weights), which quantizes a list of weights with one
+ * block size and pairs each weight with a "<name>_scale_inv" tensor.
+ *
+ * Arithmetic (bit-exact, deterministic):
+ *   a = max(amax, FP8BQ_EPS)      amax over the tile's valid elements (exact)
+ *   s = a / 448                   correctly rounded binary32 division
+ *   r = 1 / s                     correctly rounded binary32 division
+ *   y = x * r                     binary32, round to nearest even
+ *   q = e4m3fn(clamp(y, -448, 448))   round to nearest even, sign kept
+ *
+ * Conventions for every call:
+ *   - All data pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or synchronizes on these calls; work is
+ *     enqueued on `stream` (a hipStream_t; NULL means the null stream) and
+ *     results are ready when that stream reaches the call.
+ *   - x is BF16, contiguous row-major [M, N] (row pitch N elements).
+ *   - q is one byte per element, contiguous row-major [M, N]; every byte is
+ *     written.  Bytes are OCP e4m3fn codes (torch.float8_e4m3fn); 0x7F and
+ *     0xFF (NaN) are never produced for finite input.
+ *   - scale_inv is fp32, contiguous row-major [ceil(M/bm), ceil(N/bn)];
+ *     every entry is written.  Dequantization is decode(q) * scale_inv.
+ *   - Outputs must not overlap each other or x (checked per tensor).
+ *   - Non-finite input (NaN, Inf) is outside the contract; the output for
+ *     such a tile is unspecified but every write stays inside q/scale_inv.
+ *   - M == 0 or N == 0 (or count == 0) returns FP8BQ_OK without touching
+ *     the device.
+ *   - All argument checks run before any HIP call.  The first compute call
+ *     on a device checks that it is a gfx950 (the capability check the
+ *     relations section of the fp8_kernel.py page delegates to device.py).
+ *   - Any block size bm, bn >= 1 and any alignment are accepted.  Blocks
+ *     [128,128], [64,64] and [1,128] with N % 8 == 0, a 16-byte aligned x
+ *     and an 8-byte aligned q take the vectorized kernels; everything else
+ *     takes a general tile kernel with identical results.
+ *   - Thread safety: calls may be made from several host threads; each
+ *     thread has its own fp8bq_last_hip_error().
+ */
+#ifndef FP8BQ_H
+#define FP8BQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8BQ_E4M3_MAX 448.0f
+/* Floor of the tile maximum.  The page names eps without a value; 1e-10 is
+ * the value this library uses (an all-zero tile gets scale fl32(eps/448)). */
+#define FP8BQ_EPS 1e-10f
+
+enum fp8bq_status {
+  FP8BQ_OK = 0,
+  FP8BQ_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bm/bn < 1, overlap, size overflow */
+  FP8BQ_ERR_UNSUPPORTED_DEVICE = 2, /* the current device is not a gfx950 */
+  FP8BQ_ERR_WORKSPACE = 3,        /* workspace null, too small or not 16-byte aligned */
+  FP8BQ_ERR_HIP = 4               /* a HIP call failed; see fp8bq_last_hip_error() */
+};
+
+/*
+ * Quantize one BF16 matrix.
+ *   x          device, BF16 [M, N] row-major
+ *   M, N       rows and columns (>= 0, each < 2^31)
+ *   bm, bn     block rows and columns (>= 1); [128,128] is the weight
+ *              default, [1,128] the per-row-group (activation-style) shape
+ *   q          device, uint8 [M, N] row-major (e4m3fn codes)
+ *   scale_inv  device, fp32 [ceil(M/bm), ceil(N/bn)] row-major
+ *   stream     hipStream_t to enqueue on (NULL = null stream)
+ * Returns an fp8bq_status.
+ */
+int fp8bq_quantize(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn,
+                   void* q, float* scale_inv, void* stream);
+
+/* One entry of a grouped call (fields as in fp8bq_quantize). */
+typedef struct fp8bq_tensor {
+  const void* x;
+  void* q;
+  float* scale_inv;
+  int64_t M;
+  int64_t N;
+} fp8bq_tensor;
+
+/* Device workspace bytes fp8bq_quantize_many needs for `count` tensors
+ * (0 for count <= 0). */
+size_t fp8bq_many_workspace_bytes(int32_t count);
+
+/*
+ * Quantize a list of BF16 matrices that share one block size, in one kernel
+ * launch (the grouped form of the per-weight loop).
+ *   list             HOST array of `count` entries; it is copied into
+ *                    `workspace` on `stream` before the call returns, so the
+ *                    caller may reuse or free it afterwards
+ *   count            number of entries (>= 0)
+ *   bm, bn           block size shared by every entry
+ *   workspace        device buffer of at least
+ *                    fp8bq_many_workspace_bytes(count) bytes, 16-byte
+ *                    aligned; it must stay untouched until the launch on
+ *                    `stream` has finished
+ *   workspace_bytes  its size
+ *   stream           hipStream_t (NULL = null stream)
+ * Entries with M == 0 or N == 0 are skipped.  Outputs of different entries
+ * must not overlap each other or any entry's x (not checked across entries).
+ * Returns an fp8bq_status; on an argument error nothing is enqueued.
+ */
+int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int32_t bn,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The final cast alone (clamp to +-448, round to e4m3fn), for checking the
+ * hardware convert over every float32 input.
+ *   y  device, fp32 [n];  q  device, uint8 [n];  n >= 0.
+ */
+int fp8bq_encode_e4m3(const float* y, void* q, int64_t n, void* stream);
+
+/* Static English text for a status code (never NULL). */
+const char* fp8bq_status_string(int status);
+
+/* hipError_t of the last failed HIP call made by this thread inside the
+ * library (0 if none). */
+int fp8bq_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BQ_H */

@@ -1,0 +1,155 @@
+"""C-ABI library: loads, exports every declared symbol, and rejects every bad
+argument before touching a device (CPU only: no call here reaches a kernel).
+
+Calls with fake pointer values are all built so that an argument check
+rejects them; none of them may ever pass validation.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_blockwise_weight_amd as fq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bq.h")
+
+INVALID = fq.ERR_INVALID_ARGUMENT
+WORKSPACE = fq.ERR_WORKSPACE
+
+# Fake, never dereferenced addresses (16-byte aligned, far apart).
+X = 0x10_0000_0000
+Q = 0x20_0000_0000
+S = 0x30_0000_0000
+W = 0x40_0000_0000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fq.load_library()
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(fp8bq_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(fq.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.fp8bq_status_string(code)
+    assert lib.fp8bq_status_string(99) == b"unknown status"
+    assert lib.fp8bq_last_hip_error() == 0
+
+
+def test_workspace_bytes(lib):
+    assert lib.fp8bq_many_workspace_bytes(0) == 0
+    assert lib.fp8bq_many_workspace_bytes(-3) == 0
+    for n in (1, 7, 252, 256, 4096):
+        b = lib.fp8bq_many_workspace_bytes(n)
+        assert b >= 64 * n + 8 * (n + 1) and b % 256 == 0
+
+
+@pytest.mark.parametrize("args", [
+    (X, -1, 128, 128, 128, Q, S),          # negative M
+    (X, 128, -1, 128, 128, Q, S),          # negative N
+    (X, 128, 128, 0, 128, Q, S),           # bm < 1
+    (X, 128, 128, 128, 0, Q, S),           # bn < 1
+    (X, 128, 128, -5, 128, Q, S),
+    (None, 128, 128, 128, 128, Q, S),      # null x
+    (X, 128, 128, 128, 128, None, S),      # null q
+    (X, 128, 128, 128, 128, Q, None),      # null scale
+    (X + 1, 128, 128, 128, 128, Q, S),     # x not 2-byte aligned
+    (X, 128, 128, 128, 128, Q, S + 2),     # scale not 4-byte aligned
+    (X, 128, 128, 128, 128, X + 100, S),   # q overlaps x
+    (X, 128, 128, 128, 128, Q, X + 4),     # scale overlaps x
+    (X, 128, 128, 128, 128, Q, Q + 16),    # scale overlaps q
+    (X, 1 << 31, 8, 128, 128, Q, S),       # M too large
+    (X, 8, 1 << 31, 128, 128, Q, S),       # N too large
+    (X, 1 << 20, 1 << 20, 1, 1, Q, S),     # 2^40 tiles
+])
+def test_quantize_rejects(lib, args):
+    x, M, N, bm, bn, q, s = args
+    assert lib.fp8bq_quantize(x, M, N, bm, bn, q, s, None) == INVALID
+
+
+@pytest.mark.parametrize("M,N", [(0, 128), (128, 0), (0, 0)])
+def test_quantize_empty_is_ok_without_device(lib, M, N):
+    # Empty input: nothing to do, no device is touched (null pointers allowed).
+    assert lib.fp8bq_quantize(None, M, N, 128, 128, None, None, None) == fq.OK
+
+
+def _entries(rows):
+    arr = (fq.TensorEntry * len(rows))()
+    for i, (x, q, s, M, N) in enumerate(rows):
+        arr[i].x, arr[i].q, arr[i].scale_inv, arr[i].M, arr[i].N = x, q, s, M, N
+    return arr
+
+
+def test_quantize_many_rejects(lib):
+    good = _entries([(X, Q, S, 256, 256)])
+    need = lib.fp8bq_many_workspace_bytes(1)
+    f = lib.fp8bq_quantize_many
+    assert f(good, -1, 128, 128, W, need, None) == INVALID          # count < 0
+    assert f(None, 1, 128, 128, W, need, None) == INVALID           # null list
+    assert f(good, 1, 0, 128, W, need, None) == INVALID             # bm < 1
+    assert f(good, 1, 128, 0, W, need, None) == INVALID             # bn < 1
+    assert f(good, 1, 128, 128, None, need, None) == WORKSPACE      # null workspace
+    assert f(good, 1, 128, 128, W, need - 1, None) == WORKSPACE     # too small
+    assert f(good, 1, 128, 128, W + 8, need, None) == WORKSPACE     # misaligned
+    # one bad entry anywhere rejects the whole call
+    bad = _entries([(X, Q, S, 256, 256), (X + 0x1000000, None, S + 0x1000, 4, 4)])
+    assert f(bad, 2, 128, 128, W, lib.fp8bq_many_workspace_bytes(2), None) == INVALID
+    bad = _entries([(X, Q, S, 256, 256), (X, Q, S, -1, 4)])
+    assert f(bad, 2, 128, 128, W, lib.fp8bq_many_workspace_bytes(2), None) == INVALID
+    bad = _entries([(X, X + 64, S, 256, 256)])                     # q overlaps x
+    assert f(bad, 1, 128, 128, W, need, None) == INVALID
+
+
+def test_quantize_many_empty_is_ok_without_device(lib):
+    assert lib.fp8bq_quantize_many(None, 0, 128, 128, None, 0, None) == fq.OK
+    empty = _entries([(None, None, None, 0, 4096), (None, None, None, 7, 0)])
+    assert lib.fp8bq_quantize_many(empty, 2, 128, 128, W, lib.fp8bq_many_workspace_bytes(2),
+                                   None) == fq.OK
+
+
+def test_encode_rejects(lib):
+    assert lib.fp8bq_encode_e4m3(X, Q, -1, None) == INVALID
+    assert lib.fp8bq_encode_e4m3(None, Q, 10, None) == INVALID
+    assert lib.fp8bq_encode_e4m3(X, None, 10, None) == INVALID
+    assert lib.fp8bq_encode_e4m3(X + 2, Q, 10, None) == INVALID
+    assert lib.fp8bq_encode_e4m3(X, X + 8, 10, None) == INVALID     # overlap
+    assert lib.fp8bq_encode_e4m3(None, None, 0, None) == fq.OK
+
+
+def test_python_block_size_checks():
+    with pytest.raises(ValueError):
+        fq.block_shape(None)
+    with pytest.raises(ValueError):
+        fq.block_shape((0, 128))
+    assert fq.block_shape([128, 128]) == (128, 128)
+    assert fq.scale_shape(4097, 11008, 128, 128) == (33, 86)
+
+
+def test_python_rejects_cpu_tensor():
+    import torch
+
+    with pytest.raises(TypeError):
+        fq.quantize(torch.zeros(4, 4, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        fq.quantize(torch.zeros(4, 4, dtype=torch.float32))
+
+
+def test_entry_layout_matches_header():
+    # fp8bq_tensor: three pointers then two int64 -> 40 bytes on LP64
+    assert ctypes.sizeof(fq.TensorEntry) == 40

@@ -1,0 +1,332 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bit-exact in both outputs: every fp8 byte and every fp32 scale.  Small and
+medium tensors are compared whole; the full-size weight sets (the 36-layer
+dense stack, the MoE layers, the 151937x4096 matrix) are compared on every
+scale (oracle scale function on the exact per-tile maximum), on sampled
+tiles (oracle run tile by tile) and on size-independent invariants.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_blockwise_weight_amd as fq
+import oracle
+from fp8_blockwise_weight_amd import workloads as wl
+from gpu_helpers import (assert_matches_oracle, assert_properties_gpu,
+                         assert_scales_match_oracle, assert_tiles_match_oracle, bits_np,
+                         codes_np, sample_tiles, scales_bits)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+BLOCKS = [(128, 128), (64, 64), (1, 128)]
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def bf16_from_bits(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(bits.astype(np.uint16).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+# ------------------------------------------------------------------ C1
+
+def test_c1_matches_oracle_and_closed_forms(gpu_lib):
+    (spec,) = wl.c1()
+    x = wl.materialize(spec, DEV)
+    q, s = fq.quantize(x, (128, 128))
+    torch.cuda.synchronize()
+    assert q.dtype == torch.float8_e4m3fn and q.shape == (256, 256)
+    assert s.dtype == torch.float32 and s.shape == (2, 2)
+    assert_matches_oracle(x, q, s, 128, 128, "C1")
+    sh = s.cpu().numpy()
+    assert sh[0, 0] == np.float32(5.0 / 448.0)
+    assert sh[1, 1] == np.float32(np.float64(np.float32(1e-10)) / 448.0)
+    codes = codes_np(q)
+    xb = bits_np(x)
+    outl = np.abs(oracle.bf16_bits_to_f64(xb[:128, :128])) == 5.0
+    assert outl.sum() == 8
+    assert set(np.unique(codes[:128, :128][outl])) <= {0x7E, 0xFE}
+    assert np.all(codes[128:, 128:] == 0)
+
+
+# ------------------------------------------------------------------ shapes and tails
+
+@pytest.mark.parametrize("bm,bn", BLOCKS)
+def test_vector_kinds_small_shapes(gpu_lib, bm, bn):
+    """Every tail combination around the 64/128-row and 128-column unit edges."""
+    g = torch.Generator(device=DEV).manual_seed(1234 + bm)
+    for M in (1, 2, 15, 16, 17, 63, 64, 65, 127, 128, 129, 200, 257):
+        for N in (8, 16, 120, 128, 136, 248, 256, 264, 384):
+            say("case", bm, bn, M, N)
+            x = (torch.randn((M, N), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+            q, s = fq.quantize(x, (bm, bn))
+            assert_matches_oracle(x, q, s, bm, bn, f"{M}x{N}/{bm}x{bn}")
+
+
+def test_general_tiny_exhaustive(gpu_lib):
+    """All M, N in 1..6 and bm, bn in 1..4 (the element-wise kernel)."""
+    g = torch.Generator(device=DEV).manual_seed(99)
+    for M in range(1, 7):
+        for N in range(1, 7):
+            x = (torch.randn((M, N), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+            x[torch.rand((M, N), generator=g, device=DEV) < 0.2] = 0
+            for bm in range(1, 5):
+                for bn in range(1, 5):
+                    q, s = fq.quantize(x, (bm, bn))
+                    assert_matches_oracle(x, q, s, bm, bn, f"{M}x{N}/{bm}x{bn}")
+
+
+@pytest.mark.parametrize("block", [(128, 128), (64, 64), (1, 128), (128, 64), (32, 32), (3, 5),
+                                   (1, 1), (256, 256), (1, 4096)])
+def test_general_path_odd_and_misaligned(gpu_lib, block):
+    """N % 8 != 0, misaligned x or q, and block sizes without a vector kernel."""
+    bm, bn = block
+    g = torch.Generator(device=DEV).manual_seed(7)
+    for M, N in ((300, 7), (129, 1001), (65, 3001), (200, 520)):
+        say("case", block, M, N)
+        big = (torch.randn(M * N + 8, generator=g, device=DEV) * 0.3).to(torch.bfloat16)
+        for off in (0, 1, 3):
+            x = big[off:off + M * N].view(M, N)   # off > 0: x not 16-byte aligned
+            qbuf = torch.empty(M * N + 8, dtype=torch.uint8, device=DEV)
+            q = qbuf[off:off + M * N].view(M, N)  # off > 0: q not 8-byte aligned
+            s = torch.empty(fq.scale_shape(M, N, bm, bn), dtype=torch.float32, device=DEV)
+            fq.quantize(x, block, out=(q, s))
+            assert_matches_oracle(x, q, s, bm, bn, f"{M}x{N}/{block}/off{off}")
+
+
+def test_special_values(gpu_lib):
+    """Zero, -0, BF16 subnormals, huge magnitudes and exact e4m3 ties."""
+    rows = []
+    ties = [448.0, 1.0625, -1.1875, 0.0029296875, 248.0, -400.0, 432.0, 2.0 ** -10]
+    rows.append(np.array(ties + [0.0] * 120, dtype=np.float32))
+    rows.append(np.array([-0.0] * 128, dtype=np.float32))
+    rows.append(np.zeros(128, dtype=np.float32))
+    sub = np.array([((i % 127) + 1) * 2.0 ** -133 for i in range(128)], dtype=np.float32)
+    rows.append(sub * np.where(np.arange(128) % 2, -1, 1))
+    rows.append(np.linspace(-3.3e38, 3.3e38, 128).astype(np.float32))
+    rows.append(np.array([1e-12] * 64 + [-3e-11] * 64, dtype=np.float32))  # below eps
+    x32 = torch.from_numpy(np.stack(rows))
+    x = x32.to(torch.bfloat16).to(DEV)
+    for bm, bn in [(1, 128), (128, 128), (64, 64), (2, 3), (6, 128)]:
+        q, s = fq.quantize(x, (bm, bn))
+        assert_matches_oracle(x, q, s, bm, bn, f"special/{bm}x{bn}")
+
+
+# ------------------------------------------------------------------ sweeps
+
+def _anchor_rows(anchors, rng):
+    """[1,128] rows: column 0 holds the anchor, the rest sweep every BF16
+    magnitude at or below it (random signs)."""
+    rows = []
+    for a in anchors:
+        mags = np.arange(0, a + 1, dtype=np.uint32)
+        mags = mags[rng.permutation(mags.size)]
+        pad = (-mags.size) % 127
+        mags = np.concatenate([mags, np.zeros(pad, dtype=np.uint32)]).reshape(-1, 127)
+        sign = (rng.integers(0, 2, mags.shape).astype(np.uint32) << 15)
+        body = (mags | sign).astype(np.uint16)
+        anchor = np.full((body.shape[0], 1), a, dtype=np.uint16)
+        anchor |= (rng.integers(0, 2, anchor.shape).astype(np.uint16) << 15)
+        rows.append(np.concatenate([anchor, body], axis=1))
+    return np.concatenate(rows)
+
+
+def test_anchor_sweep_every_bf16(gpu_lib):
+    """Every finite BF16 magnitude below each of many anchors, through the
+    [1,128] kernel and (re-tiled) the [128,128] kernel."""
+    rng = np.random.default_rng(2024)
+    anchors = sorted(set(int(v) for v in rng.integers(0x0080, 0x7F7F, 120)) |
+                     {0x43E0, 0x3F80, 0x40A0, 0x7F7F, 0x0001, 0x2EDB, 0x2EDC})
+    for i in range(0, len(anchors), 16):
+        bits = _anchor_rows(anchors[i:i + 16], rng)
+        x = bf16_from_bits(bits)
+        say("anchors", i, bits.shape)
+        q, s = fq.quantize(x, (1, 128))
+        assert_matches_oracle(x, q, s, 1, 128, f"anchor rows {i}")
+        rows = (bits.shape[0] // 128) * 128
+        if rows:
+            xt = x[:rows].contiguous()
+            q, s = fq.quantize(xt, (128, 128))
+            assert_matches_oracle(xt, q, s, 128, 128, f"anchor tiles {i}")
+
+
+def test_encoder_exhaustive_fp32(gpu_lib):
+    """The hardware convert over every float32 from 0 to 448 (and negatives,
+    and everything above 448 after the clamp): equal to the oracle encoder.
+
+    The codes of the positive patterns form a non-decreasing step function of
+    the bit pattern; so does the oracle's (a composition of monotone steps),
+    so agreement at both sides of every GPU step edge plus a strided sample
+    proves agreement everywhere."""
+    top = 0x43E00000  # 448.0
+    chunk = 1 << 27
+    prev_last = None
+    checked = 0
+    for start in range(0, top + 1, chunk):
+        end = min(top + 1, start + chunk)
+        pat = torch.arange(start, end, dtype=torch.int32, device=DEV)
+        y = pat.view(torch.float32)
+        c = fq.encode_e4m3(y)
+        cn = fq.encode_e4m3((pat | torch.tensor(-0x80000000, dtype=torch.int32, device=DEV))
+                            .view(torch.float32))
+        assert torch.equal(cn, c | 0x80), ("negative", start)
+        assert bool((c[1:] >= c[:-1]).all()), ("monotone", start)
+        if prev_last is not None:
+            assert int(c[0]) >= prev_last
+        prev_last = int(c[-1])
+        edges = torch.nonzero(c[1:] != c[:-1]).flatten().cpu().numpy()
+        idx = np.unique(np.concatenate([edges, edges + 1, [0, end - start - 1],
+                                        np.arange(0, end - start, 4099)]))
+        got = c.cpu().numpy()[idx]
+        vals = (idx.astype(np.int64) + start).astype(np.uint32).view(np.float32).astype(np.float64)
+        want = oracle.encode_np(vals)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, [(float(vals[i]), int(got[i]), int(want[i])) for i in bad[:5]]
+        checked += idx.size
+        say("encoder chunk", hex(start), "edges", edges.size)
+    assert checked > 0
+    # above 448: the clamp sends every finite value to 0x7E / 0xFE
+    for start in range(top + 1, 0x7F800000, chunk):
+        end = min(0x7F800000, start + chunk)
+        pat = torch.arange(start, end, dtype=torch.int32, device=DEV)
+        assert bool((fq.encode_e4m3(pat.view(torch.float32)) == 0x7E).all())
+        neg = (pat | torch.tensor(-0x80000000, dtype=torch.int32, device=DEV)).view(torch.float32)
+        assert bool((fq.encode_e4m3(neg) == 0xFE).all())
+
+
+# ------------------------------------------------------------------ weight sets
+
+def test_c2_layer_grouped_equals_oracle_and_single(gpu_lib):
+    specs = wl.c2()
+    xs = [wl.materialize(sp, DEV) for sp in specs]
+    outs = fq.quantize_many(xs, (128, 128))
+    torch.cuda.synchronize()
+    for sp, x, (q, s) in zip(specs, xs, outs):
+        say("C2", sp.name)
+        assert_matches_oracle(x, q, s, 128, 128, sp.name)
+        q1, s1 = fq.quantize(x, (128, 128))
+        assert torch.equal(q1.view(torch.uint8), q.view(torch.uint8))
+        assert torch.equal(s1.view(torch.int32), s.view(torch.int32))
+
+
+def test_determinism_and_canaries(gpu_lib):
+    """Same bytes on every run; nothing written outside q and scale_inv."""
+    G = 256
+    g = torch.Generator(device=DEV).manual_seed(5)
+    for M, N, block in ((77, 128, (128, 128)), (4097, 11008, (128, 128)), (1000, 3000, (64, 64)),
+                        (1000, 3000, (1, 128)), (129, 1001, (128, 128)), (33, 40, (5, 7))):
+        say("canary", M, N, block)
+        x = (torch.randn((M, N), generator=g, device=DEV) * 0.05).to(torch.bfloat16)
+        TM, TN = fq.scale_shape(M, N, *block)
+        results = []
+        for _ in range(2):
+            qb = torch.full((M * N + 2 * G,), 0xA5, dtype=torch.uint8, device=DEV)
+            sb = torch.full((TM * TN + 2 * G,), -7.5, dtype=torch.float32, device=DEV)
+            q = qb[G:G + M * N].view(M, N)
+            s = sb[G:G + TM * TN].view(TM, TN)
+            fq.quantize(x, block, out=(q, s))
+            torch.cuda.synchronize()
+            assert bool((qb[:G] == 0xA5).all()) and bool((qb[G + M * N:] == 0xA5).all())
+            assert bool((sb[:G] == -7.5).all()) and bool((sb[G + TM * TN:] == -7.5).all())
+            results.append((q.clone(), s.clone()))
+        assert torch.equal(results[0][0], results[1][0])
+        assert torch.equal(results[0][1].view(torch.int32), results[1][1].view(torch.int32))
+
+
+def test_grouped_mixed_list(gpu_lib):
+    """One grouped launch over empty, odd-N, misaligned and aligned tensors
+    equals single calls and the oracle, for every block kind."""
+    g = torch.Generator(device=DEV).manual_seed(11)
+    base = (torch.randn(600 * 1001 + 16, generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    mats = [
+        (torch.randn((300, 512), generator=g, device=DEV) * 0.02).to(torch.bfloat16),
+        torch.empty((0, 128), dtype=torch.bfloat16, device=DEV),
+        base[1:1 + 129 * 1001].view(129, 1001),                       # odd N, misaligned
+        (torch.randn((1, 8), generator=g, device=DEV)).to(torch.bfloat16),
+        torch.zeros((128, 256), dtype=torch.bfloat16, device=DEV),
+        base[8:8 + 200 * 136].view(200, 136),                          # aligned view
+        torch.empty((5, 0), dtype=torch.bfloat16, device=DEV),
+        (torch.randn((1537, 2048), generator=g, device=DEV) * 0.03).to(torch.bfloat16),
+    ]
+    for block in BLOCKS + [(3, 5)]:
+        say("mixed", block)
+        outs = fq.quantize_many(mats, block)
+        for i, (x, (q, s)) in enumerate(zip(mats, outs)):
+            if x.numel() == 0:
+                continue
+            assert_matches_oracle(x, q, s, *block, f"mixed[{i}]/{block}")
+            q1, s1 = fq.quantize(x, block)
+            assert torch.equal(q1.view(torch.uint8), q.view(torch.uint8))
+
+
+@pytest.mark.parametrize("bm,bn", BLOCKS)
+def test_c5_ragged_full(gpu_lib, bm, bn):
+    for sp in wl.c5():
+        x = wl.materialize(sp, DEV)
+        q, s = fq.quantize(x, (bm, bn))
+        say("C5", sp.name, bm, bn)
+        if sp.M * sp.N <= 50_000_000:
+            assert_matches_oracle(x, q, s, bm, bn, f"{sp.name}/{bm}x{bn}")
+        else:
+            assert_scales_match_oracle(x, s, bm, bn, sp.name)
+            assert_tiles_match_oracle(x, q, s, bm, bn,
+                                      sample_tiles(sp.M, sp.N, bm, bn, 40, seed=bm * 7 + bn), sp.name)
+            # the last tile rows whole (ragged bottom edge)
+            r0 = ((sp.M - 1) // 128) * 128
+            xs = x[r0:].contiguous()
+            qs, ss = fq.quantize(xs, (bm, bn))
+            assert torch.equal(qs.view(torch.uint8), q[r0:].view(torch.uint8))
+            assert_matches_oracle(xs, qs, ss, bm, bn, sp.name + "/tail")
+        assert_properties_gpu(x, q, s, bm, bn, sp.name)
+        del x, q, s
+
+
+def test_c3_dense_stack_one_grouped_launch(gpu_lib):
+    """The 36-layer dense weight set (252 tensors, 13.9 GB) in the one grouped
+    launch the benchmark times: every scale, sampled tiles, invariants."""
+    specs = wl.c3()
+    xs = [wl.materialize(sp, DEV) for sp in specs]
+    say("C3 generated", len(xs))
+    outs = fq.quantize_many(xs, (128, 128))
+    torch.cuda.synchronize()
+    for i, (sp, x, (q, s)) in enumerate(zip(specs, xs, outs)):
+        assert_scales_match_oracle(x, s, 128, 128, sp.name)
+        assert_properties_gpu(x, q, s, 128, 128, sp.name)
+        if i % 6 == 0:
+            assert_tiles_match_oracle(x, q, s, 128, 128,
+                                      sample_tiles(sp.M, sp.N, 128, 128, 3, seed=i), sp.name)
+    say("C3 checked")
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_c4_moe_per_layer_grouped(gpu_lib, part):
+    """MoE weight set: 48 layers x 256 expert matrices, one grouped launch per
+    layer (12 layers per test)."""
+    for layer in range(part * 12, part * 12 + 12):
+        specs = wl.c4_layer(layer)
+        xs = [wl.materialize(sp, DEV) for sp in specs]
+        outs = fq.quantize_many(xs, (128, 128))
+        say("C4 layer", layer)
+        # scales of the whole layer at once: stack the per-tile maxima
+        for j in (0, 1):
+            sub = list(range(j, len(xs), 2))
+            xg = torch.stack([xs[k] for k in sub])
+            E, M, N = xg.shape
+            amax = xg.abs().view(E, M // 128, 128, N // 128, 128).amax(dim=(2, 4))
+            s_ref, _ = oracle.blockwise.tile_scales_np(amax.float().cpu().numpy().astype(np.float64))
+            s_got = torch.stack([outs[k][1] for k in sub]).cpu().numpy()
+            assert np.array_equal(scales_bits(s_got), scales_bits(s_ref.astype(np.float32))), layer
+            qg = torch.stack([outs[k][0].view(torch.uint8) for k in sub])
+            assert not bool(((qg == 0x7F) | (qg == 0xFF)).any())
+            tmax = (qg & 0x7F).view(E, M // 128, 128, N // 128, 128).amax(dim=(2, 4))
+            assert bool((tmax == 0x7E).all()), layer
+        for k in (0, 1, 254, 255):
+            x, (q, s) = xs[k], outs[k]
+            assert_tiles_match_oracle(x, q, s, 128, 128,
+                                      sample_tiles(*x.shape, 128, 128, 2, seed=layer * 256 + k),
+                                      specs[k].name)
+        del xs, outs
