@@ -16,8 +16,8 @@ Reported value: algorithmic GB/s = (2 B read + 1 B written per element +
                 workload (one layer), on this host.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3]
-                       [--workload dense|dense-layer|moe|ragged]
-                       [--no-cpu-baseline] [--calibrate-copy]
+                       [--workload dense|dense-layer|moe|ragged|vocab] [--block bm,bn]
+                       [--per-tensor] [--no-cpu-baseline] [--calibrate-copy]
 """
 
 import argparse
@@ -66,7 +66,7 @@ def committed_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
-def build_workload(name, dev):
+def build_workload(name, dev, block=None):
     import torch  # noqa: F401
     from fp8_blockwise_weight_amd import workloads as wl
 
@@ -84,8 +84,13 @@ def build_workload(name, dev):
         desc = "moe 48 layers x 128 experts (w13 1536x2048, down 2048x768), one launch per layer"
     elif name == "ragged":
         groups = [[sp] for sp in wl.c5()]
-        block = (128, 128)
-        desc = "ragged 1000x3000, 4097x11008, 151937x4096, 77x128, one launch each"
+        block = block or (128, 128)
+        desc = (f"ragged 1000x3000, 4097x11008, 151937x4096, 77x128 at block "
+                f"[{block[0]},{block[1]}], one launch each")
+    elif name == "vocab":
+        groups = [[sp] for sp in wl.c5() if sp.M == 151937]
+        block = block or (128, 128)
+        desc = f"151937x4096 (vocab-shaped) at block [{block[0]},{block[1]}]"
     else:
         raise SystemExit(f"unknown workload {name}")
     return groups, block, desc
@@ -97,6 +102,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense")
+    ap.add_argument("--block", default=None, help="bm,bn for the ragged/vocab workloads")
+    ap.add_argument("--per-tensor", action="store_true",
+                    help="also time one fp8bq_quantize call per tensor (HIP events per call)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of known size (for counter calibration)")
@@ -116,7 +124,8 @@ def main():
     lib = fq.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    groups, (bm, bn), desc = build_workload(args.workload, dev)
+    block = tuple(int(v) for v in args.block.split(",")) if args.block else None
+    groups, (bm, bn), desc = build_workload(args.workload, dev, block)
     from fp8_blockwise_weight_amd import workloads as wl
 
     t0 = time.perf_counter()
@@ -186,7 +195,12 @@ def main():
         torch.cuda.synchronize()
         log("calibration copy: 3 x 1 GiB device-to-device")
 
-    traffic = committed_traffic()
+    per_tensor = None
+    if args.per_tensor:
+        per_tensor = time_per_tensor(lib, keep, groups, bm, bn, stream, sptr)
+
+    traffic = committed_traffic() if args.workload == "dense" else None
+    kind = {(128, 128): "kT128", (64, 64): "kT64", (1, 128): "kR128"}.get((bm, bn), "kGeneral")
     roofline = {
         "bound": "hbm",
         "achieved": round(achieved, 1),
@@ -194,7 +208,7 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": traffic,
-        "kernel": f"fp8bq::quantize_group<kT128> ({'one launch' if launches == 1 else f'{launches} launches'} per step)",
+        "kernel": f"fp8bq::quantize_group<{kind}> ({'one launch' if launches == 1 else f'{launches} launches'} per step)",
         "bytes_per_launch": bytes_per_launch,
         "mean_launch_ms": round(mean_launch_ms, 4),
     }
@@ -228,7 +242,46 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if per_tensor is not None:
+        out["per_tensor"] = per_tensor
     print(json.dumps(out), flush=True)
+
+
+def time_per_tensor(lib, keep, groups, bm, bn, stream, sptr, reps=3):
+    """One fp8bq_quantize launch per tensor, HIP events around each call.
+    Returns GB/s per tensor shape (mean over tensors of that shape) and the
+    end-to-end rate of the per-tensor loop."""
+    import torch
+
+    calls = []
+    for (xs, outs), specs in zip(keep, groups):
+        for x, (q, s), sp in zip(xs, outs, specs):
+            calls.append((sp, x, q, s))
+    for sp, x, q, s in calls[:8]:
+        lib.fp8bq_quantize(x.data_ptr(), sp.M, sp.N, bm, bn, q.data_ptr(), s.data_ptr(), sptr)
+    torch.cuda.synchronize()
+    by_shape = {}
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        evs = []
+        for sp, x, q, s in calls:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            st = lib.fp8bq_quantize(x.data_ptr(), sp.M, sp.N, bm, bn, q.data_ptr(), s.data_ptr(), sptr)
+            b.record(stream)
+            if st != 0:
+                raise RuntimeError(f"fp8bq_quantize failed: {st}")
+            evs.append((sp, a, b))
+        torch.cuda.synchronize()
+        for sp, a, b in evs:
+            key = f"{sp.name.split('.')[-1]} {sp.M}x{sp.N}"
+            by_shape.setdefault(key, []).append(algorithmic_bytes(sp.M, sp.N, bm, bn) / (a.elapsed_time(b) * 1e-3) / 1e9)
+    wall = (time.perf_counter() - t0) / reps
+    total = sum(algorithmic_bytes(sp.M, sp.N, bm, bn) for sp, *_ in calls)
+    res = {k: round(sum(v) / len(v), 1) for k, v in by_shape.items()}
+    res["loop_of_single_calls_GBps"] = round(total / wall / 1e9, 1)
+    log("per-tensor single calls (GB/s): " + json.dumps(res))
+    return res
 
 
 def cpu_baseline(xs, specs, bm, bn):

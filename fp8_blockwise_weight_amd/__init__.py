@@ -35,6 +35,9 @@ EXPORTS = (
     "fp8bq_many_workspace_bytes",
     "fp8bq_quantize_many",
     "fp8bq_encode_e4m3",
+    "fp8bq_dequantize",
+    "fp8bq_tile_amax",
+    "fp8bq_quantize_amax",
     "fp8bq_status_string",
     "fp8bq_last_hip_error",
 )
@@ -81,6 +84,13 @@ def load_library() -> ctypes.CDLL:
     lib.fp8bq_quantize_many.argtypes = [ctypes.POINTER(TensorEntry), c_i32, c_i32, c_i32, c_vp,
                                         ctypes.c_size_t, c_vp]
     lib.fp8bq_quantize_many.restype = ctypes.c_int
+    lib.fp8bq_dequantize.argtypes = [c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_vp, c_i32, c_vp]
+    lib.fp8bq_dequantize.restype = ctypes.c_int
+    lib.fp8bq_tile_amax.argtypes = [c_vp, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]
+    lib.fp8bq_tile_amax.restype = ctypes.c_int
+    lib.fp8bq_quantize_amax.argtypes = [c_vp, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_vp,
+                                        c_vp, c_vp, c_vp]
+    lib.fp8bq_quantize_amax.restype = ctypes.c_int
     lib.fp8bq_encode_e4m3.argtypes = [c_vp, c_vp, c_i64, c_vp]
     lib.fp8bq_encode_e4m3.restype = ctypes.c_int
     lib.fp8bq_status_string.argtypes = [ctypes.c_int]
@@ -202,6 +212,88 @@ def quantize_many(tensors: Sequence, block_size=(128, 128), outputs: Optional[Se
     return list(outputs)
 
 
+def dequantize(q, scale_inv, block_size=(128, 128), out_dtype=None, out=None):
+    """x_hat = decode(q) * scale_inv (per block), as float32 or bfloat16 [M, N].
+
+    ``q`` is a float8_e4m3fn (or uint8) GPU tensor [M, N]; ``scale_inv`` the
+    float32 [ceil(M/bm), ceil(N/bn)] descale from ``quantize``.
+    """
+    import torch
+
+    bm, bn = block_shape(block_size)
+    out_dtype = out_dtype or torch.float32
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    if q.dim() != 2 or q.element_size() != 1 or not q.is_cuda or not q.is_contiguous():
+        raise TypeError("q must be a contiguous 2-D one-byte GPU tensor")
+    M, N = q.shape
+    if tuple(scale_inv.shape) != scale_shape(M, N, bm, bn) or scale_inv.dtype != torch.float32 \
+            or not scale_inv.is_contiguous():
+        raise TypeError("scale_inv must be contiguous float32 [ceil(M/bm), ceil(N/bn)]")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=q.device)
+    code = 0 if out_dtype == torch.float32 else 1
+    with torch.cuda.device(q.device):
+        _check("fp8bq_dequantize",
+               load_library().fp8bq_dequantize(q.data_ptr(), scale_inv.data_ptr(), M, N, bm, bn,
+                                               out.data_ptr(), code, _stream(q.device)))
+    return out
+
+
+def local_grid(M: int, N: int, bm: int, bn: int, phase=(0, 0)) -> Tuple[int, int]:
+    """Tile grid of a shard whose element (0,0) sits at ``phase`` inside a tile."""
+    rp, cp = phase
+    if not (0 <= rp < bm and 0 <= cp < bn):
+        raise ValueError("phase must satisfy 0 <= phase < block")
+    return (-(-(rp + M) // bm), -(-(cp + N) // bn))
+
+
+def tile_amax(x, block_size=(128, 128), phase=(0, 0), out=None):
+    """Per-tile max |x| (float32 [TMl, TNl]) of a BF16 shard at tile ``phase``.
+
+    Combine the results of shards that share tiles with an element-wise max
+    (exact), then pass the full maxima to ``quantize_with_amax``.
+    """
+    import torch
+
+    bm, bn = block_shape(block_size)
+    _check_input(x)
+    M, N = x.shape
+    shape = local_grid(M, N, bm, bn, phase)
+    amax = out if out is not None else torch.empty(shape, dtype=torch.float32, device=x.device)
+    with torch.cuda.device(x.device):
+        _check("fp8bq_tile_amax",
+               load_library().fp8bq_tile_amax(x.data_ptr(), M, N, bm, bn, phase[0], phase[1],
+                                              amax.data_ptr(), _stream(x.device)))
+    return amax
+
+
+def quantize_with_amax(x, amax, block_size=(128, 128), phase=(0, 0), out=None):
+    """Quantize a BF16 shard with given whole-tile maxima ``amax`` [TMl, TNl].
+
+    Returns ``(q, scale_inv)``; ``scale_inv`` covers the shard's tiles.
+    """
+    import torch
+
+    bm, bn = block_shape(block_size)
+    _check_input(x)
+    M, N = x.shape
+    shape = local_grid(M, N, bm, bn, phase)
+    if tuple(amax.shape) != shape or amax.dtype != torch.float32 or not amax.is_contiguous():
+        raise TypeError(f"amax must be contiguous float32 {shape}")
+    if out is None:
+        q = torch.empty((M, N), dtype=torch.float8_e4m3fn, device=x.device)
+        s = torch.empty(shape, dtype=torch.float32, device=x.device)
+    else:
+        q, s = out
+    with torch.cuda.device(x.device):
+        _check("fp8bq_quantize_amax",
+               load_library().fp8bq_quantize_amax(x.data_ptr(), M, N, bm, bn, phase[0], phase[1],
+                                                  amax.data_ptr(), q.data_ptr(), s.data_ptr(),
+                                                  _stream(x.device)))
+    return q, s
+
+
 def encode_e4m3(y):
     """The final cast alone: float32 GPU tensor -> e4m3fn codes (uint8), clamped to +-448."""
     import torch
@@ -217,6 +309,7 @@ def encode_e4m3(y):
 
 
 __all__ = [
-    "EXPORTS", "Fp8bqError", "TensorEntry", "block_shape", "encode_e4m3", "load_library",
+    "EXPORTS", "Fp8bqError", "TensorEntry", "block_shape", "dequantize", "encode_e4m3",
+    "load_library", "local_grid", "quantize_with_amax", "tile_amax",
     "make_entries", "quantize", "quantize_many", "scale_shape", "workspace_bytes",
 ]

@@ -128,6 +128,67 @@ void launch_group(const Desc* descs, const int64_t* start, int32_t count, int32_
                      st, descs, start, count, bm, bn, units);
 }
 
+// Effective tile of an [M, N] tensor: more than kBigTile elements takes the
+// two-pass path.
+bool big_tiles(int64_t M, int64_t N, int32_t bm, int32_t bn) {
+  const int64_t rows = M < bm ? M : bm;
+  const int64_t cols = N < bn ? N : bn;
+  return rows * cols > fp8bq::kBigTile;
+}
+
+// Describes a sub-matrix at tile phase (rp, cp) for the two-pass kernels.
+fp8bq::Big make_big(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, int32_t rp,
+                    int32_t cp, void* q) {
+  fp8bq::Big b;
+  b.x = static_cast<const uint16_t*>(x);
+  b.q = static_cast<uint8_t*>(q);
+  b.M = M;
+  b.N = N;
+  b.bm = bm;
+  b.bn = bn;
+  b.row_phase = rp;
+  b.col_phase = cp;
+  b.TMl = ceil_div(rp + M, bm);
+  b.TNl = ceil_div(cp + N, bn);
+  b.flat = (cp == 0 && bn >= N) ? 1 : 0;
+  const uintptr_t xa = reinterpret_cast<uintptr_t>(x);
+  const uintptr_t qa = reinterpret_cast<uintptr_t>(q);
+  b.vec = ((N % 8) == 0 && (xa & 15) == 0 && (qa & 7) == 0) ? 1 : 0;
+  const int64_t rows_max = M < bm ? M : bm;
+  const int64_t cols_max = N < bn ? N : bn;
+  if (b.flat) {
+    b.cpt = ceil_div(rows_max * N, fp8bq::kChunk);
+  } else {
+    const int64_t rows_per = cols_max >= fp8bq::kChunk ? 1 : fp8bq::kChunk / cols_max;
+    b.cpt = ceil_div(rows_max, rows_per);
+  }
+  b.items = b.TMl * b.TNl * b.cpt;
+  return b;
+}
+
+unsigned grid_capped(int64_t n, int64_t per_block) {
+  const int64_t blocks = (n + per_block - 1) / per_block;
+  return static_cast<unsigned>(blocks < 65536 * 16 ? (blocks < 1 ? 1 : blocks) : 65536 * 16);
+}
+
+// Pass 1 (maxima into `amax`, zeroed first), optional pass 2 and scales.
+// `amax` may be `scale_inv` itself (it then serves as the scratch).
+void launch_big_amax(const fp8bq::Big& b, float* amax, hipStream_t st) {
+  const int64_t nt = b.TMl * b.TNl;
+  hipLaunchKernelGGL(fp8bq::fill_zero, dim3(grid_capped(nt, fp8bq::kThreads)), dim3(fp8bq::kThreads),
+                     0, st, reinterpret_cast<uint32_t*>(amax), nt);
+  hipLaunchKernelGGL(fp8bq::big_tiles<0>, dim3(grid_for(b.items)), dim3(fp8bq::kThreads), 0, st, b,
+                     reinterpret_cast<uint32_t*>(amax), static_cast<const float*>(nullptr));
+}
+
+void launch_big_quant(const fp8bq::Big& b, const float* amax, float* scale_inv, hipStream_t st) {
+  const int64_t nt = b.TMl * b.TNl;
+  hipLaunchKernelGGL(fp8bq::big_tiles<1>, dim3(grid_for(b.items)), dim3(fp8bq::kThreads), 0, st, b,
+                     static_cast<uint32_t*>(nullptr), amax);
+  hipLaunchKernelGGL(fp8bq::finalize_scales, dim3(grid_capped(nt, fp8bq::kThreads)),
+                     dim3(fp8bq::kThreads), 0, st, amax, scale_inv, nt);
+}
+
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 size_t descs_bytes(int32_t count) { return align_up(sizeof(Desc) * static_cast<size_t>(count), 256); }
@@ -151,6 +212,14 @@ int fp8bq_quantize(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, 
   if (st != FP8BQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
+  if (big_tiles(M, N, bm, bn)) {
+    // scale_inv doubles as the scratch for the per-tile maxima.
+    const fp8bq::Big b = make_big(x, M, N, bm, bn, 0, 0, q);
+    launch_big_amax(b, scale_inv, s);
+    launch_big_quant(b, scale_inv, scale_inv, s);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
+  }
   switch (d.general ? static_cast<int>(fp8bq::kGeneral) : kind) {
     case fp8bq::kT128: launch_one<fp8bq::kT128>(d, bm, bn, units, s); break;
     case fp8bq::kT64: launch_one<fp8bq::kT64>(d, bm, bn, units, s); break;
@@ -182,22 +251,42 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
   int64_t* start = reinterpret_cast<int64_t*>(g_stage.data() + descs_bytes(count));
   int32_t n = 0;
   int64_t total = 0;
+  bool any_big = false;
   for (int32_t i = 0; i < count; ++i) {
     const fp8bq_tensor& t = list[i];
     int64_t units = 0;
-    const int st = make_desc(t.x, t.M, t.N, bm, bn, t.q, t.scale_inv, kind, &descs[n], &units);
+    Desc scratch;
+    const int st = make_desc(t.x, t.M, t.N, bm, bn, t.q, t.scale_inv, kind, &scratch, &units);
     if (st != FP8BQ_OK) return st;
     if (units == 0) continue;
+    if (big_tiles(t.M, t.N, bm, bn)) {  // two-pass path, launched per tensor below
+      any_big = true;
+      continue;
+    }
+    descs[n] = scratch;
     start[n] = total;
     total += units;
     ++n;
   }
-  if (n == 0) return FP8BQ_OK;
+  if (n == 0 && !any_big) return FP8BQ_OK;
   start[n] = total;
   int st = device_check();
   if (st != FP8BQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
+  if (any_big) {
+    for (int32_t i = 0; i < count; ++i) {
+      const fp8bq_tensor& t = list[i];
+      if (t.M == 0 || t.N == 0 || !big_tiles(t.M, t.N, bm, bn)) continue;
+      const fp8bq::Big b = make_big(t.x, t.M, t.N, bm, bn, 0, 0, t.q);
+      launch_big_amax(b, t.scale_inv, s);
+      launch_big_quant(b, t.scale_inv, t.scale_inv, s);
+    }
+    if (n == 0) {
+      const hipError_t e = hipGetLastError();
+      return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
+    }
+  }
   // The two tables are packed at the front of the workspace in the same
   // layout as the staging buffer, so one copy moves both.
   unsigned char* ws = static_cast<unsigned char*>(workspace);
@@ -213,6 +302,69 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
     default: launch_group<fp8bq::kGeneral>(d_descs, d_start, n, bm, bn, total, s); break;
   }
   e = hipGetLastError();
+  return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
+}
+
+int fp8bq_tile_amax(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, int32_t row_phase,
+                    int32_t col_phase, float* amax, void* stream) {
+  if (M < 0 || N < 0 || M > INT32_MAX || N > INT32_MAX || bm < 1 || bn < 1) {
+    return FP8BQ_ERR_INVALID_ARGUMENT;
+  }
+  if (row_phase < 0 || row_phase >= bm || col_phase < 0 || col_phase >= bn) {
+    return FP8BQ_ERR_INVALID_ARGUMENT;
+  }
+  if (M == 0 || N == 0) return FP8BQ_OK;
+  if (x == nullptr || amax == nullptr) return FP8BQ_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(x) & 1) != 0 || (reinterpret_cast<uintptr_t>(amax) & 3) != 0) {
+    return FP8BQ_ERR_INVALID_ARGUMENT;
+  }
+  const fp8bq::Big b = make_big(x, M, N, bm, bn, row_phase, col_phase, nullptr);
+  const uint64_t n = static_cast<uint64_t>(M) * static_cast<uint64_t>(N);
+  if (overlap(x, 2 * n, amax, 4 * static_cast<uint64_t>(b.TMl * b.TNl))) {
+    return FP8BQ_ERR_INVALID_ARGUMENT;
+  }
+  const int st = device_check();
+  if (st != FP8BQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  launch_big_amax(b, amax, s);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
+}
+
+int fp8bq_quantize_amax(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn,
+                        int32_t row_phase, int32_t col_phase, const float* amax, void* q,
+                        float* scale_inv, void* stream) {
+  if (M < 0 || N < 0 || M > INT32_MAX || N > INT32_MAX || bm < 1 || bn < 1) {
+    return FP8BQ_ERR_INVALID_ARGUMENT;
+  }
+  if (row_phase < 0 || row_phase >= bm || col_phase < 0 || col_phase >= bn) {
+    return FP8BQ_ERR_INVALID_ARGUMENT;
+  }
+  if (M == 0 || N == 0) return FP8BQ_OK;
+  if (x == nullptr || amax == nullptr || q == nullptr || scale_inv == nullptr) {
+    return FP8BQ_ERR_INVALID_ARGUMENT;
+  }
+  if ((reinterpret_cast<uintptr_t>(x) & 1) != 0 || (reinterpret_cast<uintptr_t>(amax) & 3) != 0 ||
+      (reinterpret_cast<uintptr_t>(scale_inv) & 3) != 0) {
+    return FP8BQ_ERR_INVALID_ARGUMENT;
+  }
+  const fp8bq::Big b = make_big(x, M, N, bm, bn, row_phase, col_phase, q);
+  const uint64_t n = static_cast<uint64_t>(M) * static_cast<uint64_t>(N);
+  const uint64_t nt = 4 * static_cast<uint64_t>(b.TMl * b.TNl);
+  // amax may be scale_inv itself (converted in place), but not partly overlap it.
+  const bool same = static_cast<const void*>(amax) == static_cast<const void*>(scale_inv);
+  if (overlap(x, 2 * n, q, n) || overlap(x, 2 * n, scale_inv, nt) || overlap(q, n, scale_inv, nt) ||
+      overlap(x, 2 * n, amax, nt) || overlap(q, n, amax, nt) ||
+      (!same && overlap(amax, nt, scale_inv, nt))) {
+    return FP8BQ_ERR_INVALID_ARGUMENT;
+  }
+  const int st = device_check();
+  if (st != FP8BQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  launch_big_quant(b, amax, scale_inv, s);
+  const hipError_t e = hipGetLastError();
   return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
 }
 
@@ -233,6 +385,60 @@ int fp8bq_encode_e4m3(const float* y, void* q, int64_t n, void* stream) {
   const unsigned grid = static_cast<unsigned>(blocks < 65536 * 16 ? blocks : 65536 * 16);
   hipLaunchKernelGGL(fp8bq::encode_e4m3, dim3(grid), dim3(fp8bq::kThreads), 0, s, y,
                      static_cast<uint8_t*>(q), n);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
+}
+
+int fp8bq_dequantize(const void* q, const float* scale_inv, int64_t M, int64_t N, int32_t bm,
+                     int32_t bn, void* out, int32_t out_dtype, void* stream) {
+  if (M < 0 || N < 0 || M > INT32_MAX || N > INT32_MAX || bm < 1 || bn < 1) {
+    return FP8BQ_ERR_INVALID_ARGUMENT;
+  }
+  if (out_dtype != FP8BQ_OUT_F32 && out_dtype != FP8BQ_OUT_BF16) return FP8BQ_ERR_INVALID_ARGUMENT;
+  if (M == 0 || N == 0) return FP8BQ_OK;
+  if (q == nullptr || scale_inv == nullptr || out == nullptr) return FP8BQ_ERR_INVALID_ARGUMENT;
+  const uintptr_t qa = reinterpret_cast<uintptr_t>(q);
+  const uintptr_t sa = reinterpret_cast<uintptr_t>(scale_inv);
+  const uintptr_t oa = reinterpret_cast<uintptr_t>(out);
+  const uint64_t esize = out_dtype == FP8BQ_OUT_F32 ? 4 : 2;
+  if ((sa & 3) != 0 || (oa & (esize - 1)) != 0) return FP8BQ_ERR_INVALID_ARGUMENT;
+  const int64_t TM = ceil_div(M, bm);
+  const int64_t TN = ceil_div(N, bn);
+  const uint64_t n = static_cast<uint64_t>(M) * static_cast<uint64_t>(N);
+  const uint64_t ns = static_cast<uint64_t>(TM) * static_cast<uint64_t>(TN);
+  if (overlap(out, esize * n, q, n) || overlap(out, esize * n, scale_inv, 4 * ns)) {
+    return FP8BQ_ERR_INVALID_ARGUMENT;
+  }
+  const int st = device_check();
+  if (st != FP8BQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const uint8_t* qb = static_cast<const uint8_t*>(q);
+  const int32_t tn = static_cast<int32_t>(TN);
+  const bool vec = (N % 16) == 0 && (bn % 16) == 0 && (qa & 15) == 0 && (oa & 15) == 0;
+  if (vec) {
+    const int64_t chunks = static_cast<int64_t>(n / 16);
+    const int64_t blocks = (chunks + fp8bq::kThreads - 1) / fp8bq::kThreads;
+    if (blocks > kMaxGrid) return FP8BQ_ERR_INVALID_ARGUMENT;
+    const dim3 grid(static_cast<unsigned>(blocks));
+    if (out_dtype == FP8BQ_OUT_F32) {
+      hipLaunchKernelGGL(fp8bq::dequant_vec<fp8bq::kOutF32>, grid, dim3(fp8bq::kThreads), 0, s, qb,
+                         scale_inv, N, bm, bn, tn, out, chunks);
+    } else {
+      hipLaunchKernelGGL(fp8bq::dequant_vec<fp8bq::kOutBF16>, grid, dim3(fp8bq::kThreads), 0, s, qb,
+                         scale_inv, N, bm, bn, tn, out, chunks);
+    }
+  } else {
+    const int64_t blocks = (static_cast<int64_t>(n) + fp8bq::kThreads - 1) / fp8bq::kThreads;
+    const dim3 grid(static_cast<unsigned>(blocks < 65536 * 16 ? blocks : 65536 * 16));
+    if (out_dtype == FP8BQ_OUT_F32) {
+      hipLaunchKernelGGL(fp8bq::dequant_elem<fp8bq::kOutF32>, grid, dim3(fp8bq::kThreads), 0, s, qb,
+                         scale_inv, N, bm, bn, tn, out, static_cast<int64_t>(n));
+    } else {
+      hipLaunchKernelGGL(fp8bq::dequant_elem<fp8bq::kOutBF16>, grid, dim3(fp8bq::kThreads), 0, s, qb,
+                         scale_inv, N, bm, bn, tn, out, static_cast<int64_t>(n));
+    }
+  }
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
 }

@@ -120,6 +120,13 @@ __device__ __forceinline__ void tile_scale(uint32_t maxbits, float& s, float& r)
   r = 1.0f / s;
 }
 
+// Same from a maximum given as a float (for maxima combined outside a tile).
+__device__ __forceinline__ void tile_scale_f(float amax, float& s, float& r) {
+  const float a = fmaxf(amax, kEps);
+  s = a / kE4m3Max;
+  r = 1.0f / s;
+}
+
 __device__ __forceinline__ float clamp448(float y) {
   return __builtin_amdgcn_fmed3f(y, -kE4m3Max, kE4m3Max);
 }
@@ -357,6 +364,241 @@ __global__ __launch_bounds__(kThreads) void quantize_group(const Desc* __restric
     const Desc d = descs[lo];
     run_unit<KIND>(d, bm, bn, u - start[lo], red);
     __syncthreads();  // red[] is reused by the next round
+  }
+}
+
+// ---------------------------------------------------------------- large tiles and shards
+//
+// Tiles too large for one workgroup (per-tensor scales, [1, N] rows of
+// huge N, any tile above kBigTile elements) and sub-matrices that start
+// inside a tile (shards) take two passes: pass 1 reduces chunks of each tile
+// and folds them into a per-tile maximum with an atomic max; pass 2
+// quantizes the chunks with the finished maxima; a last tiny kernel turns
+// maxima into scales.  The sub-matrix's element (0,0) sits at
+// (row_phase, col_phase) inside a tile of the full matrix's grid.
+
+constexpr int64_t kBigTile = 65536;     // elements; larger tiles take this path
+constexpr int64_t kChunk = 16384;       // elements per workgroup pass
+
+struct Big {
+  const uint16_t* x;
+  uint8_t* q;
+  int64_t M;
+  int64_t N;
+  int32_t bm;
+  int32_t bn;
+  int32_t row_phase;
+  int32_t col_phase;
+  int64_t TMl;   // local tile rows
+  int64_t TNl;   // local tile columns
+  int64_t cpt;   // chunks per tile
+  int64_t items; // TMl * TNl * cpt
+  int32_t flat;  // tiles cover whole rows: a chunk is one contiguous range
+  int32_t vec;   // x 16-byte aligned, q 8-byte aligned, N % 8 == 0
+};
+
+// Rows [r0, r1) and columns [c0, c1) of local tile (ti, tj).
+__device__ __forceinline__ void big_rect(const Big& b, int64_t ti, int64_t tj, int64_t& r0,
+                                         int64_t& r1, int64_t& c0, int64_t& c1) {
+  r0 = ti * b.bm - b.row_phase;
+  r1 = r0 + b.bm;
+  c0 = tj * b.bn - b.col_phase;
+  c1 = c0 + b.bn;
+  r0 = r0 < 0 ? 0 : r0;
+  c0 = c0 < 0 ? 0 : c0;
+  r1 = r1 > b.M ? b.M : r1;
+  c1 = c1 > b.N ? b.N : c1;
+}
+
+// Workgroup-wide max of one value per thread (uniform result).
+__device__ __forceinline__ uint32_t block_max(uint32_t m, uint32_t* red) {
+  m = max16(m);
+  const uint32_t wm = rows_max<0>(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = wm;
+  __syncthreads();
+  const uint32_t r = max(max(red[0], red[1]), max(red[2], red[3]));
+  __syncthreads();  // red[] is reused by the next call
+  return r;
+}
+
+// PASS 0: partial maxima (as fp32 bit patterns of the BF16 magnitudes) into
+// amax_bits, which must start at zero.  PASS 1: quantize with amax.
+template <int PASS>
+__global__ __launch_bounds__(kThreads) void big_tiles(Big b, uint32_t* __restrict__ amax_bits,
+                                                      const float* __restrict__ amax) {
+  __shared__ uint32_t red[4];
+  const int t = threadIdx.x;
+  const FP8BQ_GLOBAL uint16_t* x = (const FP8BQ_GLOBAL uint16_t*)b.x;
+  FP8BQ_GLOBAL uint8_t* q = (FP8BQ_GLOBAL uint8_t*)b.q;
+  for (int64_t it = blockIdx.x; it < b.items; it += gridDim.x) {
+    const int64_t tile = it / b.cpt;
+    const int64_t k = it - tile * b.cpt;
+    const int64_t ti = tile / b.TNl;
+    const int64_t tj = tile - ti * b.TNl;
+    int64_t r0, r1, c0, c1;
+    big_rect(b, ti, tj, r0, r1, c0, c1);
+    float r = 0.0f;
+    if (PASS == 1) {
+      float s;
+      tile_scale_f(((const FP8BQ_GLOBAL float*)amax)[tile], s, r);
+    }
+    uint32_t m = 0;
+    if (b.flat) {
+      // The tile is rows [r0, r1) in full: one contiguous range of elements.
+      const int64_t f0 = r0 * b.N + k * kChunk;
+      int64_t f1 = f0 + kChunk;
+      f1 = f1 > r1 * b.N ? r1 * b.N : f1;
+      if (f0 >= f1) continue;  // uniform: this chunk index lies past a short tile
+      int64_t head = f0;
+      if (b.vec) {
+        // f0 is a multiple of 8 (kChunk and N are), so 16-byte vectors from f0.
+        const int64_t nv = (f1 - f0) / 8;
+        const FP8BQ_GLOBAL u32x4* xv = (const FP8BQ_GLOBAL u32x4*)(x + f0);
+        FP8BQ_GLOBAL u32x2* qv = (FP8BQ_GLOBAL u32x2*)(q + f0);
+        for (int64_t v = t; v < nv; v += kThreads) {
+          const u32x4 w = __builtin_nontemporal_load(&xv[v]);
+          if (PASS == 0) {
+            m = max(m, halves_max(fold_abs(w)));
+          } else {
+            __builtin_nontemporal_store(quant8(w, r), &qv[v]);
+          }
+        }
+        head = f0 + nv * 8;
+      }
+      for (int64_t e = head + t; e < f1; e += kThreads) {
+        const uint32_t bits = x[e];
+        if (PASS == 0) {
+          m = max(m, bits & 0x7FFFu);
+        } else {
+          const float y = clamp448(__uint_as_float(bits << 16) * r);
+          q[e] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xFF);
+        }
+      }
+    } else {
+      // General rectangle: rows of the chunk, element by element.
+      const int64_t cols = c1 - c0;
+      const int64_t rows_per = cols >= kChunk ? 1 : kChunk / cols;
+      const int64_t ra = r0 + k * rows_per;
+      int64_t rb = ra + rows_per;
+      rb = rb > r1 ? r1 : rb;
+      if (ra >= rb) continue;  // uniform
+      const int64_t n = (rb - ra) * cols;
+      for (int64_t e = t; e < n; e += kThreads) {
+        const int64_t rr = e / cols;
+        const int64_t cc = e - rr * cols;
+        const size_t off = (size_t)(ra + rr) * b.N + c0 + cc;
+        const uint32_t bits = x[off];
+        if (PASS == 0) {
+          m = max(m, bits & 0x7FFFu);
+        } else {
+          const float y = clamp448(__uint_as_float(bits << 16) * r);
+          q[off] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xFF);
+        }
+      }
+    }
+    if (PASS == 0) {
+      const uint32_t wm = block_max(m, red);
+      if (t == 0 && wm != 0) atomicMax(&amax_bits[tile], wm << 16);
+    }
+  }
+}
+
+// out[i] = 0 for i < n.
+__global__ __launch_bounds__(kThreads) void fill_zero(uint32_t* __restrict__ out, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
+    ((FP8BQ_GLOBAL uint32_t*)out)[i] = 0u;
+  }
+}
+
+// scale[i] = fl32(max(amax[i], eps) / 448); amax and scale may be the same array.
+__global__ __launch_bounds__(kThreads) void finalize_scales(const float* amax, float* scale,
+                                                            int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
+    float s, r;
+    tile_scale_f(((const FP8BQ_GLOBAL float*)amax)[i], s, r);
+    ((FP8BQ_GLOBAL float*)scale)[i] = s;
+  }
+}
+
+// ---------------------------------------------------------------- dequantization
+//
+// The consumer side of the descale: x_hat = decode(q) * s, rounded once to
+// fp32, optionally rounded again to BF16 (nearest, ties to even).  HBM-bound:
+// 1 byte read and 4 (fp32) or 2 (BF16) bytes written per element.
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+enum OutType : int { kOutF32 = 0, kOutBF16 = 1 };
+
+// Round a finite fp32 value to BF16 bits, nearest with ties to even: add
+// half an ulp of the 16 dropped bits (minus one when the kept LSB is 0).
+__device__ __forceinline__ uint32_t bf16_rne(float y) {
+  const uint32_t b = __float_as_uint(y);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// Four e4m3fn bytes of one dword -> four floats times s.
+__device__ __forceinline__ f32x4 dq4(uint32_t w, float s) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  return f32x4{lo.x * s, lo.y * s, hi.x * s, hi.y * s};
+}
+
+// One thread per 16-byte chunk of q (16 elements in one tile: N % 16 == 0,
+// bn % 16 == 0, q and out 16-byte aligned).
+template <int OUT>
+__global__ __launch_bounds__(kThreads) void dequant_vec(const uint8_t* __restrict__ q,
+                                                        const float* __restrict__ s, int64_t N,
+                                                        int32_t bm, int32_t bn, int32_t TN,
+                                                        void* __restrict__ out, int64_t chunks) {
+  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (c >= chunks) return;
+  const int64_t cpr = N / 16;
+  const int64_t row = c / cpr;
+  const int64_t col = (c - row * cpr) * 16;
+  const float sc = ((const FP8BQ_GLOBAL float*)s)[(row / bm) * TN + col / bn];
+  const size_t off = (size_t)row * N + col;
+  const u32x4 w = __builtin_nontemporal_load((const FP8BQ_GLOBAL u32x4*)(q + off));
+  const f32x4 a = dq4(w.x, sc), b = dq4(w.y, sc), e = dq4(w.z, sc), f = dq4(w.w, sc);
+  if constexpr (OUT == kOutF32) {
+    FP8BQ_GLOBAL f32x4* o = (FP8BQ_GLOBAL f32x4*)((float*)out + off);
+    __builtin_nontemporal_store(a, o);
+    __builtin_nontemporal_store(b, o + 1);
+    __builtin_nontemporal_store(e, o + 2);
+    __builtin_nontemporal_store(f, o + 3);
+  } else {
+    FP8BQ_GLOBAL u32x4* o = (FP8BQ_GLOBAL u32x4*)((uint16_t*)out + off);
+    const u32x4 p0{bf16_rne(a.x) | (bf16_rne(a.y) << 16), bf16_rne(a.z) | (bf16_rne(a.w) << 16),
+                   bf16_rne(b.x) | (bf16_rne(b.y) << 16), bf16_rne(b.z) | (bf16_rne(b.w) << 16)};
+    const u32x4 p1{bf16_rne(e.x) | (bf16_rne(e.y) << 16), bf16_rne(e.z) | (bf16_rne(e.w) << 16),
+                   bf16_rne(f.x) | (bf16_rne(f.y) << 16), bf16_rne(f.z) | (bf16_rne(f.w) << 16)};
+    __builtin_nontemporal_store(p0, o);
+    __builtin_nontemporal_store(p1, o + 1);
+  }
+}
+
+// One thread per element: any shape, block size and alignment.
+template <int OUT>
+__global__ __launch_bounds__(kThreads) void dequant_elem(const uint8_t* __restrict__ q,
+                                                         const float* __restrict__ s, int64_t N,
+                                                         int32_t bm, int32_t bn, int32_t TN,
+                                                         void* __restrict__ out, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n; e += stride) {
+    const int64_t row = e / N;
+    const int64_t col = e - row * N;
+    const float sc = ((const FP8BQ_GLOBAL float*)s)[(row / bm) * TN + col / bn];
+    const f32x2 v2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)((const FP8BQ_GLOBAL uint8_t*)q)[e], false);
+    const float v = v2[0];
+    const float y = v * sc;
+    if constexpr (OUT == kOutF32) {
+      ((FP8BQ_GLOBAL float*)out)[e] = y;
+    } else {
+      ((FP8BQ_GLOBAL uint16_t*)out)[e] = (uint16_t)bf16_rne(y);
+    }
   }
 }
 

@@ -40,8 +40,10 @@
  *     relations section of the fp8_kernel.py page delegates to device.py).
  *   - Any block size bm, bn >= 1 and any alignment are accepted.  Blocks
  *     [128,128], [64,64] and [1,128] with N % 8 == 0, a 16-byte aligned x
- *     and an 8-byte aligned q take the vectorized kernels; everything else
- *     takes a general tile kernel with identical results.
+ *     and an 8-byte aligned q take the vectorized kernels; tiles of more
+ *     than 65536 elements take two passes (maxima, then quantization); all
+ *     other cases take a general one-workgroup-per-tile kernel.  Results are
+ *     identical whichever kernel runs.
  *   - Thread safety: calls may be made from several host threads; each
  *     thread has its own fp8bq_last_hip_error().
  */
@@ -115,6 +117,59 @@ size_t fp8bq_many_workspace_bytes(int32_t count);
  */
 int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int32_t bn,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Shards and large tiles.  A shard is an [M, N] sub-matrix of a larger
+ * matrix whose element (0,0) sits at (row_phase, col_phase) inside a tile of
+ * the full matrix's [bm, bn] grid (0 <= row_phase < bm, 0 <= col_phase < bn;
+ * both 0 for a whole matrix or a tile-aligned shard).  Its local tile grid is
+ * TMl = ceil((row_phase + M) / bm) by TNl = ceil((col_phase + N) / bn).
+ *
+ * fp8bq_tile_amax writes amax[TMl, TNl] (fp32, device): the largest |x| over
+ * the part of each tile inside this shard -- the first step of the blockwise
+ * cast of the fp8_kernel.py page (section 2) restricted to one shard.  Tiles
+ * shared by several shards (rows or columns cut inside a tile) get their
+ * full maximum as the max over those shards' partial maxima; the values are
+ * exact BF16 magnitudes, so the combination is exact in any order.
+ *
+ * fp8bq_quantize_amax quantizes the shard with the given whole-tile maxima
+ * and writes q [M, N] and scale_inv [TMl, TNl] (the shard's rows of the full
+ * scale grid).  `amax` may be the same array as `scale_inv` (converted in
+ * place), but must not partly overlap it.  Given the full maxima, every
+ * shard's bytes equal the corresponding bytes of quantizing the whole matrix.
+ *
+ * The same two-pass kernels serve fp8bq_quantize / fp8bq_quantize_many for
+ * tiles of more than 65536 elements (e.g. one scale per tensor: bm = M,
+ * bn = N), using scale_inv as the scratch for the maxima.
+ * Both calls enqueue on `stream`; the pointers follow the conventions above.
+ */
+int fp8bq_tile_amax(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, int32_t row_phase,
+                    int32_t col_phase, float* amax, void* stream);
+int fp8bq_quantize_amax(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn,
+                        int32_t row_phase, int32_t col_phase, const float* amax, void* q,
+                        float* scale_inv, void* stream);
+
+/* Output element type of fp8bq_dequantize. */
+enum fp8bq_out_dtype {
+  FP8BQ_OUT_F32 = 0,  /* float32 */
+  FP8BQ_OUT_BF16 = 1  /* bfloat16, rounded to nearest (ties to even) from the fp32 product */
+};
+
+/*
+ * Dequantize: out[i,j] = decode(q[i,j]) * scale_inv[i/bm, j/bn], the
+ * consumer side of the descale (the "descale" output of the fp8_kernel.py
+ * page, section 1; the "<name>_scale_inv" tensor of the vllm_fp8_utils.py
+ * page, section 3).  The product is rounded once to fp32; FP8BQ_OUT_BF16
+ * rounds that fp32 value to BF16 (nearest, ties to even).
+ *   q          device, e4m3fn bytes [M, N] row-major
+ *   scale_inv  device, fp32 [ceil(M/bm), ceil(N/bn)] row-major
+ *   out        device, [M, N] row-major of out_dtype (fp32 or BF16), aligned
+ *              to its element size; must not overlap q or scale_inv
+ * Any shape, block size and alignment; N % 16 == 0, bn % 16 == 0 and 16-byte
+ * aligned q/out take the vectorized kernel.  NaN codes decode to NaN.
+ */
+int fp8bq_dequantize(const void* q, const float* scale_inv, int64_t M, int64_t N, int32_t bm,
+                     int32_t bn, void* out, int32_t out_dtype, void* stream);
 
 /*
  * The final cast alone (clamp to +-448, round to e4m3fn), for checking the

@@ -23,15 +23,21 @@ Modules
 ``e4m3fn``     the 8-bit format: decode, scalar and numpy encoders.
 ``fp32``       float32 rounding helpers and BF16 widening.
 ``blockwise``  the tile pipeline: a pure-Python scalar version for tiny
-               inputs and a numpy version (per tile row) for larger ones.
+               inputs and a numpy version (per tile row) for larger ones;
+               dequantization (decode(q) * s, to float32 or BF16); partial
+               tile maxima of a shard and quantization with given maxima.
 """
 
 from .blockwise import (  # noqa: F401
     EPS,
     E4M3_MAX,
+    dequantize,
+    local_grid,
     quantize,
+    quantize_with_amax,
     quantize_scalar,
     quantize_tile,
+    tile_amax,
     tile_scale,
     tile_grid,
 )

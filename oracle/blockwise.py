@@ -32,7 +32,7 @@ import math
 
 import numpy as np
 
-from .e4m3fn import encode, encode_np
+from .e4m3fn import decode_np, encode, encode_np
 from .fp32 import bf16_bits_to_f64, bf16_bits_to_float, fl32
 
 E4M3_MAX = 448.0
@@ -152,3 +152,94 @@ def quantize(x_bits: np.ndarray, bm: int, bn: int, eps: float = EPS):
         q[r0:r1] = scale_clamp_encode(x, r_col)
         scale_inv[ti] = s.astype(np.float32)
     return q, scale_inv
+
+
+def round_to_bf16(y: np.ndarray) -> np.ndarray:
+    """Round float64 values (float32-representable, normal range) to the
+    nearest BF16 value, ties to even: 8 significant bits."""
+    y = np.asarray(y, dtype=np.float64)
+    nz = y != 0
+    a = np.abs(y[nz])
+    if np.any(a < 2.0 ** -126) or np.any(a >= 2.0 ** 128):
+        raise ValueError("BF16 rounding here covers the normal range only")
+    frac, exp = np.frexp(y[nz])                    # y = frac * 2**exp, 0.5 <= |frac| < 1
+    out = y.copy()
+    out[nz] = np.ldexp(np.rint(frac * 256.0) / 256.0, exp)   # np.rint: half to even
+    return out
+
+
+def dequantize(q: np.ndarray, scale_inv: np.ndarray, bm: int, bn: int, out: str = "f32"):
+    """Dequantization, the consumer side of the descale: x_hat = decode(q) * s.
+
+    The page "fp8_kernel.py — FP8 量化内核" (section 1) calls the second
+    output the descale, and the "vllm_fp8_utils.py" page (section 3) names
+    it ``<weight>_scale_inv``: the stored value multiplies the FP8 value back.
+    The product is rounded once to float32; ``out="bf16"`` rounds that
+    float32 to the nearest BF16 (ties to even).  Returns float64 holding the
+    float32 or BF16 values.
+    """
+    q = np.asarray(q, dtype=np.uint8)
+    M, N = q.shape
+    TM, TN = tile_grid(M, N, bm, bn)
+    s = np.asarray(scale_inv, dtype=np.float32).astype(np.float64)
+    if s.shape != (TM, TN):
+        raise ValueError(f"scale_inv shape {s.shape} != {(TM, TN)}")
+    s_full = np.repeat(np.repeat(s, bm, axis=0)[:M], bn, axis=1)[:, :N]
+    y = (decode_np(q) * s_full).astype(np.float32).astype(np.float64)     # fl32(v * s)
+    if out == "f32":
+        return y
+    if out == "bf16":
+        return round_to_bf16(y)
+    raise ValueError("out must be 'f32' or 'bf16'")
+
+
+def local_grid(M: int, N: int, bm: int, bn: int, row_phase: int = 0, col_phase: int = 0):
+    """Tile grid of an [M, N] sub-matrix whose element (0, 0) sits at
+    (row_phase, col_phase) inside a tile of the full matrix's grid."""
+    if not (0 <= row_phase < bm and 0 <= col_phase < bn):
+        raise ValueError("phases must satisfy 0 <= phase < block")
+    return -(-(row_phase + M) // bm), -(-(col_phase + N) // bn)
+
+
+def tile_amax(x_bits: np.ndarray, bm: int, bn: int, row_phase: int = 0, col_phase: int = 0):
+    """Largest |x| of each tile's part inside a sub-matrix (float64 [TMl, TNl]).
+
+    For a sub-matrix cut out of a larger matrix (a shard), the maximum of
+    each tile of the full matrix is the max over the shards of these partial
+    maxima; the tile maximum is the first step of the blockwise cast (page
+    "fp8_kernel.py — FP8 量化内核", section 2).
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    M, N = x_bits.shape
+    TM, TN = local_grid(M, N, bm, bn, row_phase, col_phase)
+    out = np.zeros((TM, TN), dtype=np.float64)
+    if M == 0 or N == 0:
+        return out
+    a = np.abs(bf16_bits_to_f64(x_bits))
+    if not np.all(np.isfinite(a)):
+        raise ValueError("non-finite input is outside the quantizer's contract")
+    padded = np.zeros((TM * bm, TN * bn), dtype=np.float64)
+    padded[row_phase:row_phase + M, col_phase:col_phase + N] = a
+    return padded.reshape(TM, bm, TN, bn).max(axis=(1, 3))
+
+
+def quantize_with_amax(x_bits: np.ndarray, bm: int, bn: int, amax: np.ndarray,
+                       row_phase: int = 0, col_phase: int = 0, eps: float = EPS):
+    """Quantize a sub-matrix with given whole-tile maxima (float64 [TMl, TNl]):
+    scales and reciprocals from ``amax`` exactly as in ``tile_scales_np``,
+    then each element scaled by its tile's reciprocal, clamped and encoded.
+    Returns (q uint8 [M, N], scale_inv float32 [TMl, TNl])."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    M, N = x_bits.shape
+    TM, TN = local_grid(M, N, bm, bn, row_phase, col_phase)
+    amax = np.asarray(amax, dtype=np.float64)
+    if amax.shape != (TM, TN):
+        raise ValueError(f"amax shape {amax.shape} != {(TM, TN)}")
+    s, r = tile_scales_np(amax, eps)
+    q = np.empty((M, N), dtype=np.uint8)
+    if M and N:
+        rows = (np.arange(M) + row_phase) // bm
+        cols = (np.arange(N) + col_phase) // bn
+        r_full = r[rows][:, cols]
+        q[:] = scale_clamp_encode(bf16_bits_to_f64(x_bits), r_full)
+    return q, s.astype(np.float32)

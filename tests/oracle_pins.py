@@ -370,6 +370,112 @@ def pin_tile_independence(quick=True):
         assert np.array_equal(s[1:, 2:], s2)
 
 
+# ---------------------------------------------------------------- dequantization
+
+def pin_dequant_bruteforce(quick=True):
+    """decode(q) * s rounded once to float32: equal to exact arithmetic with a
+    nearest-float32 search; the BF16 output equals torch's CPU
+    float32 -> bfloat16 cast (a library routine)."""
+    rng = _rng(23)
+    n = 300 if quick else 3000
+    codes = rng.integers(0, 256, (1, n)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x7E                     # no NaN codes
+    bm, bn = 1, 1
+    scales = _f32(np.exp2(rng.uniform(-40, 40, (1, n))))
+    got = oracle.dequantize(codes, scales, bm, bn, "f32")
+    got16 = oracle.dequantize(codes, scales, bm, bn, "bf16")
+    for j in range(n):
+        v = bf.E4M3_POS_VALUES[int(codes[0, j]) & 0x7F] * (-1 if codes[0, j] & 0x80 else 1)
+        want = bf.nearest_f32(v * Fraction(float(scales[0, j])), negative_zero=bool(codes[0, j] & 0x80))
+        assert got[0, j] == float(want), (int(codes[0, j]), float(scales[0, j]))
+    ref16 = torch.from_numpy(got.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(ref16.astype(np.float64), got16)
+    big = _f32(np.exp2(rng.uniform(-120, 120, 200_000 if not quick else 20_000)) *
+               rng.choice([-1.0, 1.0], 200_000 if not quick else 20_000))
+    ref = torch.from_numpy(big).to(torch.bfloat16).float().numpy().astype(np.float64)
+    assert np.array_equal(oracle.blockwise.round_to_bf16(big.astype(np.float64)), ref)
+
+
+def pin_dequant_roundtrip(quick=True):
+    """I3 through dequantization: e4m3 multiples come back exactly (float32
+    and BF16); I4: the float32 dequantized error stays within half an e4m3
+    ulp of the scaled value times s (plus float32 rounding)."""
+    rng = _rng(29)
+    pos = np.array([float(v) for v in bf.E4M3_POS_VALUES])
+    for k in range(-20, 20, 9 if quick else 3):
+        c = rng.choice(pos, size=(8, 32)) * rng.choice([-1.0, 1.0], size=(8, 32))
+        c[0, 0] = 448.0
+        x = c * 2.0 ** k
+        bits = _bits_of(_f32(x))
+        q, s = oracle.quantize(bits, 8, 32)                  # one tile holding the 448
+        for out in ("f32", "bf16"):
+            assert np.array_equal(oracle.dequantize(q, s, 8, 32, out), x), (k, out)
+    for name, bits, bm, bn in _inv_inputs(True)[:3]:
+        q, s = oracle.quantize(bits, bm, bn)
+        xf = oracle.bf16_bits_to_f64(bits)
+        xh = oracle.dequantize(q, s, bm, bn, "f32")
+        s_full = np.repeat(np.repeat(s.astype(np.float64), bm, 0)[:bits.shape[0]], bn, 1)[:, :bits.shape[1]]
+        y = np.abs(xf) / s_full
+        e = np.floor(np.log2(np.maximum(y, 2.0 ** -6)))
+        ulp = np.where(y >= 2.0 ** -6, np.exp2(e - 3), 2.0 ** -9)
+        assert np.all(np.abs(xf - xh) <= 0.5 * ulp * s_full + 2.0 ** -21 * np.abs(xf)), name
+
+
+# ---------------------------------------------------------------- shards
+
+def shard_quantize(bits, bm, bn, row_cuts, col_cuts, amax_fn, quant_fn):
+    """Quantize a matrix shard by shard: partial maxima per shard, combined by
+    max over the shards that share a tile, then each shard quantized with the
+    combined maxima.  Returns the re-assembled (q, scale_inv)."""
+    M, N = bits.shape
+    TM, TN = oracle.tile_grid(M, N, bm, bn)
+    rb = [0] + list(row_cuts) + [M]
+    cb = [0] + list(col_cuts) + [N]
+    full = np.zeros((TM, TN))
+    parts = []
+    for i in range(len(rb) - 1):
+        for j in range(len(cb) - 1):
+            r0, r1, c0, c1 = rb[i], rb[i + 1], cb[j], cb[j + 1]
+            if r0 == r1 or c0 == c1:
+                continue
+            rp, cp = r0 % bm, c0 % bn
+            a = amax_fn(np.ascontiguousarray(bits[r0:r1, c0:c1]), bm, bn, rp, cp)
+            t0, u0 = r0 // bm, c0 // bn
+            view = full[t0:t0 + a.shape[0], u0:u0 + a.shape[1]]
+            np.maximum(view, a, out=view)
+            parts.append((r0, r1, c0, c1, rp, cp, t0, u0))
+    q = np.zeros((M, N), dtype=np.uint8)
+    s_out = np.zeros((TM, TN), dtype=np.float32)
+    for r0, r1, c0, c1, rp, cp, t0, u0 in parts:
+        TMl, TNl = oracle.local_grid(r1 - r0, c1 - c0, bm, bn, rp, cp)
+        qs, ss = quant_fn(np.ascontiguousarray(bits[r0:r1, c0:c1]), bm, bn,
+                          full[t0:t0 + TMl, u0:u0 + TNl], rp, cp)
+        q[r0:r1, c0:c1] = qs
+        s_out[t0:t0 + TMl, u0:u0 + TNl] = ss
+    return q, s_out
+
+
+def pin_shards_equal_whole(quick=True):
+    """Sharded quantization (partial maxima exchanged as a max over the shards
+    sharing a tile, cuts anywhere, including inside tiles) equals quantizing
+    the whole matrix; and whole-matrix maxima reproduce ``quantize``."""
+    rng = _rng(37)
+    cases = [(300, 520, 128, 128), (77, 200, 64, 64), (129, 257, 1, 128), (50, 60, 7, 9),
+             (200, 300, 200, 300)]
+    for M, N, bm, bn in cases[: 3 if quick else None]:
+        bits = _random_bf16(rng, (M, N))
+        q_ref, s_ref = oracle.quantize(bits, bm, bn)
+        a = oracle.tile_amax(bits, bm, bn)
+        q1, s1 = oracle.quantize_with_amax(bits, bm, bn, a)
+        assert np.array_equal(q1, q_ref) and np.array_equal(s1.view(np.uint32), s_ref.view(np.uint32))
+        for _ in range(2 if quick else 6):
+            rc = sorted(set(int(v) for v in rng.integers(1, M, rng.integers(0, 4))))
+            cc = sorted(set(int(v) for v in rng.integers(1, N, rng.integers(0, 3))))
+            q2, s2 = shard_quantize(bits, bm, bn, rc, cc, oracle.tile_amax, oracle.quantize_with_amax)
+            assert np.array_equal(q2, q_ref), (M, N, bm, bn, rc, cc)
+            assert np.array_equal(s2.view(np.uint32), s_ref.view(np.uint32)), (M, N, bm, bn, rc, cc)
+
+
 PINS = [
     pin_decode_matches_torch,
     pin_format_golden,
@@ -384,4 +490,7 @@ PINS = [
     pin_invariants,
     pin_roundtrip_e4m3_multiples,
     pin_tile_independence,
+    pin_dequant_bruteforce,
+    pin_dequant_roundtrip,
+    pin_shards_equal_whole,
 ]

@@ -16,6 +16,12 @@ import fp8_blockwise_weight_amd as fq
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fp8bq.h")
 
+# These calls pass fake device addresses; they are only ever run where no GPU
+# is visible, so even a wrongly accepted call cannot reach a kernel.
+pytestmark = pytest.mark.skipif(
+    __import__("torch").cuda.device_count() > 0,
+    reason="fake-pointer validation tests run only on machines without a visible GPU")
+
 INVALID = fq.ERR_INVALID_ARGUMENT
 WORKSPACE = fq.ERR_WORKSPACE
 
@@ -130,6 +136,43 @@ def test_encode_rejects(lib):
     assert lib.fp8bq_encode_e4m3(X + 2, Q, 10, None) == INVALID
     assert lib.fp8bq_encode_e4m3(X, X + 8, 10, None) == INVALID     # overlap
     assert lib.fp8bq_encode_e4m3(None, None, 0, None) == fq.OK
+
+
+def test_dequantize_rejects(lib):
+    f = lib.fp8bq_dequantize
+    assert f(Q, S, -1, 128, 128, 128, X, 0, None) == INVALID        # negative M
+    assert f(Q, S, 128, 128, 0, 128, X, 0, None) == INVALID         # bm < 1
+    assert f(Q, S, 128, 128, 128, 128, X, 2, None) == INVALID       # unknown out dtype
+    assert f(None, S, 128, 128, 128, 128, X, 0, None) == INVALID    # null q
+    assert f(Q, None, 128, 128, 128, 128, X, 0, None) == INVALID    # null scale
+    assert f(Q, S, 128, 128, 128, 128, None, 0, None) == INVALID    # null out
+    assert f(Q, S + 1, 128, 128, 128, 128, X, 0, None) == INVALID   # scale misaligned
+    assert f(Q, S, 128, 128, 128, 128, X + 1, 1, None) == INVALID   # bf16 out misaligned
+    assert f(Q, S, 128, 128, 128, 128, X + 2, 0, None) == INVALID   # fp32 out misaligned
+    assert f(Q, S, 128, 128, 128, 128, Q + 64, 0, None) == INVALID  # out overlaps q
+    assert f(Q, S, 128, 128, 128, 128, S - 64, 0, None) == INVALID  # out overlaps scale
+    assert f(None, None, 0, 128, 128, 128, None, 0, None) == fq.OK
+
+
+def test_shard_calls_reject(lib):
+    ta, qa = lib.fp8bq_tile_amax, lib.fp8bq_quantize_amax
+    A = 0x50_0000_0000
+    assert ta(X, 128, 128, 128, 128, 128, 0, A, None) == INVALID     # row phase >= bm
+    assert ta(X, 128, 128, 128, 128, 0, -1, A, None) == INVALID      # negative phase
+    assert ta(X, 128, 128, 0, 128, 0, 0, A, None) == INVALID         # bm < 1
+    assert ta(None, 128, 128, 128, 128, 0, 0, A, None) == INVALID
+    assert ta(X, 128, 128, 128, 128, 0, 0, None, None) == INVALID
+    assert ta(X, 128, 128, 128, 128, 0, 0, A + 2, None) == INVALID   # amax misaligned
+    assert ta(X, 128, 128, 128, 128, 0, 0, X + 64, None) == INVALID  # amax overlaps x
+    assert ta(None, 0, 128, 128, 128, 0, 0, None, None) == fq.OK
+    assert qa(X, 128, 128, 128, 128, 0, 128, A, Q, S, None) == INVALID   # col phase >= bn
+    assert qa(X, 128, 128, 128, 128, 0, 0, None, Q, S, None) == INVALID
+    assert qa(X, 128, 128, 128, 128, 0, 0, A, None, S, None) == INVALID
+    assert qa(X, 128, 128, 128, 128, 0, 0, A, Q, None, None) == INVALID
+    # amax [8, 8] floats at S, scale_inv at S + 4: the two ranges partly overlap
+    assert qa(X, 1024, 1024, 128, 128, 0, 0, S + 0, Q, S + 4, None) == INVALID
+    assert qa(X, 128, 128, 128, 128, 0, 0, A, X + 2, S, None) == INVALID      # q overlaps x
+    assert qa(None, 5, 0, 128, 128, 0, 0, None, None, None, None) == fq.OK
 
 
 def test_python_block_size_checks():

@@ -330,3 +330,173 @@ def test_c4_moe_per_layer_grouped(gpu_lib, part):
                                       sample_tiles(*x.shape, 128, 128, 2, seed=layer * 256 + k),
                                       specs[k].name)
         del xs, outs
+
+
+# ------------------------------------------------------------------ dequantization
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_dequant_matches_oracle(gpu_lib, out_dtype):
+    """decode(q) * s on the GPU equals the oracle, bit for bit, on the vector
+    kernel (N % 16 == 0, bn % 16 == 0, aligned) and the element-wise kernel."""
+    tdt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    g = torch.Generator(device=DEV).manual_seed(31)
+    cases = [(256, 256, (128, 128)), (1000, 3000, (64, 64)), (77, 128, (1, 128)),
+             (4097, 1008, (128, 128)), (129, 1001, (128, 128)), (300, 520, (3, 5)),
+             (65, 48, (16, 16)), (33, 40, (1, 1))]
+    for M, N, block in cases:
+        say("dequant", out_dtype, M, N, block)
+        x = (torch.randn((M, N), generator=g, device=DEV) * 0.05).to(torch.bfloat16)
+        x[0] = 0
+        q, s = fq.quantize(x, block)
+        xh = fq.dequantize(q, s, block, out_dtype=tdt)
+        torch.cuda.synchronize()
+        want = oracle.dequantize(codes_np(q), s.cpu().numpy(), *block, out_dtype)
+        got = xh.float().cpu().numpy().astype(np.float64)
+        bad = np.nonzero(got != want)
+        assert bad[0].size == 0, (M, N, block, bad[0].size)
+        # misaligned q and out take the element-wise kernel
+        qb = torch.empty(M * N + 16, dtype=torch.uint8, device=DEV)
+        q2 = qb[1:1 + M * N].view(M, N)
+        q2.copy_(q.view(torch.uint8))
+        ob = torch.empty(M * N + 8, dtype=tdt, device=DEV)
+        o2 = ob[1:1 + M * N].view(M, N)
+        fq.dequantize(q2, s, block, out_dtype=tdt, out=o2)
+        assert torch.equal(o2.float(), xh.float())
+
+
+def test_dequant_roundtrip_bound_layer(gpu_lib):
+    """I4 over a whole Qwen3-8B-shaped layer on the GPU: |x - dequant(q)| is
+    within half an e4m3 ulp of the scaled value times s (+ fp32 rounding)."""
+    for sp in wl.c2():
+        x = wl.materialize(sp, DEV)
+        q, s = fq.quantize(x, (128, 128))
+        xh = fq.dequantize(q, s, (128, 128)).double()
+        xd = x.double()
+        sf = s.double().repeat_interleave(128, 0)[:sp.M].repeat_interleave(128, 1)[:, :sp.N]
+        y = xd.abs() / sf
+        e = torch.floor(torch.log2(torch.clamp(y, min=2.0 ** -6)))
+        ulp = torch.where(y >= 2.0 ** -6, torch.exp2(e - 3), torch.full_like(y, 2.0 ** -9))
+        ok = (xd - xh).abs() <= 0.5 * ulp * sf + 2.0 ** -21 * xd.abs()
+        assert bool(ok.all()), sp.name
+        del x, q, s, xh, xd, sf, y, e, ulp, ok
+
+
+# ------------------------------------------------------------------ large tiles and shards
+
+def _shards(x, block, row_cuts, col_cuts):
+    """Quantize ``x`` shard by shard on the GPU: partial maxima per shard,
+    an element-wise max over shards sharing a tile (the exchange), then
+    each shard quantized with the full maxima; returns assembled (q, s)."""
+    bm, bn = block
+    M, N = x.shape
+    TM, TN = fq.scale_shape(M, N, bm, bn)
+    full = torch.zeros((TM, TN), dtype=torch.float32, device=DEV)
+    rb, cb = [0] + row_cuts + [M], [0] + col_cuts + [N]
+    parts = []
+    for i in range(len(rb) - 1):
+        for j in range(len(cb) - 1):
+            r0, r1, c0, c1 = rb[i], rb[i + 1], cb[j], cb[j + 1]
+            if r0 == r1 or c0 == c1:
+                continue
+            xs = x[r0:r1, c0:c1].contiguous()
+            ph = (r0 % bm, c0 % bn)
+            a = fq.tile_amax(xs, block, ph)
+            t0, u0 = r0 // bm, c0 // bn
+            v = full[t0:t0 + a.shape[0], u0:u0 + a.shape[1]]
+            v.copy_(torch.maximum(v, a))
+            parts.append((r0, r1, c0, c1, xs, ph, t0, u0, a.shape))
+    q = torch.empty((M, N), dtype=torch.uint8, device=DEV)
+    s = torch.empty((TM, TN), dtype=torch.float32, device=DEV)
+    for r0, r1, c0, c1, xs, ph, t0, u0, shp in parts:
+        am = full[t0:t0 + shp[0], u0:u0 + shp[1]].contiguous()
+        qs, ss = fq.quantize_with_amax(xs, am, block, ph)
+        q[r0:r1, c0:c1] = qs.view(torch.uint8)
+        s[t0:t0 + shp[0], u0:u0 + shp[1]] = ss
+    return q, s
+
+
+def test_tile_amax_and_quantize_amax_match_oracle(gpu_lib):
+    g = torch.Generator(device=DEV).manual_seed(41)
+    rng = np.random.default_rng(41)
+    for M, N, block in [(300, 520, (128, 128)), (77, 200, (64, 64)), (129, 257, (1, 128)),
+                        (50, 61, (7, 9)), (1000, 3000, (512, 512)), (64, 100000, (1, 100000))]:
+        bm, bn = block
+        for _ in range(3):
+            ph = (int(rng.integers(bm)), int(rng.integers(bn)))
+            say("amax", M, N, block, ph)
+            x = (torch.randn((M, N), generator=g, device=DEV) * 0.05).to(torch.bfloat16)
+            a = fq.tile_amax(x, block, ph)
+            xb = bits_np(x)
+            a_ref = oracle.tile_amax(xb, bm, bn, *ph)
+            assert np.array_equal(a.cpu().numpy().astype(np.float64), a_ref)
+            q, s = fq.quantize_with_amax(x, a, block, ph)
+            q_ref, s_ref = oracle.quantize_with_amax(xb, bm, bn, a_ref, *ph)
+            assert np.array_equal(codes_np(q), q_ref)
+            assert np.array_equal(scales_bits(s), scales_bits(s_ref))
+
+
+def test_shards_equal_whole(gpu_lib):
+    """Cuts anywhere (inside tiles too): shard-wise maxima, exchanged as a
+    max, then shard-wise quantization reproduce the whole-matrix bytes."""
+    g = torch.Generator(device=DEV).manual_seed(43)
+    rng = np.random.default_rng(43)
+    for M, N, block in [(1000, 3000, (128, 128)), (4097, 1024, (64, 64)), (300, 640, (1, 128)),
+                        (1536, 2048, (128, 128))]:
+        x = (torch.randn((M, N), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+        q_ref, s_ref = fq.quantize(x, block)
+        for _ in range(4):
+            rc = sorted(set(int(v) for v in rng.integers(1, M, rng.integers(1, 5))))
+            cc = sorted(set(int(v) for v in rng.integers(1, N, rng.integers(0, 3))))
+            say("shards", M, N, block, rc, cc)
+            q, s = _shards(x, block, rc, cc)
+            assert torch.equal(q, q_ref.view(torch.uint8)), (rc, cc)
+            assert torch.equal(s.view(torch.int32), s_ref.view(torch.int32)), (rc, cc)
+
+
+def test_per_tensor_and_large_tiles(gpu_lib):
+    """Tiles above 65536 elements (one scale per tensor, wide rows, big
+    squares) through fp8bq_quantize and the grouped call."""
+    g = torch.Generator(device=DEV).manual_seed(47)
+    for M, N, block in [(1000, 3000, (1000, 3000)), (4097, 1008, (4097, 1008)),
+                        (300, 520, (512, 512)), (33, 70001, (1, 70001)), (129, 1001, (129, 1001)),
+                        (1536, 2048, (1024, 1024))]:
+        say("large", M, N, block)
+        x = (torch.randn((M, N), generator=g, device=DEV) * 0.05).to(torch.bfloat16)
+        x[0] = 0
+        q, s = fq.quantize(x, block)
+        assert_matches_oracle(x, q, s, *block, f"large {M}x{N}/{block}")
+    # misaligned x / odd N take the scalar paths of the same kernels
+    big = (torch.randn(999 * 1001 + 8, generator=g, device=DEV)).to(torch.bfloat16)
+    x = big[3:3 + 999 * 1001].view(999, 1001)
+    q, s = fq.quantize(x, (999, 1001))
+    assert_matches_oracle(x, q, s, 999, 1001, "large misaligned")
+    # grouped call with per-tensor blocks: one scale per tensor for the C2 layer
+    specs = wl.c2()
+    xs = [wl.materialize(sp, DEV) for sp in specs]
+    outs = fq.quantize_many(xs, (16384, 16384))
+    for sp, x, (q, s) in zip(specs, xs, outs):
+        assert s.shape == (1, 1)
+        amax = float(x.abs().max().float())
+        assert float(s[0, 0]) == float(np.float32(max(amax, np.float32(1e-10)) / 448.0)), sp.name
+        q1, s1 = fq.quantize(x, (16384, 16384))
+        assert torch.equal(q1.view(torch.uint8), q.view(torch.uint8)), sp.name
+        rows = slice(0, 64)
+        q_ref, _ = oracle.quantize_with_amax(bits_np(x[rows].contiguous()), 16384, 16384,
+                                             np.array([[amax]]))
+        assert np.array_equal(codes_np(q[rows].contiguous()), q_ref), sp.name
+        assert_properties_gpu(x, q, s, sp.M, sp.N, sp.name)
+
+
+def test_per_tensor_vocab_matrix(gpu_lib):
+    """One scale for the whole 151937x4096 matrix (1.2 GB): the scale from the
+    exact maximum, sampled rows against the oracle, invariants everywhere."""
+    sp = [t for t in wl.c5() if t.M == 151937][0]
+    x = wl.materialize(sp, DEV)
+    q, s = fq.quantize(x, (sp.M, sp.N))
+    amax = float(x.abs().max().float())
+    assert float(s[0, 0]) == float(np.float32(max(amax, np.float32(1e-10)) / 448.0))
+    for r0 in (0, 1, 77777, sp.M - 300):
+        xs = x[r0:r0 + 300].contiguous()
+        q_ref, _ = oracle.quantize_with_amax(bits_np(xs), sp.M, sp.N, np.array([[amax]]))
+        assert np.array_equal(codes_np(q[r0:r0 + 300].contiguous()), q_ref), r0
+    assert_properties_gpu(x, q, s, sp.M, sp.N, "vocab per-tensor")

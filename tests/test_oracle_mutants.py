@@ -159,6 +159,40 @@ def m_columns_shifted(mp):
     mp.setattr(blockwise, "scale_clamp_encode", sce)
 
 
+def m_dequant_divides(mp):
+    """Dequantization divides by the descale instead of multiplying."""
+    orig = blockwise.dequantize
+
+    def deq(q, scale_inv, bm, bn, out="f32"):
+        inv = (1.0 / np.asarray(scale_inv, dtype=np.float64)).astype(np.float32)
+        return orig(q, inv, bm, bn, out)
+    mp.setattr(blockwise, "dequantize", deq)
+    mp.setattr(oracle, "dequantize", deq)
+
+
+def m_bf16_truncates(mp):
+    """BF16 output truncated (rounded toward zero) instead of rounded to nearest even."""
+    def rt(y):
+        y = np.asarray(y, dtype=np.float64)
+        b = y.astype(np.float32).view(np.uint32) & np.uint32(0xFFFF0000)
+        return b.view(np.float32).astype(np.float64)
+    mp.setattr(blockwise, "round_to_bf16", rt)
+
+
+def m_phase_ignored(mp):
+    """Shard maxima computed as if every shard started on a tile boundary."""
+    orig = blockwise.tile_amax
+
+    def ta(x_bits, bm, bn, row_phase=0, col_phase=0):
+        a = orig(x_bits, bm, bn, 0, 0)
+        TM, TN = blockwise.local_grid(*np.asarray(x_bits).shape, bm, bn, row_phase, col_phase)
+        out = np.zeros((TM, TN))
+        out[:min(TM, a.shape[0]), :min(TN, a.shape[1])] = a[:TM, :TN]
+        return out
+    mp.setattr(blockwise, "tile_amax", ta)
+    mp.setattr(oracle, "tile_amax", ta)
+
+
 MUTANTS = [
     m_single_division,
     m_no_eps_floor,
@@ -171,6 +205,9 @@ MUTANTS = [
     m_amax_drops_last_row,
     m_no_float32_product,
     m_columns_shifted,
+    m_dequant_divides,
+    m_bf16_truncates,
+    m_phase_ignored,
 ]
 
 
