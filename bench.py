@@ -30,7 +30,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
 METRIC = "blockwise FP8 quantize GB/s (bf16 in + fp8/scale out), % of HBM peak, 1 GPU"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_group_t128_dense36_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_t128_dense36_traffic.md")
 KERNEL_SOURCES = ("fp8_blockwise_weight_amd/csrc/kernels.hpp", "fp8_blockwise_weight_amd/csrc/fp8bq.hip")
 
 
@@ -64,6 +64,15 @@ def committed_traffic():
     if not rec or rec.get("kernel_sha") != kernel_sha():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def group_kernel_name(kind, count):
+    """Kernel a grouped call of `count` tensors launches (table in the kernel
+    arguments up to 512 tensors, else in a workspace)."""
+    if count <= 512:
+        cap = 8 if count <= 8 else (64 if count <= 64 else 512)
+        return f"fp8bq::quantize_group_args<{kind},{cap}>"
+    return f"fp8bq::quantize_group<{kind}>"
 
 
 def build_workload(name, dev, block=None):
@@ -208,7 +217,8 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": traffic,
-        "kernel": f"fp8bq::quantize_group<{kind}> ({'one launch' if launches == 1 else f'{launches} launches'} per step)",
+        "kernel": f"{group_kernel_name(kind, max(c for _, c, _ in calls))} "
+                  f"({'one launch' if launches == 1 else f'{launches} launches'} per step)",
         "bytes_per_launch": bytes_per_launch,
         "mean_launch_ms": round(mean_launch_ms, 4),
     }

@@ -30,6 +30,15 @@ constexpr int kMaxDevices = 64;
 constexpr int64_t kMaxUnits = INT32_MAX;  // work units per tensor (32-bit unit math)
 constexpr int64_t kMaxGrid = INT32_MAX;   // workgroups per launch
 
+// Dynamic LDS reserved (and left unused) by every vectorized quantize launch
+// so that at most 4 workgroups share a CU (160 KB of LDS per gfx950 CU).
+// With fewer 32 KB tiles in flight per CU the HBM stream runs faster:
+// measured on MI355X, the dense 36-layer set goes from 76.0% to 77.1% of
+// peak and per-layer MoE launches from 73.6% to 76.5% (8 -> 4 per CU).
+constexpr unsigned kVecLds = 36 * 1024;
+
+constexpr unsigned lds_for(int kind) { return kind == fp8bq::kGeneral ? 0u : kVecLds; }
+
 // Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
 std::atomic<int> g_arch_state[kMaxDevices];
 
@@ -117,14 +126,16 @@ unsigned grid_for(int64_t units) {
 
 template <int KIND>
 void launch_one(const Desc& d, int32_t bm, int32_t bn, int64_t units, hipStream_t st) {
-  hipLaunchKernelGGL(fp8bq::quantize_one<KIND>, dim3(grid_for(units)), dim3(fp8bq::kThreads), 0,
+  hipLaunchKernelGGL(fp8bq::quantize_one<KIND>, dim3(grid_for(units)), dim3(fp8bq::kThreads),
+                     lds_for(KIND),
                      st, d, bm, bn, units);
 }
 
 template <int KIND>
 void launch_group(const Desc* descs, const int64_t* start, int32_t count, int32_t bm, int32_t bn,
                   int64_t units, hipStream_t st) {
-  hipLaunchKernelGGL(fp8bq::quantize_group<KIND>, dim3(grid_for(units)), dim3(fp8bq::kThreads), 0,
+  hipLaunchKernelGGL(fp8bq::quantize_group<KIND>, dim3(grid_for(units)), dim3(fp8bq::kThreads),
+                     lds_for(KIND),
                      st, descs, start, count, bm, bn, units);
 }
 
@@ -191,6 +202,44 @@ void launch_big_quant(const fp8bq::Big& b, const float* amax, float* scale_inv, 
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+template <int KIND, int CAP>
+void launch_args(const std::vector<Desc>& ds, const std::vector<int64_t>& st, int32_t bm,
+                 int32_t bn, int64_t total, hipStream_t s) {
+  fp8bq::GroupArgs<CAP> a;
+  std::memset(&a, 0, sizeof(a));
+  const int32_t n = static_cast<int32_t>(ds.size());
+  for (int32_t i = 0; i < n; ++i) {
+    a.start[i] = static_cast<int32_t>(st[i]);
+    a.t[i].x = ds[i].x;
+    a.t[i].q = ds[i].q;
+    a.t[i].s = ds[i].s;
+    a.t[i].M = static_cast<int32_t>(ds[i].M);
+    a.t[i].N = static_cast<int32_t>(ds[i].N);
+    a.t[i].general = ds[i].general;
+  }
+  a.start[n] = static_cast<int32_t>(total);
+  hipLaunchKernelGGL((fp8bq::quantize_group_args<KIND, CAP>), dim3(static_cast<unsigned>(total)),
+                     dim3(fp8bq::kThreads), lds_for(KIND), s, a, n, bm, bn,
+                     static_cast<int32_t>(total));
+}
+
+template <int KIND>
+void launch_args_kind(const std::vector<Desc>& ds, const std::vector<int64_t>& st, int32_t bm,
+                      int32_t bn, int64_t total, hipStream_t s) {
+  const size_t n = ds.size();
+  if (n <= 8) {
+    launch_args<KIND, 8>(ds, st, bm, bn, total, s);
+  } else if (n <= 64) {
+    launch_args<KIND, 64>(ds, st, bm, bn, total, s);
+  } else {
+    launch_args<KIND, fp8bq::kArgsMax>(ds, st, bm, bn, total, s);
+  }
+}
+
+// Host copies of a grouped call's table, reused per thread.
+thread_local std::vector<Desc> g_descs;
+thread_local std::vector<int64_t> g_starts;
+
 size_t descs_bytes(int32_t count) { return align_up(sizeof(Desc) * static_cast<size_t>(count), 256); }
 
 // Host staging of one grouped call's descriptor table, reused per thread.
@@ -231,7 +280,7 @@ int fp8bq_quantize(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, 
 }
 
 size_t fp8bq_many_workspace_bytes(int32_t count) {
-  if (count <= 0) return 0;
+  if (count <= fp8bq::kArgsMax) return 0;  // the table travels in the kernel arguments
   return descs_bytes(count) + align_up(sizeof(int64_t) * (static_cast<size_t>(count) + 1), 256);
 }
 
@@ -241,35 +290,34 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
   if (count == 0) return FP8BQ_OK;
   if (list == nullptr) return FP8BQ_ERR_INVALID_ARGUMENT;
   const size_t need = fp8bq_many_workspace_bytes(count);
-  if (workspace == nullptr || workspace_bytes < need ||
-      (reinterpret_cast<uintptr_t>(workspace) & 15) != 0) {
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need ||
+                   (reinterpret_cast<uintptr_t>(workspace) & 15) != 0)) {
     return FP8BQ_ERR_WORKSPACE;
   }
   const int kind = kind_of(bm, bn);
-  g_stage.resize(need);
-  Desc* descs = reinterpret_cast<Desc*>(g_stage.data());
-  int64_t* start = reinterpret_cast<int64_t*>(g_stage.data() + descs_bytes(count));
-  int32_t n = 0;
+  g_descs.clear();
+  g_starts.clear();
   int64_t total = 0;
   bool any_big = false;
   for (int32_t i = 0; i < count; ++i) {
     const fp8bq_tensor& t = list[i];
     int64_t units = 0;
-    Desc scratch;
-    const int st = make_desc(t.x, t.M, t.N, bm, bn, t.q, t.scale_inv, kind, &scratch, &units);
+    Desc d;
+    const int st = make_desc(t.x, t.M, t.N, bm, bn, t.q, t.scale_inv, kind, &d, &units);
     if (st != FP8BQ_OK) return st;
     if (units == 0) continue;
     if (big_tiles(t.M, t.N, bm, bn)) {  // two-pass path, launched per tensor below
       any_big = true;
       continue;
     }
-    descs[n] = scratch;
-    start[n] = total;
+    g_descs.push_back(d);
+    g_starts.push_back(total);
     total += units;
-    ++n;
   }
+  const int32_t n = static_cast<int32_t>(g_descs.size());
   if (n == 0 && !any_big) return FP8BQ_OK;
-  start[n] = total;
+  // Each launch covers at most kMaxGrid units.
+  if (total > kMaxGrid) return FP8BQ_ERR_INVALID_ARGUMENT;
   int st = device_check();
   if (st != FP8BQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -282,26 +330,36 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
       launch_big_amax(b, t.scale_inv, s);
       launch_big_quant(b, t.scale_inv, t.scale_inv, s);
     }
-    if (n == 0) {
-      const hipError_t e = hipGetLastError();
-      return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
+  }
+  if (n > 0 && n <= fp8bq::kArgsMax) {
+    // The table travels in the kernel arguments: no copy, no workspace.
+    switch (kind) {
+      case fp8bq::kT128: launch_args_kind<fp8bq::kT128>(g_descs, g_starts, bm, bn, total, s); break;
+      case fp8bq::kT64: launch_args_kind<fp8bq::kT64>(g_descs, g_starts, bm, bn, total, s); break;
+      case fp8bq::kR128: launch_args_kind<fp8bq::kR128>(g_descs, g_starts, bm, bn, total, s); break;
+      default: launch_args_kind<fp8bq::kGeneral>(g_descs, g_starts, bm, bn, total, s); break;
+    }
+  } else if (n > 0) {
+    // Larger groups: the table is copied into the workspace on the stream.
+    g_stage.resize(need);
+    std::memcpy(g_stage.data(), g_descs.data(), sizeof(Desc) * static_cast<size_t>(n));
+    int64_t* start = reinterpret_cast<int64_t*>(g_stage.data() + descs_bytes(count));
+    std::memcpy(start, g_starts.data(), sizeof(int64_t) * static_cast<size_t>(n));
+    start[n] = total;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    const size_t used = descs_bytes(count) + sizeof(int64_t) * (static_cast<size_t>(n) + 1);
+    hipError_t e = hipMemcpyAsync(ws, g_stage.data(), used, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_failed(e);
+    const Desc* d_descs = reinterpret_cast<const Desc*>(ws);
+    const int64_t* d_start = reinterpret_cast<const int64_t*>(ws + descs_bytes(count));
+    switch (kind) {
+      case fp8bq::kT128: launch_group<fp8bq::kT128>(d_descs, d_start, n, bm, bn, total, s); break;
+      case fp8bq::kT64: launch_group<fp8bq::kT64>(d_descs, d_start, n, bm, bn, total, s); break;
+      case fp8bq::kR128: launch_group<fp8bq::kR128>(d_descs, d_start, n, bm, bn, total, s); break;
+      default: launch_group<fp8bq::kGeneral>(d_descs, d_start, n, bm, bn, total, s); break;
     }
   }
-  // The two tables are packed at the front of the workspace in the same
-  // layout as the staging buffer, so one copy moves both.
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
-  const size_t used = descs_bytes(count) + sizeof(int64_t) * (static_cast<size_t>(n) + 1);
-  hipError_t e = hipMemcpyAsync(ws, g_stage.data(), used, hipMemcpyHostToDevice, s);
-  if (e != hipSuccess) return hip_failed(e);
-  const Desc* d_descs = reinterpret_cast<const Desc*>(ws);
-  const int64_t* d_start = reinterpret_cast<const int64_t*>(ws + descs_bytes(count));
-  switch (kind) {
-    case fp8bq::kT128: launch_group<fp8bq::kT128>(d_descs, d_start, n, bm, bn, total, s); break;
-    case fp8bq::kT64: launch_group<fp8bq::kT64>(d_descs, d_start, n, bm, bn, total, s); break;
-    case fp8bq::kR128: launch_group<fp8bq::kR128>(d_descs, d_start, n, bm, bn, total, s); break;
-    default: launch_group<fp8bq::kGeneral>(d_descs, d_start, n, bm, bn, total, s); break;
-  }
-  e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
 }
 

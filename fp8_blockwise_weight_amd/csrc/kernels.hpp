@@ -602,6 +602,61 @@ __global__ __launch_bounds__(kThreads) void dequant_elem(const uint8_t* __restri
   }
 }
 
+// ---------------------------------------------------------------- grouped launch, table in the arguments
+//
+// Groups of up to kArgsMax tensors pass their descriptor table by value in
+// the kernel arguments, so the launch needs no host-to-device copy (and no
+// workspace).  The table is read with uniform scalar loads like any other
+// kernel argument.
+
+constexpr int kArgsMax = 512;
+
+struct ArgTensor {
+  const uint16_t* x;
+  uint8_t* q;
+  float* s;
+  int32_t M;
+  int32_t N;
+  int32_t general;  // 1: element-wise tile body for this tensor
+  int32_t pad;
+};
+
+template <int CAP>
+struct GroupArgs {
+  int32_t start[CAP + 1];  // first unit of each tensor; start[count] = total
+  ArgTensor t[CAP];
+};
+
+template <int KIND, int CAP>
+__global__ __launch_bounds__(kThreads) void quantize_group_args(const GroupArgs<CAP> a,
+                                                                int32_t count, int32_t bm,
+                                                                int32_t bn, int32_t total) {
+  __shared__ uint32_t red[8];
+  const int64_t u = xcd_unit(blockIdx.x, total);
+  int lo = 0, hi = count - 1;  // largest t with start[t] <= u
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.start[mid] <= u) {
+      lo = mid;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  const ArgTensor& at = a.t[lo];
+  Desc d;
+  d.x = at.x;
+  d.q = at.q;
+  d.s = at.s;
+  d.M = at.M;
+  d.N = at.N;
+  d.TN = (at.N + bn - 1) / bn;
+  d.general = at.general;
+  d.UN = at.general ? d.TN : (at.N + 127) / 128;
+  d.pad = 0;
+  d.reserved = 0;
+  run_unit<KIND>(d, bm, bn, u - a.start[lo], red);
+}
+
 // The final cast alone: clamp and convert n floats.
 __global__ __launch_bounds__(kThreads) void encode_e4m3(const float* __restrict__ y,
                                                         uint8_t* __restrict__ q, int64_t n) {

@@ -93,26 +93,34 @@ typedef struct fp8bq_tensor {
   int64_t N;
 } fp8bq_tensor;
 
-/* Device workspace bytes fp8bq_quantize_many needs for `count` tensors
- * (0 for count <= 0). */
+/* Maximum number of tensors whose descriptor table fp8bq_quantize_many passes
+ * in the kernel arguments (no workspace, no host-to-device copy). */
+#define FP8BQ_MANY_ARGS_MAX 512
+
+/* Device workspace bytes fp8bq_quantize_many needs for `count` tensors: 0 for
+ * count <= FP8BQ_MANY_ARGS_MAX (the table rides in the kernel arguments). */
 size_t fp8bq_many_workspace_bytes(int32_t count);
 
 /*
  * Quantize a list of BF16 matrices that share one block size, in one kernel
  * launch (the grouped form of the per-weight loop).
- *   list             HOST array of `count` entries; it is copied into
- *                    `workspace` on `stream` before the call returns, so the
- *                    caller may reuse or free it afterwards
+ *   list             HOST array of `count` entries; its contents are captured
+ *                    before the call returns (into the kernel arguments, or
+ *                    copied into `workspace` on `stream`), so the caller may
+ *                    reuse or free it afterwards
  *   count            number of entries (>= 0)
  *   bm, bn           block size shared by every entry
  *   workspace        device buffer of at least
  *                    fp8bq_many_workspace_bytes(count) bytes, 16-byte
- *                    aligned; it must stay untouched until the launch on
- *                    `stream` has finished
+ *                    aligned, untouched until the launch on `stream` has
+ *                    finished; may be NULL when that size is 0 (count <=
+ *                    FP8BQ_MANY_ARGS_MAX)
  *   workspace_bytes  its size
  *   stream           hipStream_t (NULL = null stream)
- * Entries with M == 0 or N == 0 are skipped.  Outputs of different entries
- * must not overlap each other or any entry's x (not checked across entries).
+ * Entries with M == 0 or N == 0 are skipped.  Entries whose tiles exceed
+ * 65536 elements are quantized by the two-pass kernels (per entry, before
+ * the grouped launch).  Outputs of different entries must not overlap each
+ * other or any entry's x (not checked across entries).
  * Returns an fp8bq_status; on an argument error nothing is enqueued.
  */
 int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int32_t bn,

@@ -59,9 +59,10 @@ def test_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    assert lib.fp8bq_many_workspace_bytes(0) == 0
-    assert lib.fp8bq_many_workspace_bytes(-3) == 0
-    for n in (1, 7, 252, 256, 4096):
+    # groups of up to 512 tensors carry their table in the kernel arguments
+    for n in (-3, 0, 1, 7, 252, 256, 512):
+        assert lib.fp8bq_many_workspace_bytes(n) == 0
+    for n in (513, 4096, 20000):
         b = lib.fp8bq_many_workspace_bytes(n)
         assert b >= 64 * n + 8 * (n + 1) and b % 256 == 0
 
@@ -104,15 +105,19 @@ def _entries(rows):
 
 def test_quantize_many_rejects(lib):
     good = _entries([(X, Q, S, 256, 256)])
-    need = lib.fp8bq_many_workspace_bytes(1)
     f = lib.fp8bq_quantize_many
-    assert f(good, -1, 128, 128, W, need, None) == INVALID          # count < 0
-    assert f(None, 1, 128, 128, W, need, None) == INVALID           # null list
-    assert f(good, 1, 0, 128, W, need, None) == INVALID             # bm < 1
-    assert f(good, 1, 128, 0, W, need, None) == INVALID             # bn < 1
-    assert f(good, 1, 128, 128, None, need, None) == WORKSPACE      # null workspace
-    assert f(good, 1, 128, 128, W, need - 1, None) == WORKSPACE     # too small
-    assert f(good, 1, 128, 128, W + 8, need, None) == WORKSPACE     # misaligned
+    assert f(good, -1, 128, 128, W, 0, None) == INVALID             # count < 0
+    assert f(None, 1, 128, 128, W, 0, None) == INVALID              # null list
+    assert f(good, 1, 0, 128, W, 0, None) == INVALID                # bm < 1
+    assert f(good, 1, 128, 0, W, 0, None) == INVALID                # bn < 1
+    # more than 512 entries need a workspace (each entry its own fake slab)
+    many = _entries([(X + i * 0x100000, Q + i * 0x100000, S + i * 0x1000, 256, 256)
+                     for i in range(600)])
+    need = lib.fp8bq_many_workspace_bytes(600)
+    assert need > 0
+    assert f(many, 600, 128, 128, None, need, None) == WORKSPACE    # null workspace
+    assert f(many, 600, 128, 128, W, need - 1, None) == WORKSPACE   # too small
+    assert f(many, 600, 128, 128, W + 8, need, None) == WORKSPACE   # misaligned
     # one bad entry anywhere rejects the whole call
     bad = _entries([(X, Q, S, 256, 256), (X + 0x1000000, None, S + 0x1000, 4, 4)])
     assert f(bad, 2, 128, 128, W, lib.fp8bq_many_workspace_bytes(2), None) == INVALID

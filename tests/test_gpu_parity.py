@@ -263,6 +263,28 @@ def test_grouped_mixed_list(gpu_lib):
             assert torch.equal(q1.view(torch.uint8), q.view(torch.uint8))
 
 
+def test_grouped_workspace_path(gpu_lib):
+    """More than 512 tensors: the descriptor table goes through the workspace
+    (host-to-device copy) instead of the kernel arguments."""
+    g = torch.Generator(device=DEV).manual_seed(13)
+    rng = np.random.default_rng(13)
+    mats = []
+    for _ in range(700):
+        M, N = int(rng.integers(1, 300)), int(rng.choice([8, 64, 136, 256, 264, 7, 99]))
+        mats.append((torch.randn((M, N), generator=g, device=DEV) * 0.03).to(torch.bfloat16))
+    assert fq.workspace_bytes(len(mats)) > 0
+    for block in BLOCKS + [(5, 3)]:
+        say("workspace path", block)
+        outs = fq.quantize_many(mats, block)
+        for i, (x, (q, s)) in enumerate(zip(mats, outs)):
+            q1, s1 = fq.quantize(x, block)
+            assert torch.equal(q1.view(torch.uint8), q.view(torch.uint8)), (block, i)
+            assert torch.equal(s1.view(torch.int32), s.view(torch.int32)), (block, i)
+        for i in (0, 1, 350, 699):
+            x, (q, s) = mats[i], outs[i]
+            assert_matches_oracle(x, q, s, *block, f"workspace path [{i}] {block}")
+
+
 @pytest.mark.parametrize("bm,bn", BLOCKS)
 def test_c5_ragged_full(gpu_lib, bm, bn):
     for sp in wl.c5():
