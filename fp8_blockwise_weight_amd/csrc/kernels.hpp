@@ -15,7 +15,8 @@
 //     rows written are still full 128-byte lines;
 //   * [1,128] blocks: unit = 64 rows x 128 = 64 row-tiles; each tile's
 //     maximum is reduced inside one 16-lane DPP row, with no LDS and no
-//     barrier;
+//     barrier, and each lane divides for one row-tile only (DPP quad
+//     broadcast of the reciprocals);
 //   * any other block size, N % 8 != 0 or a misaligned pointer: one tile per
 //     unit, element by element (two passes over the tile), same arithmetic.
 //
@@ -30,6 +31,9 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
+#include <utility>
 
 namespace fp8bq {
 
@@ -109,6 +113,23 @@ __device__ __forceinline__ uint32_t rows_max(uint32_t v) {
   uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, L + 32);
   uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, L + 48);
   return max(max(a, b), max(c, d));
+}
+
+// Compile-time loop: f(std::integral_constant<int, K>) for K = 0 .. N-1.
+template <typename F, int... K>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, K...>) {
+  (f(std::integral_constant<int, K>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Value of lane K of each quad (4 consecutive lanes), for every lane of it.
+template <int K>
+__device__ __forceinline__ float quad_bcast(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_mov_dpp(__float_as_int(v), K | (K << 2) | (K << 4) | (K << 6), 0xF, 0xF, false));
 }
 
 // Scale and reciprocal from the tile's maximum magnitude bits: two correctly
@@ -200,16 +221,25 @@ __device__ __forceinline__ void vec_unit(const Desc& d, int64_t ur, int64_t uc, 
   const size_t qpitch16 = (size_t)N * 16 / 8;  // 16 rows, in 8-byte chunks
 
   if constexpr (KIND == kR128) {
-    // Every 16-lane row holds one row-tile: reduce inside the DPP row.
+    // Every 16-lane DPP row holds one row-tile per load: reduce inside it.
+    // A lane owns L = 4 row-tiles, so instead of 4 division pairs each lane
+    // computes one -- for the row-tile k = chunk % 4 -- and the quad
+    // (chunks 4j..4j+3) shares the four reciprocals by DPP broadcast.
+    static_assert(L == 4, "one division per lane needs 4 row-tiles per lane");
+    uint32_t m[L];
 #pragma unroll
-    for (int k = 0; k < L; ++k) {
-      const uint32_t m = max16(halves_max(fold_abs(v[k])));
-      float s, r;
-      tile_scale(m, s, r);
+    for (int k = 0; k < L; ++k) m[k] = max16(halves_max(fold_abs(v[k])));
+    const int mine = chunk & 3;
+    const uint32_t msel = mine == 0 ? m[0] : mine == 1 ? m[1] : mine == 2 ? m[2] : m[3];
+    float ssel, rsel;
+    tile_scale(msel, ssel, rsel);
+    static_for<L>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      const float r = quad_bcast<k>(rsel);
       const bool row_ok = !CHECK || k * 16 + prow < rows_valid;
       if (row_ok && (!CHECK || col_ok)) __builtin_nontemporal_store(quant8(v[k], r), &qp[k * qpitch16]);
-      if (chunk == 0 && row_ok) sp[(size_t)(row0 + k * 16 + prow) * d.TN + uc] = s;
-    }
+      if (chunk == k && row_ok) sp[(size_t)(row0 + k * 16 + prow) * d.TN + uc] = ssel;
+    });
   } else {
     uint32_t m = 0;
 #pragma unroll

@@ -1,0 +1,130 @@
+"""Runtime behaviour on the GPU: HIP-graph capture and replay, non-default
+streams, and concurrent calls from several host threads."""
+
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_blockwise_weight_amd as fq
+from fp8_blockwise_weight_amd import workloads as wl
+from gpu_helpers import assert_matches_oracle
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("block", [(128, 128), (1, 128), (4096, 4096)])
+def test_graph_capture_replays_match_eager(gpu_lib, block):
+    """A grouped call (table in the kernel arguments; for the 4096x4096
+    block, the two-pass large-tile kernels) captured in a HIP graph: every
+    replay, with eager work and synchronizations in between, equals an
+    eager call on the same inputs."""
+    specs = wl.c2()[:3] + wl.c4_layer(0)[:5]
+    xs = [wl.materialize(sp, DEV) for sp in specs]
+    outs = [(torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=DEV),
+             torch.empty(fq.scale_shape(*x.shape, *block), dtype=torch.float32, device=DEV))
+            for x in xs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fq.quantize_many(xs, block, outputs=outs)          # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fq.quantize_many(xs, block, outputs=outs)
+    torch.cuda.synchronize()
+    g = torch.Generator(device=DEV).manual_seed(3)
+    for rep in range(4):
+        _say("replay", block, rep)
+        for x in xs:                                       # eager work between replays
+            x.mul_(torch.where(torch.rand(x.shape, generator=g, device=DEV) < 0.5, -1.0, 1.0)
+                   .to(torch.bfloat16))
+        for q, s in outs:
+            q.view(torch.uint8).fill_(0xA5)
+            s.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for x, (q, s) in zip(xs, outs):
+            q1, s1 = fq.quantize(x, block)
+            assert torch.equal(q1.view(torch.uint8), q.view(torch.uint8)), (block, rep)
+            assert torch.equal(s1.view(torch.int32), s.view(torch.int32)), (block, rep)
+    assert_matches_oracle(xs[0], outs[0][0], outs[0][1], *block, "graph replay")
+
+
+def test_non_default_streams(gpu_lib):
+    """Work is enqueued on the caller's current stream and ordered with it."""
+    x = wl.materialize(wl.c2()[0], DEV)
+    q0, s0 = fq.quantize(x, (128, 128))
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        y = x * 2                                          # produced on st
+        q1, s1 = fq.quantize(y, (128, 128))                # must see y on st
+        xh = fq.dequantize(q1, s1, (128, 128))
+    st.synchronize()
+    assert torch.equal(q1.view(torch.uint8), q0.view(torch.uint8))   # scaling by 2 is exact
+    assert torch.equal(s1, s0 * 2)
+    assert xh.shape == x.shape
+
+
+def test_concurrent_host_threads(gpu_lib):
+    """Several host threads, each with its own stream, quantizing different
+    weight lists at once (grouped and single calls) give the same bytes as
+    one thread doing it alone."""
+    lists = [[wl.materialize(sp, DEV) for sp in wl.c4_layer(layer)[:64]] for layer in range(4)]
+    ref = [[(q.view(torch.uint8).clone(), s.clone()) for q, s in fq.quantize_many(xs, (128, 128))]
+           for xs in lists]
+    torch.cuda.synchronize()
+    results = [None] * len(lists)
+    errors = []
+
+    def work(i):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                got = []
+                for _ in range(3):
+                    got = fq.quantize_many(lists[i], (128, 128))
+                    singles = [fq.quantize(x, (128, 128)) for x in lists[i][:8]]
+                st.synchronize()
+            results[i] = (got, singles)
+        except Exception as exc:  # noqa: BLE001 - reported below
+            errors.append(exc)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(lists))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for i, (got, singles) in enumerate(results):
+        for (q, s), (qr, sr) in zip(got, ref[i]):
+            assert torch.equal(q.view(torch.uint8), qr) and torch.equal(s, sr), i
+        for (q, s), (qr, sr) in zip(singles, ref[i][:8]):
+            assert torch.equal(q.view(torch.uint8), qr), i
+
+
+def test_error_reporting_on_device(gpu_lib):
+    """Argument errors raise with the library's status text; nothing is
+    launched (outputs keep their fill)."""
+    x = torch.zeros((64, 64), dtype=torch.bfloat16, device=DEV)
+    q = torch.full((64, 64), 0x11, dtype=torch.uint8, device=DEV)
+    s = torch.full((1, 1), 3.0, device=DEV)
+    with pytest.raises(fq.Fp8bqError, match="invalid argument"):
+        fq.quantize(x, (64, 64), out=(q.view(64, 64), x[:1, :2].view(torch.float32)))  # scale overlaps x
+    torch.cuda.synchronize()
+    assert bool((q == 0x11).all()) and float(s[0, 0]) == 3.0
+    ws_small = torch.empty(16, dtype=torch.uint8, device=DEV)
+    mats = [torch.zeros((8, 8), dtype=torch.bfloat16, device=DEV) for _ in range(600)]
+    with pytest.raises(fq.Fp8bqError, match="workspace"):
+        fq.quantize_many(mats, (8, 8), workspace=ws_small)
+    assert np.isfinite(1.0)
