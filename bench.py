@@ -81,15 +81,12 @@ def build_workload(name, dev, block=None):
 
     if name == "dense":
         groups = [wl.c3()]
-        block = (128, 128)
         desc = "qwen3-8b-shaped dense stack, 36 layers x 7 linears (252 tensors)"
     elif name == "dense-layer":
         groups = [wl.c2()]
-        block = (128, 128)
         desc = "one qwen3-8b-shaped decoder layer (7 tensors)"
     elif name == "moe":
         groups = [wl.c4_layer(layer) for layer in range(wl.MOE_LAYERS)]
-        block = (128, 128)
         desc = "moe 48 layers x 128 experts (w13 1536x2048, down 2048x768), one launch per layer"
     elif name == "ragged":
         groups = [[sp] for sp in wl.c5()]
@@ -102,6 +99,9 @@ def build_workload(name, dev, block=None):
         desc = f"151937x4096 (vocab-shaped) at block [{block[0]},{block[1]}]"
     else:
         raise SystemExit(f"unknown workload {name}")
+    block = block or (128, 128)
+    if block != (128, 128) and name in ("dense", "dense-layer", "moe"):
+        desc += f" at block [{block[0]},{block[1]}]"
     return groups, block, desc
 
 
@@ -112,6 +112,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense")
     ap.add_argument("--block", default=None, help="bm,bn for the ragged/vocab workloads")
+    ap.add_argument("--op", default="quantize", choices=["quantize", "dequant-f32", "dequant-bf16"],
+                    help="quantize (default) or time fp8bq_dequantize on the quantized workload")
     ap.add_argument("--per-tensor", action="store_true",
                     help="also time one fp8bq_quantize call per tensor (HIP events per call)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -204,6 +206,10 @@ def main():
         torch.cuda.synchronize()
         log("calibration copy: 3 x 1 GiB device-to-device")
 
+    if args.op != "quantize":
+        time_dequant(lib, keep, groups, bm, bn, args, stream, sptr, desc)
+        return
+
     per_tensor = None
     if args.per_tensor:
         per_tensor = time_per_tensor(lib, keep, groups, bm, bn, stream, sptr)
@@ -255,6 +261,49 @@ def main():
     if per_tensor is not None:
         out["per_tensor"] = per_tensor
     print(json.dumps(out), flush=True)
+
+
+def time_dequant(lib, keep, groups, bm, bn, args, stream, sptr, desc):
+    """Dequantize every tensor of the (already quantized) workload, one
+    fp8bq_dequantize launch per tensor; report output GB/s and % of peak."""
+    import torch
+
+    f32 = args.op == "dequant-f32"
+    esize = 4 if f32 else 2
+    items = []
+    for (xs, outs), specs in zip(keep, groups):
+        for x, (q, s), sp in zip(xs, outs, specs):
+            o = torch.empty(x.shape, dtype=torch.float32 if f32 else torch.bfloat16, device=x.device)
+            items.append((sp, q, s, o))
+    nbytes = sum(sp.M * sp.N * (1 + esize) + 4 * -(-sp.M // bm) * -(-sp.N // bn)
+                 for sp, *_ in items)
+
+    def step():
+        for sp, q, s, o in items:
+            st = lib.fp8bq_dequantize(q.data_ptr(), s.data_ptr(), sp.M, sp.N, bm, bn, o.data_ptr(),
+                                      0 if f32 else 1, sptr)
+            if st != 0:
+                raise RuntimeError(f"fp8bq_dequantize failed: {st}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    a.record(stream)
+    for _ in range(args.steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - w0) * 1e3 / args.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    ev = a.elapsed_time(b) / args.steps
+    log(f"{args.op}: {len(items)} launches/step, wall {ms:.3f} ms/step (events {ev:.3f}); "
+        f"{gbs:.1f} GB/s = {100 * gbs / HBM_PEAK_GBS:.1f}% of peak")
+    print(json.dumps({"op": args.op, "workload": desc, "launches_per_step": len(items),
+                      "bytes_per_step": nbytes, "ms_per_step": round(ms, 4),
+                      "GBps": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}),
+          flush=True)
 
 
 def time_per_tensor(lib, keep, groups, bm, bn, stream, sptr, reps=3):

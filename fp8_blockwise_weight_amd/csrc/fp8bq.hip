@@ -93,7 +93,11 @@ int make_desc(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, void*
   if (overlap(x, 2 * n, q, n) || overlap(x, 2 * n, s, 4 * ns) || overlap(q, n, s, 4 * ns)) {
     return FP8BQ_ERR_INVALID_ARGUMENT;
   }
-  const bool vec = kind != fp8bq::kGeneral && (N % 8) == 0 && (xa & 15) == 0 && (qa & 7) == 0;
+  const bool aligned = (N % 8) == 0 && (xa & 15) == 0 && (qa & 7) == 0;
+  const bool vec = kind != fp8bq::kGeneral && aligned;
+  // A whole tile fits the register body: at most kRegTile elements, 8-aligned columns.
+  const bool reg = aligned && (bn % 8) == 0 &&
+                   static_cast<int64_t>(bm) * static_cast<int64_t>(bn) <= fp8bq::kRegTile;
   d->x = static_cast<const uint16_t*>(x);
   d->q = static_cast<uint8_t*>(q);
   d->s = s;
@@ -106,12 +110,12 @@ int make_desc(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, void*
   if (vec) {
     const int64_t rows = kind == fp8bq::kT128 ? 128 : 64;
     d->UN = static_cast<int32_t>(ceil_div(N, 128));
-    d->general = 0;
+    d->body = fp8bq::kBodyVec;
     u = ceil_div(M, rows) * d->UN;
   } else {
     if (TN > INT32_MAX) return FP8BQ_ERR_INVALID_ARGUMENT;
     d->UN = static_cast<int32_t>(TN);
-    d->general = 1;
+    d->body = reg ? fp8bq::kBodyRegTile : fp8bq::kBodyScalar;
     if (TM > kMaxUnits / TN) return FP8BQ_ERR_INVALID_ARGUMENT;
     u = TM * TN;
   }
@@ -188,14 +192,15 @@ void launch_big_amax(const fp8bq::Big& b, float* amax, hipStream_t st) {
   const int64_t nt = b.TMl * b.TNl;
   hipLaunchKernelGGL(fp8bq::fill_zero, dim3(grid_capped(nt, fp8bq::kThreads)), dim3(fp8bq::kThreads),
                      0, st, reinterpret_cast<uint32_t*>(amax), nt);
-  hipLaunchKernelGGL(fp8bq::big_tiles<0>, dim3(grid_for(b.items)), dim3(fp8bq::kThreads), 0, st, b,
-                     reinterpret_cast<uint32_t*>(amax), static_cast<const float*>(nullptr));
+  const int64_t items = b.TMl * b.TNl * ceil_div(b.cpt, fp8bq::kChunksPerMax);
+  hipLaunchKernelGGL(fp8bq::big_max, dim3(grid_for(items)), dim3(fp8bq::kThreads), 0, st, b,
+                     reinterpret_cast<uint32_t*>(amax), items);
 }
 
 void launch_big_quant(const fp8bq::Big& b, const float* amax, float* scale_inv, hipStream_t st) {
   const int64_t nt = b.TMl * b.TNl;
-  hipLaunchKernelGGL(fp8bq::big_tiles<1>, dim3(grid_for(b.items)), dim3(fp8bq::kThreads), 0, st, b,
-                     static_cast<uint32_t*>(nullptr), amax);
+  hipLaunchKernelGGL(fp8bq::big_quant, dim3(grid_for(b.items)), dim3(fp8bq::kThreads), 0, st, b,
+                     amax);
   hipLaunchKernelGGL(fp8bq::finalize_scales, dim3(grid_capped(nt, fp8bq::kThreads)),
                      dim3(fp8bq::kThreads), 0, st, amax, scale_inv, nt);
 }
@@ -215,7 +220,7 @@ void launch_args(const std::vector<Desc>& ds, const std::vector<int64_t>& st, in
     a.t[i].s = ds[i].s;
     a.t[i].M = static_cast<int32_t>(ds[i].M);
     a.t[i].N = static_cast<int32_t>(ds[i].N);
-    a.t[i].general = ds[i].general;
+    a.t[i].body = ds[i].body;
   }
   a.start[n] = static_cast<int32_t>(total);
   hipLaunchKernelGGL((fp8bq::quantize_group_args<KIND, CAP>), dim3(static_cast<unsigned>(total)),
@@ -269,7 +274,7 @@ int fp8bq_quantize(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, 
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
   }
-  switch (d.general ? static_cast<int>(fp8bq::kGeneral) : kind) {
+  switch (d.body != fp8bq::kBodyVec ? static_cast<int>(fp8bq::kGeneral) : kind) {
     case fp8bq::kT128: launch_one<fp8bq::kT128>(d, bm, bn, units, s); break;
     case fp8bq::kT64: launch_one<fp8bq::kT64>(d, bm, bn, units, s); break;
     case fp8bq::kR128: launch_one<fp8bq::kR128>(d, bm, bn, units, s); break;
@@ -473,18 +478,20 @@ int fp8bq_dequantize(const void* q, const float* scale_inv, int64_t M, int64_t N
   (void)hipGetLastError();
   const uint8_t* qb = static_cast<const uint8_t*>(q);
   const int32_t tn = static_cast<int32_t>(TN);
-  const bool vec = (N % 16) == 0 && (bn % 16) == 0 && (qa & 15) == 0 && (oa & 15) == 0;
+  const int64_t G = out_dtype == FP8BQ_OUT_F32 ? 4 : 8;
+  const bool vec = (N % G) == 0 && (bn % G) == 0 && (qa % G) == 0 && (oa & 15) == 0;
   if (vec) {
-    const int64_t chunks = static_cast<int64_t>(n / 16);
-    const int64_t blocks = (chunks + fp8bq::kThreads - 1) / fp8bq::kThreads;
+    const int64_t groups = static_cast<int64_t>(n) / G;
+    const int64_t per_block = static_cast<int64_t>(fp8bq::kThreads) * fp8bq::kDqUnroll;
+    const int64_t blocks = (groups + per_block - 1) / per_block;
     if (blocks > kMaxGrid) return FP8BQ_ERR_INVALID_ARGUMENT;
     const dim3 grid(static_cast<unsigned>(blocks));
     if (out_dtype == FP8BQ_OUT_F32) {
       hipLaunchKernelGGL(fp8bq::dequant_vec<fp8bq::kOutF32>, grid, dim3(fp8bq::kThreads), 0, s, qb,
-                         scale_inv, N, bm, bn, tn, out, chunks);
+                         scale_inv, N, bm, bn, tn, out, groups);
     } else {
       hipLaunchKernelGGL(fp8bq::dequant_vec<fp8bq::kOutBF16>, grid, dim3(fp8bq::kThreads), 0, s, qb,
-                         scale_inv, N, bm, bn, tn, out, chunks);
+                         scale_inv, N, bm, bn, tn, out, groups);
     }
   } else {
     const int64_t blocks = (static_cast<int64_t>(n) + fp8bq::kThreads - 1) / fp8bq::kThreads;

@@ -60,10 +60,16 @@ struct Desc {
   int64_t N;
   int32_t TN;       // tile columns: row pitch of s
   int32_t UN;       // work-unit columns
-  int32_t general;  // 1: this tensor takes the element-wise tile body
+  int32_t body;     // which unit body this tensor takes (Body below)
   int32_t pad;
   int64_t reserved;  // pads the entry to 64 bytes
 };
+
+// Unit bodies: the block-shape kernel of the launch (a [128,128], [64,64] or
+// [1,128] unit), a whole tile held in registers (any block of at most
+// kRegTile elements with 8-aligned columns), or a tile element by element.
+enum Body : int { kBodyVec = 0, kBodyScalar = 1, kBodyRegTile = 2 };
+constexpr int64_t kRegTile = 16384;
 static_assert(sizeof(Desc) == 64, "descriptor layout is part of the workspace format");
 
 // ---------------------------------------------------------------- helpers
@@ -281,6 +287,53 @@ __device__ __forceinline__ void vec_unit(const Desc& d, int64_t ur, int64_t uc, 
   }
 }
 
+// A whole tile of at most kRegTile elements held in registers: rows x cols
+// with cols % 8 == 0, x 16-byte and q 8-byte aligned, N % 8 == 0.  Vector v
+// of the tile is row v / (cols/8), 8-column group v % (cols/8); thread t
+// holds vectors t, t + 256, ... (at most 8), so the tile is read once.
+__device__ __forceinline__ void reg_tile(const Desc& d, int32_t bm, int32_t bn, int64_t ti,
+                                         int64_t tj, uint32_t* red) {
+  const int t = threadIdx.x;
+  const int64_t r0 = ti * bm;
+  const int64_t c0 = tj * bn;
+  const uint32_t rows = (uint32_t)((d.M - r0) < bm ? (d.M - r0) : bm);
+  const uint32_t cols = (uint32_t)((d.N - c0) < bn ? (d.N - c0) : bn);
+  const uint32_t vpr = cols / 8;
+  const uint32_t nvec = rows * vpr;
+  const size_t base = (size_t)r0 * d.N + c0;
+  const FP8BQ_GLOBAL uint16_t* x = (const FP8BQ_GLOBAL uint16_t*)(d.x + base);
+  FP8BQ_GLOBAL uint8_t* q = (FP8BQ_GLOBAL uint8_t*)(d.q + base);
+  u32x4 v[8];
+  size_t off[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t vi = (uint32_t)t + (uint32_t)k * kThreads;
+    if (vi < nvec) {
+      const uint32_t rr = vi / vpr;
+      off[k] = (size_t)rr * d.N + (size_t)(vi - rr * vpr) * 8;
+      v[k] = __builtin_nontemporal_load((const FP8BQ_GLOBAL u32x4*)(x + off[k]));
+    } else {
+      v[k] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m = pk_max_u16(m, fold_abs(v[k]));
+  m = max16(halves_max(m));
+  const uint32_t wm = rows_max<0>(m);
+  if ((t & 63) == 0) red[t >> 6] = wm;
+  __syncthreads();
+  const uint32_t tm = max(max(red[0], red[1]), max(red[2], red[3]));
+  float s, r;
+  tile_scale(tm, s, r);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t vi = (uint32_t)t + (uint32_t)k * kThreads;
+    if (vi < nvec) __builtin_nontemporal_store(quant8(v[k], r), (FP8BQ_GLOBAL u32x2*)(q + off[k]));
+  }
+  if (t == 0) ((FP8BQ_GLOBAL float*)d.s)[(size_t)ti * d.TN + tj] = s;
+}
+
 // Element-wise tile body: any block size, any alignment.  Pass 1 takes the
 // maximum, pass 2 re-reads the tile and writes one byte per element.
 __device__ __forceinline__ void general_tile(const Desc& d, int32_t bm, int32_t bn, int64_t ti,
@@ -324,7 +377,11 @@ __device__ __forceinline__ void run_unit(const Desc& d, int32_t bm, int32_t bn, 
   const uint32_t un = (uint32_t)d.UN;
   const uint32_t ur = uu / un;
   const uint32_t uc = uu - ur * un;
-  if (KIND == kGeneral || d.general) {
+  if (d.body == kBodyRegTile) {
+    reg_tile(d, bm, bn, ur, uc, red);
+    return;
+  }
+  if (KIND == kGeneral || d.body == kBodyScalar) {
     general_tile(d, bm, bn, ur, uc, red);
     return;
   }
@@ -451,40 +508,47 @@ __device__ __forceinline__ uint32_t block_max(uint32_t m, uint32_t* red) {
   return r;
 }
 
-// PASS 0: partial maxima (as fp32 bit patterns of the BF16 magnitudes) into
-// amax_bits, which must start at zero.  PASS 1: quantize with amax.
+// One chunk of a large tile: PASS 0 returns this thread's max of the
+// magnitude bits; PASS 1 quantizes the chunk with reciprocal r.
+// Returns false when chunk k lies past the end of a short tile (uniform).
 template <int PASS>
-__global__ __launch_bounds__(kThreads) void big_tiles(Big b, uint32_t* __restrict__ amax_bits,
-                                                      const float* __restrict__ amax) {
-  __shared__ uint32_t red[4];
+__device__ __forceinline__ bool big_chunk(const Big& b, int64_t tile, int64_t k, float r,
+                                          uint32_t& m) {
   const int t = threadIdx.x;
   const FP8BQ_GLOBAL uint16_t* x = (const FP8BQ_GLOBAL uint16_t*)b.x;
   FP8BQ_GLOBAL uint8_t* q = (FP8BQ_GLOBAL uint8_t*)b.q;
-  for (int64_t it = blockIdx.x; it < b.items; it += gridDim.x) {
-    const int64_t tile = it / b.cpt;
-    const int64_t k = it - tile * b.cpt;
-    const int64_t ti = tile / b.TNl;
-    const int64_t tj = tile - ti * b.TNl;
-    int64_t r0, r1, c0, c1;
-    big_rect(b, ti, tj, r0, r1, c0, c1);
-    float r = 0.0f;
-    if (PASS == 1) {
-      float s;
-      tile_scale_f(((const FP8BQ_GLOBAL float*)amax)[tile], s, r);
-    }
-    uint32_t m = 0;
-    if (b.flat) {
-      // The tile is rows [r0, r1) in full: one contiguous range of elements.
-      const int64_t f0 = r0 * b.N + k * kChunk;
-      int64_t f1 = f0 + kChunk;
-      f1 = f1 > r1 * b.N ? r1 * b.N : f1;
-      if (f0 >= f1) continue;  // uniform: this chunk index lies past a short tile
-      int64_t head = f0;
-      if (b.vec) {
-        // f0 is a multiple of 8 (kChunk and N are), so 16-byte vectors from f0.
-        const int64_t nv = (f1 - f0) / 8;
-        const FP8BQ_GLOBAL u32x4* xv = (const FP8BQ_GLOBAL u32x4*)(x + f0);
-        FP8BQ_GLOBAL u32x2* qv = (FP8BQ_GLOBAL u32x2*)(q + f0);
+  const int64_t ti = tile / b.TNl;
+  const int64_t tj = tile - ti * b.TNl;
+  int64_t r0, r1, c0, c1;
+  big_rect(b, ti, tj, r0, r1, c0, c1);
+  if (b.flat) {
+    // The tile is rows [r0, r1) in full: one contiguous range of elements.
+    const int64_t f0 = r0 * b.N + k * kChunk;
+    int64_t f1 = f0 + kChunk;
+    f1 = f1 > r1 * b.N ? r1 * b.N : f1;
+    if (f0 >= f1) return false;
+    int64_t head = f0;
+    if (b.vec) {
+      // f0 is a multiple of 8 (kChunk and N are), so 16-byte vectors from f0.
+      const int64_t nv = (f1 - f0) / 8;
+      const FP8BQ_GLOBAL u32x4* xv = (const FP8BQ_GLOBAL u32x4*)(x + f0);
+      FP8BQ_GLOBAL u32x2* qv = (FP8BQ_GLOBAL u32x2*)(q + f0);
+      constexpr int kPer = (int)(kChunk / 8 / kThreads);  // vectors per thread, full chunk
+      if (nv == kChunk / 8) {
+        u32x4 w[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) w[i] = __builtin_nontemporal_load(&xv[t + i * kThreads]);
+        uint32_t mm = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          if (PASS == 0) {
+            mm = pk_max_u16(mm, fold_abs(w[i]));
+          } else {
+            __builtin_nontemporal_store(quant8(w[i], r), &qv[t + i * kThreads]);
+          }
+        }
+        if (PASS == 0) m = max(m, halves_max(mm));
+      } else {
         for (int64_t v = t; v < nv; v += kThreads) {
           const u32x4 w = __builtin_nontemporal_load(&xv[v]);
           if (PASS == 0) {
@@ -493,43 +557,80 @@ __global__ __launch_bounds__(kThreads) void big_tiles(Big b, uint32_t* __restric
             __builtin_nontemporal_store(quant8(w, r), &qv[v]);
           }
         }
-        head = f0 + nv * 8;
       }
-      for (int64_t e = head + t; e < f1; e += kThreads) {
-        const uint32_t bits = x[e];
-        if (PASS == 0) {
-          m = max(m, bits & 0x7FFFu);
-        } else {
-          const float y = clamp448(__uint_as_float(bits << 16) * r);
-          q[e] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xFF);
-        }
-      }
-    } else {
-      // General rectangle: rows of the chunk, element by element.
-      const int64_t cols = c1 - c0;
-      const int64_t rows_per = cols >= kChunk ? 1 : kChunk / cols;
-      const int64_t ra = r0 + k * rows_per;
-      int64_t rb = ra + rows_per;
-      rb = rb > r1 ? r1 : rb;
-      if (ra >= rb) continue;  // uniform
-      const int64_t n = (rb - ra) * cols;
-      for (int64_t e = t; e < n; e += kThreads) {
-        const int64_t rr = e / cols;
-        const int64_t cc = e - rr * cols;
-        const size_t off = (size_t)(ra + rr) * b.N + c0 + cc;
-        const uint32_t bits = x[off];
-        if (PASS == 0) {
-          m = max(m, bits & 0x7FFFu);
-        } else {
-          const float y = clamp448(__uint_as_float(bits << 16) * r);
-          q[off] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xFF);
-        }
+      head = f0 + nv * 8;
+    }
+    for (int64_t e = head + t; e < f1; e += kThreads) {
+      const uint32_t bits = x[e];
+      if (PASS == 0) {
+        m = max(m, bits & 0x7FFFu);
+      } else {
+        const float y = clamp448(__uint_as_float(bits << 16) * r);
+        q[e] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xFF);
       }
     }
+    return true;
+  }
+  // General rectangle: rows of the chunk, element by element.
+  const int64_t cols = c1 - c0;
+  const int64_t rows_per = cols >= kChunk ? 1 : kChunk / cols;
+  const int64_t ra = r0 + k * rows_per;
+  int64_t rb = ra + rows_per;
+  rb = rb > r1 ? r1 : rb;
+  if (ra >= rb) return false;
+  const int64_t n = (rb - ra) * cols;
+  for (int64_t e = t; e < n; e += kThreads) {
+    const int64_t rr = e / cols;
+    const int64_t cc = e - rr * cols;
+    const size_t off = (size_t)(ra + rr) * b.N + c0 + cc;
+    const uint32_t bits = x[off];
     if (PASS == 0) {
-      const uint32_t wm = block_max(m, red);
-      if (t == 0 && wm != 0) atomicMax(&amax_bits[tile], wm << 16);
+      m = max(m, bits & 0x7FFFu);
+    } else {
+      const float y = clamp448(__uint_as_float(bits << 16) * r);
+      q[off] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xFF);
     }
+  }
+  return true;
+}
+
+// Pass 1 of the large-tile path: partial maxima (as fp32 bit patterns of the
+// BF16 magnitudes) into amax_bits, which must start at zero.  A workgroup
+// reduces kChunksPerMax chunks of one tile before its single atomic max, and
+// skips the atomic when a coherent read shows the tile maximum is already at
+// least as large: many workgroups folding into one address (one scale per
+// tensor) would otherwise serialize on it.
+constexpr int64_t kChunksPerMax = 16;
+
+__global__ __launch_bounds__(kThreads) void big_max(Big b, uint32_t* __restrict__ amax_bits,
+                                                    int64_t items) {
+  __shared__ uint32_t red[4];
+  const int64_t groups = (b.cpt + kChunksPerMax - 1) / kChunksPerMax;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int64_t tile = it / groups;
+    const int64_t g = it - tile * groups;
+    uint32_t m = 0;
+    for (int64_t k = g * kChunksPerMax; k < (g + 1) * kChunksPerMax && k < b.cpt; ++k) {
+      if (!big_chunk<0>(b, tile, k, 0.0f, m)) break;
+    }
+    const uint32_t wm = block_max(m, red);
+    if (threadIdx.x == 0 && wm != 0) {
+      const uint32_t cur = __hip_atomic_load(&amax_bits[tile], __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      if ((wm << 16) > cur) atomicMax(&amax_bits[tile], wm << 16);
+    }
+  }
+}
+
+// Pass 2: quantize chunk by chunk with the finished maxima.
+__global__ __launch_bounds__(kThreads) void big_quant(Big b, const float* __restrict__ amax) {
+  for (int64_t it = blockIdx.x; it < b.items; it += gridDim.x) {
+    const int64_t tile = it / b.cpt;
+    const int64_t k = it - tile * b.cpt;
+    float s, r;
+    tile_scale_f(((const FP8BQ_GLOBAL float*)amax)[tile], s, r);
+    uint32_t unused = 0;
+    big_chunk<1>(b, tile, k, r, unused);
   }
 }
 
@@ -577,36 +678,49 @@ __device__ __forceinline__ f32x4 dq4(uint32_t w, float s) {
   return f32x4{lo.x * s, lo.y * s, hi.x * s, hi.y * s};
 }
 
-// One thread per 16-byte chunk of q (16 elements in one tile: N % 16 == 0,
-// bn % 16 == 0, q and out 16-byte aligned).
+// Vector dequantization: every lane writes one 16-byte output chunk per
+// group -- 4 codes to 4 fp32, or 8 codes to 8 BF16 -- so each wave store is
+// one contiguous 1 KB run (16 B per lane, lanes adjacent).  A workgroup
+// handles kDqUnroll * 256 groups, all loads issued before the stores.
+// Needs N % G == 0, bn % G == 0 (a group never straddles a row or a tile),
+// q aligned to G bytes and out to 16 bytes (G = 4 for fp32, 8 for BF16).
+constexpr int kDqUnroll = 4;
+
 template <int OUT>
 __global__ __launch_bounds__(kThreads) void dequant_vec(const uint8_t* __restrict__ q,
                                                         const float* __restrict__ s, int64_t N,
                                                         int32_t bm, int32_t bn, int32_t TN,
-                                                        void* __restrict__ out, int64_t chunks) {
-  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (c >= chunks) return;
-  const int64_t cpr = N / 16;
-  const int64_t row = c / cpr;
-  const int64_t col = (c - row * cpr) * 16;
-  const float sc = ((const FP8BQ_GLOBAL float*)s)[(row / bm) * TN + col / bn];
-  const size_t off = (size_t)row * N + col;
-  const u32x4 w = __builtin_nontemporal_load((const FP8BQ_GLOBAL u32x4*)(q + off));
-  const f32x4 a = dq4(w.x, sc), b = dq4(w.y, sc), e = dq4(w.z, sc), f = dq4(w.w, sc);
-  if constexpr (OUT == kOutF32) {
-    FP8BQ_GLOBAL f32x4* o = (FP8BQ_GLOBAL f32x4*)((float*)out + off);
-    __builtin_nontemporal_store(a, o);
-    __builtin_nontemporal_store(b, o + 1);
-    __builtin_nontemporal_store(e, o + 2);
-    __builtin_nontemporal_store(f, o + 3);
-  } else {
-    FP8BQ_GLOBAL u32x4* o = (FP8BQ_GLOBAL u32x4*)((uint16_t*)out + off);
-    const u32x4 p0{bf16_rne(a.x) | (bf16_rne(a.y) << 16), bf16_rne(a.z) | (bf16_rne(a.w) << 16),
-                   bf16_rne(b.x) | (bf16_rne(b.y) << 16), bf16_rne(b.z) | (bf16_rne(b.w) << 16)};
-    const u32x4 p1{bf16_rne(e.x) | (bf16_rne(e.y) << 16), bf16_rne(e.z) | (bf16_rne(e.w) << 16),
-                   bf16_rne(f.x) | (bf16_rne(f.y) << 16), bf16_rne(f.z) | (bf16_rne(f.w) << 16)};
-    __builtin_nontemporal_store(p0, o);
-    __builtin_nontemporal_store(p1, o + 1);
+                                                        void* __restrict__ out, int64_t groups) {
+  constexpr int G = OUT == kOutF32 ? 4 : 8;
+  typedef typename std::conditional<G == 4, uint32_t, u32x2>::type QWord;
+  const int64_t gpr = N / G;  // groups per row
+  const int64_t g0 = (int64_t)blockIdx.x * (kThreads * kDqUnroll) + threadIdx.x;
+  QWord w[kDqUnroll];
+  float sc[kDqUnroll];
+#pragma unroll
+  for (int k = 0; k < kDqUnroll; ++k) {
+    const int64_t g = g0 + (int64_t)k * kThreads;
+    if (g < groups) {
+      const int64_t row = g / gpr;
+      const int64_t col = (g - row * gpr) * G;
+      w[k] = __builtin_nontemporal_load((const FP8BQ_GLOBAL QWord*)(q) + g);
+      sc[k] = ((const FP8BQ_GLOBAL float*)s)[(row / bm) * TN + col / bn];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kDqUnroll; ++k) {
+    const int64_t g = g0 + (int64_t)k * kThreads;
+    if (g >= groups) continue;
+    if constexpr (OUT == kOutF32) {
+      const f32x4 a = dq4(w[k], sc[k]);
+      __builtin_nontemporal_store(a, (FP8BQ_GLOBAL f32x4*)out + g);
+    } else {
+      const f32x4 a = dq4(w[k].x, sc[k]);
+      const f32x4 b = dq4(w[k].y, sc[k]);
+      const u32x4 p{bf16_rne(a.x) | (bf16_rne(a.y) << 16), bf16_rne(a.z) | (bf16_rne(a.w) << 16),
+                    bf16_rne(b.x) | (bf16_rne(b.y) << 16), bf16_rne(b.z) | (bf16_rne(b.w) << 16)};
+      __builtin_nontemporal_store(p, (FP8BQ_GLOBAL u32x4*)out + g);
+    }
   }
 }
 
@@ -647,7 +761,7 @@ struct ArgTensor {
   float* s;
   int32_t M;
   int32_t N;
-  int32_t general;  // 1: element-wise tile body for this tensor
+  int32_t body;     // Body of this tensor
   int32_t pad;
 };
 
@@ -680,8 +794,8 @@ __global__ __launch_bounds__(kThreads) void quantize_group_args(const GroupArgs<
   d.M = at.M;
   d.N = at.N;
   d.TN = (at.N + bn - 1) / bn;
-  d.general = at.general;
-  d.UN = at.general ? d.TN : (at.N + 127) / 128;
+  d.body = at.body;
+  d.UN = at.body != kBodyVec ? d.TN : (at.N + 127) / 128;
   d.pad = 0;
   d.reserved = 0;
   run_unit<KIND>(d, bm, bn, u - a.start[lo], red);

@@ -173,8 +173,9 @@ enum fp8bq_out_dtype {
  *   scale_inv  device, fp32 [ceil(M/bm), ceil(N/bn)] row-major
  *   out        device, [M, N] row-major of out_dtype (fp32 or BF16), aligned
  *              to its element size; must not overlap q or scale_inv
- * Any shape, block size and alignment; N % 16 == 0, bn % 16 == 0 and 16-byte
- * aligned q/out take the vectorized kernel.  NaN codes decode to NaN.
+ * Any shape, block size and alignment; with G = 4 (fp32) or 8 (BF16),
+ * N % G == 0, bn % G == 0, q aligned to G bytes and out to 16 bytes take the
+ * vectorized kernel.  NaN codes decode to NaN.
  */
 int fp8bq_dequantize(const void* q, const float* scale_inv, int64_t M, int64_t N, int32_t bm,
                      int32_t bn, void* out, int32_t out_dtype, void* stream);

@@ -98,6 +98,22 @@ def test_general_path_odd_and_misaligned(gpu_lib, block):
             assert_matches_oracle(x, q, s, bm, bn, f"{M}x{N}/{block}/off{off}")
 
 
+@pytest.mark.parametrize("block", [(1, 4096), (16, 1024), (128, 64), (8, 8), (1, 16384), (32, 512)])
+def test_register_tile_body(gpu_lib, block):
+    """Blocks of at most 16384 elements with 8-aligned columns take the
+    register-resident tile body; ragged edges included."""
+    bm, bn = block
+    g = torch.Generator(device=DEV).manual_seed(17)
+    for M, N in ((77, 128), (1000, 3000), (4097, 1008), (33, 16392)):
+        say("reg tile", block, M, N)
+        x = (torch.randn((M, N), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+        x[M // 2] = 0
+        q, s = fq.quantize(x, block)
+        assert_matches_oracle(x, q, s, bm, bn, f"reg {M}x{N}/{block}")
+    outs = fq.quantize_many([x, x[:100].contiguous()], block)
+    assert torch.equal(outs[0][0].view(torch.uint8), q.view(torch.uint8))
+
+
 def test_special_values(gpu_lib):
     """Zero, -0, BF16 subnormals, huge magnitudes and exact e4m3 ties."""
     rows = []
