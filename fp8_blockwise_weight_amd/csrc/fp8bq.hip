@@ -28,7 +28,9 @@ int hip_failed(hipError_t e) {
 
 constexpr int kMaxDevices = 64;
 constexpr int64_t kMaxUnits = INT32_MAX;  // work units per tensor (32-bit unit math)
-constexpr int64_t kMaxGrid = INT32_MAX;   // workgroups per launch
+// Workgroups per launch: a dispatch counts at most 2^32 - 1 work-items.
+// Kernels whose work exceeds the grid cover it in grid-sized rounds.
+constexpr int64_t kMaxGrid = static_cast<int64_t>(UINT32_MAX) / fp8bq::kThreads;
 
 // Dynamic LDS reserved (and left unused) by every vectorized quantize launch
 // so that at most 4 workgroups share a CU (160 KB of LDS per gfx950 CU).
@@ -205,6 +207,52 @@ void launch_big_quant(const fp8bq::Big& b, const float* amax, float* scale_inv, 
                      dim3(fp8bq::kThreads), 0, st, amax, scale_inv, nt);
 }
 
+constexpr int kBigGroupCap = 128;  // tensors per grouped large-tile launch
+
+// Whole tensors with large tiles, up to kBigGroupCap per group: 4 launches per
+// group (zero maxima, maxima, quantize, scales).  Returns false if the
+// group's item counts do not fit 32 bits (the caller then goes per tensor).
+bool launch_big_group(const fp8bq_tensor* const* ts, int32_t n, int32_t bm, int32_t bn,
+                      hipStream_t st) {
+  fp8bq::BigGroupArgs<kBigGroupCap> a;
+  std::memset(&a, 0, sizeof(a));
+  int64_t tiles = 0, maxi = 0, quanti = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const fp8bq_tensor& t = *ts[i];
+    const fp8bq::Big b = make_big(t.x, t.M, t.N, bm, bn, 0, 0, t.q);
+    a.tile_start[i] = static_cast<int32_t>(tiles);
+    a.max_start[i] = static_cast<int32_t>(maxi);
+    a.quant_start[i] = static_cast<int32_t>(quanti);
+    a.e[i].x = static_cast<const uint16_t*>(t.x);
+    a.e[i].q = static_cast<uint8_t*>(t.q);
+    a.e[i].s = t.scale_inv;
+    a.e[i].M = static_cast<int32_t>(t.M);
+    a.e[i].N = static_cast<int32_t>(t.N);
+    a.e[i].cpt = static_cast<int32_t>(b.cpt);
+    a.e[i].flags = b.flat | (b.vec << 1);
+    tiles += b.TMl * b.TNl;
+    maxi += b.TMl * b.TNl * ceil_div(b.cpt, fp8bq::kChunksPerMax);
+    quanti += b.items;
+    if (tiles > INT32_MAX || maxi > INT32_MAX || quanti > INT32_MAX || b.cpt > INT32_MAX) {
+      return false;
+    }
+  }
+  a.tile_start[n] = static_cast<int32_t>(tiles);
+  a.max_start[n] = static_cast<int32_t>(maxi);
+  a.quant_start[n] = static_cast<int32_t>(quanti);
+  const dim3 blk(fp8bq::kThreads);
+  const dim3 gt(static_cast<unsigned>(ceil_div(tiles, fp8bq::kThreads)));
+  hipLaunchKernelGGL((fp8bq::big_group_tiles<kBigGroupCap, 0>), gt, blk, 0, st, a, n,
+                     static_cast<int32_t>(tiles));
+  hipLaunchKernelGGL((fp8bq::big_group_max<kBigGroupCap>), dim3(grid_for(maxi)), blk, 0, st, a, n,
+                     bm, bn);
+  hipLaunchKernelGGL((fp8bq::big_group_quant<kBigGroupCap>), dim3(grid_for(quanti)), blk, 0, st, a,
+                     n, bm, bn);
+  hipLaunchKernelGGL((fp8bq::big_group_tiles<kBigGroupCap, 1>), gt, blk, 0, st, a, n,
+                     static_cast<int32_t>(tiles));
+  return true;
+}
+
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 template <int KIND, int CAP>
@@ -223,7 +271,7 @@ void launch_args(const std::vector<Desc>& ds, const std::vector<int64_t>& st, in
     a.t[i].body = ds[i].body;
   }
   a.start[n] = static_cast<int32_t>(total);
-  hipLaunchKernelGGL((fp8bq::quantize_group_args<KIND, CAP>), dim3(static_cast<unsigned>(total)),
+  hipLaunchKernelGGL((fp8bq::quantize_group_args<KIND, CAP>), dim3(grid_for(total)),
                      dim3(fp8bq::kThreads), lds_for(KIND), s, a, n, bm, bn,
                      static_cast<int32_t>(total));
 }
@@ -321,28 +369,54 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
   }
   const int32_t n = static_cast<int32_t>(g_descs.size());
   if (n == 0 && !any_big) return FP8BQ_OK;
-  // Each launch covers at most kMaxGrid units.
-  if (total > kMaxGrid) return FP8BQ_ERR_INVALID_ARGUMENT;
+  // The table in the kernel arguments indexes units with 32 bits.
+  const bool args_fit = n <= fp8bq::kArgsMax && total <= INT32_MAX;
   int st = device_check();
   if (st != FP8BQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (any_big) {
+    // Grouped two-pass launches, kBigGroupCap tensors at a time.
+    std::vector<const fp8bq_tensor*> group;
+    auto flush = [&]() {
+      if (group.empty()) return;
+      if (!launch_big_group(group.data(), static_cast<int32_t>(group.size()), bm, bn, s)) {
+        for (const fp8bq_tensor* t : group) {  // item counts beyond 32 bits: per tensor
+          const fp8bq::Big b = make_big(t->x, t->M, t->N, bm, bn, 0, 0, t->q);
+          launch_big_amax(b, t->scale_inv, s);
+          launch_big_quant(b, t->scale_inv, t->scale_inv, s);
+        }
+      }
+      group.clear();
+    };
     for (int32_t i = 0; i < count; ++i) {
       const fp8bq_tensor& t = list[i];
       if (t.M == 0 || t.N == 0 || !big_tiles(t.M, t.N, bm, bn)) continue;
-      const fp8bq::Big b = make_big(t.x, t.M, t.N, bm, bn, 0, 0, t.q);
-      launch_big_amax(b, t.scale_inv, s);
-      launch_big_quant(b, t.scale_inv, t.scale_inv, s);
+      group.push_back(&t);
+      if (static_cast<int>(group.size()) == kBigGroupCap) flush();
     }
+    flush();
   }
-  if (n > 0 && n <= fp8bq::kArgsMax) {
+  if (n > 0 && args_fit) {
     // The table travels in the kernel arguments: no copy, no workspace.
     switch (kind) {
       case fp8bq::kT128: launch_args_kind<fp8bq::kT128>(g_descs, g_starts, bm, bn, total, s); break;
       case fp8bq::kT64: launch_args_kind<fp8bq::kT64>(g_descs, g_starts, bm, bn, total, s); break;
       case fp8bq::kR128: launch_args_kind<fp8bq::kR128>(g_descs, g_starts, bm, bn, total, s); break;
       default: launch_args_kind<fp8bq::kGeneral>(g_descs, g_starts, bm, bn, total, s); break;
+    }
+  } else if (n > 0 && need == 0) {
+    // At most kArgsMax tensors but more than 2^31 units in all (tiny blocks):
+    // one launch per tensor.
+    for (int32_t i = 0; i < n; ++i) {
+      const Desc& d = g_descs[i];
+      const int64_t units = (i + 1 < n ? g_starts[i + 1] : total) - g_starts[i];
+      switch (d.body != fp8bq::kBodyVec ? static_cast<int>(fp8bq::kGeneral) : kind) {
+        case fp8bq::kT128: launch_one<fp8bq::kT128>(d, bm, bn, units, s); break;
+        case fp8bq::kT64: launch_one<fp8bq::kT64>(d, bm, bn, units, s); break;
+        case fp8bq::kR128: launch_one<fp8bq::kR128>(d, bm, bn, units, s); break;
+        default: launch_one<fp8bq::kGeneral>(d, bm, bn, units, s); break;
+      }
     }
   } else if (n > 0) {
     // Larger groups: the table is copied into the workspace on the stream.
@@ -483,9 +557,7 @@ int fp8bq_dequantize(const void* q, const float* scale_inv, int64_t M, int64_t N
   if (vec) {
     const int64_t groups = static_cast<int64_t>(n) / G;
     const int64_t per_block = static_cast<int64_t>(fp8bq::kThreads) * fp8bq::kDqUnroll;
-    const int64_t blocks = (groups + per_block - 1) / per_block;
-    if (blocks > kMaxGrid) return FP8BQ_ERR_INVALID_ARGUMENT;
-    const dim3 grid(static_cast<unsigned>(blocks));
+    const dim3 grid(grid_for((groups + per_block - 1) / per_block));
     if (out_dtype == FP8BQ_OUT_F32) {
       hipLaunchKernelGGL(fp8bq::dequant_vec<fp8bq::kOutF32>, grid, dim3(fp8bq::kThreads), 0, s, qb,
                          scale_inv, N, bm, bn, tn, out, groups);

@@ -413,18 +413,29 @@ __device__ __forceinline__ int64_t xcd_unit(int64_t wg, int64_t n) {
   return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 
+// Calls f(u) for the units this workgroup owns: units are handed out in
+// rounds of gridDim.x (a dispatch holds at most 2^32 - 1 work-items, i.e.
+// 16,777,215 workgroups of 256), XCD-aware within each round.  Barriers in f
+// are safe: every thread of a workgroup runs the same rounds.
+template <typename F>
+__device__ __forceinline__ void for_each_unit(int64_t total, F&& f) {
+  for (int64_t b0 = 0; b0 < total; b0 += gridDim.x) {
+    const int64_t n = (total - b0) < (int64_t)gridDim.x ? (total - b0) : (int64_t)gridDim.x;
+    if ((int64_t)blockIdx.x >= n) return;
+    f(b0 + xcd_unit(blockIdx.x, n));
+  }
+}
+
 // One tensor: workgroup -> unit -> (unit row, unit column) of d.  The grid
 // normally equals `total`; larger counts are covered in grid-sized rounds.
 template <int KIND>
 __global__ __launch_bounds__(kThreads) void quantize_one(Desc d, int32_t bm, int32_t bn,
                                                          int64_t total) {
   __shared__ uint32_t red[8];
-  for (int64_t b0 = 0; b0 < total; b0 += gridDim.x) {
-    const int64_t n = (total - b0) < (int64_t)gridDim.x ? (total - b0) : (int64_t)gridDim.x;
-    if ((int64_t)blockIdx.x >= n) return;
-    run_unit<KIND>(d, bm, bn, b0 + xcd_unit(blockIdx.x, n), red);
+  for_each_unit(total, [&](int64_t u) {
+    run_unit<KIND>(d, bm, bn, u, red);
     __syncthreads();  // red[] is reused by the next round
-  }
+  });
 }
 
 // A list of tensors: start[t] is the first global unit of tensor t
@@ -435,10 +446,7 @@ __global__ __launch_bounds__(kThreads) void quantize_group(const Desc* __restric
                                                            int32_t count, int32_t bm, int32_t bn,
                                                            int64_t total) {
   __shared__ uint32_t red[8];
-  for (int64_t b0 = 0; b0 < total; b0 += gridDim.x) {
-    const int64_t n = (total - b0) < (int64_t)gridDim.x ? (total - b0) : (int64_t)gridDim.x;
-    if ((int64_t)blockIdx.x >= n) return;
-    const int64_t u = b0 + xcd_unit(blockIdx.x, n);
+  for_each_unit(total, [&](int64_t u) {
     int lo = 0, hi = count - 1;  // largest t with start[t] <= u
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -451,7 +459,7 @@ __global__ __launch_bounds__(kThreads) void quantize_group(const Desc* __restric
     const Desc d = descs[lo];
     run_unit<KIND>(d, bm, bn, u - start[lo], red);
     __syncthreads();  // red[] is reused by the next round
-  }
+  });
 }
 
 // ---------------------------------------------------------------- large tiles and shards
@@ -602,36 +610,134 @@ __device__ __forceinline__ bool big_chunk(const Big& b, int64_t tile, int64_t k,
 // tensor) would otherwise serialize on it.
 constexpr int64_t kChunksPerMax = 16;
 
-__global__ __launch_bounds__(kThreads) void big_max(Big b, uint32_t* __restrict__ amax_bits,
-                                                    int64_t items) {
-  __shared__ uint32_t red[4];
+// Item `it` of pass 1 for one tensor: kChunksPerMax chunks of one tile.
+__device__ __forceinline__ void big_max_item(const Big& b, uint32_t* amax_bits, int64_t it,
+                                             uint32_t* red) {
   const int64_t groups = (b.cpt + kChunksPerMax - 1) / kChunksPerMax;
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int64_t tile = it / groups;
-    const int64_t g = it - tile * groups;
-    uint32_t m = 0;
-    for (int64_t k = g * kChunksPerMax; k < (g + 1) * kChunksPerMax && k < b.cpt; ++k) {
-      if (!big_chunk<0>(b, tile, k, 0.0f, m)) break;
-    }
-    const uint32_t wm = block_max(m, red);
-    if (threadIdx.x == 0 && wm != 0) {
-      const uint32_t cur = __hip_atomic_load(&amax_bits[tile], __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-      if ((wm << 16) > cur) atomicMax(&amax_bits[tile], wm << 16);
-    }
+  const int64_t tile = it / groups;
+  const int64_t g = it - tile * groups;
+  uint32_t m = 0;
+  for (int64_t k = g * kChunksPerMax; k < (g + 1) * kChunksPerMax && k < b.cpt; ++k) {
+    if (!big_chunk<0>(b, tile, k, 0.0f, m)) break;
+  }
+  const uint32_t wm = block_max(m, red);
+  if (threadIdx.x == 0 && wm != 0) {
+    const uint32_t cur = __hip_atomic_load(&amax_bits[tile], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    if ((wm << 16) > cur) atomicMax(&amax_bits[tile], wm << 16);
   }
 }
 
-// Pass 2: quantize chunk by chunk with the finished maxima.
+// Item `it` of pass 2 for one tensor: one chunk, quantized with its tile's maximum.
+__device__ __forceinline__ void big_quant_item(const Big& b, const float* amax, int64_t it) {
+  const int64_t tile = it / b.cpt;
+  const int64_t k = it - tile * b.cpt;
+  float s, r;
+  tile_scale_f(((const FP8BQ_GLOBAL float*)amax)[tile], s, r);
+  uint32_t unused = 0;
+  big_chunk<1>(b, tile, k, r, unused);
+}
+
+__global__ __launch_bounds__(kThreads) void big_max(Big b, uint32_t* __restrict__ amax_bits,
+                                                    int64_t items) {
+  __shared__ uint32_t red[4];
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) big_max_item(b, amax_bits, it, red);
+}
+
 __global__ __launch_bounds__(kThreads) void big_quant(Big b, const float* __restrict__ amax) {
-  for (int64_t it = blockIdx.x; it < b.items; it += gridDim.x) {
-    const int64_t tile = it / b.cpt;
-    const int64_t k = it - tile * b.cpt;
-    float s, r;
-    tile_scale_f(((const FP8BQ_GLOBAL float*)amax)[tile], s, r);
-    uint32_t unused = 0;
-    big_chunk<1>(b, tile, k, r, unused);
+  for (int64_t it = blockIdx.x; it < b.items; it += gridDim.x) big_quant_item(b, amax, it);
+}
+
+// Grouped form for a list of whole tensors with large tiles (phase 0): the
+// table rides in the kernel arguments and each kernel covers every tensor,
+// so a group costs 4 launches instead of 4 per tensor.
+struct BigEntry {
+  const uint16_t* x;
+  uint8_t* q;
+  float* s;        // scale_inv, also the scratch for the maxima
+  int32_t M;
+  int32_t N;
+  int32_t cpt;     // chunks per tile
+  int32_t flags;   // bit 0: flat, bit 1: vec
+};
+
+template <int CAP>
+struct BigGroupArgs {
+  int32_t tile_start[CAP + 1];   // prefix of tiles (fill and finalize)
+  int32_t max_start[CAP + 1];    // prefix of pass-1 items
+  int32_t quant_start[CAP + 1];  // prefix of pass-2 items
+  BigEntry e[CAP];
+};
+
+template <int CAP>
+__device__ __forceinline__ int big_find(const int32_t* start, int count, int64_t u) {
+  int lo = 0, hi = count - 1;  // largest t with start[t] <= u
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (start[mid] <= u) {
+      lo = mid;
+    } else {
+      hi = mid - 1;
+    }
   }
+  return lo;
+}
+
+__device__ __forceinline__ Big big_of(const BigEntry& e, int32_t bm, int32_t bn) {
+  Big b;
+  b.x = e.x;
+  b.q = e.q;
+  b.M = e.M;
+  b.N = e.N;
+  b.bm = bm;
+  b.bn = bn;
+  b.row_phase = 0;
+  b.col_phase = 0;
+  b.TMl = (e.M + bm - 1) / bm;
+  b.TNl = (e.N + bn - 1) / bn;
+  b.cpt = e.cpt;
+  b.items = b.TMl * b.TNl * b.cpt;
+  b.flat = e.flags & 1;
+  b.vec = (e.flags >> 1) & 1;
+  return b;
+}
+
+// PHASE 0: zero every tensor's maxima; PHASE 1: maxima -> scales in place.
+template <int CAP, int PHASE>
+__global__ __launch_bounds__(kThreads) void big_group_tiles(const BigGroupArgs<CAP> a, int32_t count,
+                                                            int32_t total) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= total) return;
+  const int t = big_find<CAP>(a.tile_start, count, i);
+  FP8BQ_GLOBAL float* sp = (FP8BQ_GLOBAL float*)a.e[t].s + (i - a.tile_start[t]);
+  if (PHASE == 0) {
+    *(FP8BQ_GLOBAL uint32_t*)sp = 0u;
+  } else {
+    float s, r;
+    tile_scale_f(*sp, s, r);
+    *sp = s;
+  }
+}
+
+template <int CAP>
+__global__ __launch_bounds__(kThreads) void big_group_max(const BigGroupArgs<CAP> a, int32_t count,
+                                                          int32_t bm, int32_t bn) {
+  __shared__ uint32_t red[4];
+  for_each_unit(a.max_start[count], [&](int64_t u) {
+    const int t = big_find<CAP>(a.max_start, count, u);
+    const Big b = big_of(a.e[t], bm, bn);
+    big_max_item(b, (uint32_t*)a.e[t].s, u - a.max_start[t], red);
+  });
+}
+
+template <int CAP>
+__global__ __launch_bounds__(kThreads) void big_group_quant(const BigGroupArgs<CAP> a, int32_t count,
+                                                            int32_t bm, int32_t bn) {
+  for_each_unit(a.quant_start[count], [&](int64_t u) {
+    const int t = big_find<CAP>(a.quant_start, count, u);
+    const Big b = big_of(a.e[t], bm, bn);
+    big_quant_item(b, a.e[t].s, u - a.quant_start[t]);
+  });
 }
 
 // out[i] = 0 for i < n.
@@ -694,7 +800,10 @@ __global__ __launch_bounds__(kThreads) void dequant_vec(const uint8_t* __restric
   constexpr int G = OUT == kOutF32 ? 4 : 8;
   typedef typename std::conditional<G == 4, uint32_t, u32x2>::type QWord;
   const int64_t gpr = N / G;  // groups per row
-  const int64_t g0 = (int64_t)blockIdx.x * (kThreads * kDqUnroll) + threadIdx.x;
+  const int64_t per_block = (int64_t)kThreads * kDqUnroll;
+  for (int64_t b0 = (int64_t)blockIdx.x * per_block; b0 < groups;
+       b0 += (int64_t)gridDim.x * per_block) {
+  const int64_t g0 = b0 + threadIdx.x;
   QWord w[kDqUnroll];
   float sc[kDqUnroll];
 #pragma unroll
@@ -721,6 +830,7 @@ __global__ __launch_bounds__(kThreads) void dequant_vec(const uint8_t* __restric
                     bf16_rne(b.x) | (bf16_rne(b.y) << 16), bf16_rne(b.z) | (bf16_rne(b.w) << 16)};
       __builtin_nontemporal_store(p, (FP8BQ_GLOBAL u32x4*)out + g);
     }
+  }
   }
 }
 
@@ -776,29 +886,31 @@ __global__ __launch_bounds__(kThreads) void quantize_group_args(const GroupArgs<
                                                                 int32_t count, int32_t bm,
                                                                 int32_t bn, int32_t total) {
   __shared__ uint32_t red[8];
-  const int64_t u = xcd_unit(blockIdx.x, total);
-  int lo = 0, hi = count - 1;  // largest t with start[t] <= u
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.start[mid] <= u) {
-      lo = mid;
-    } else {
-      hi = mid - 1;
+  for_each_unit(total, [&](int64_t u) {
+    int lo = 0, hi = count - 1;  // largest t with start[t] <= u
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.start[mid] <= u) {
+        lo = mid;
+      } else {
+        hi = mid - 1;
+      }
     }
-  }
-  const ArgTensor& at = a.t[lo];
-  Desc d;
-  d.x = at.x;
-  d.q = at.q;
-  d.s = at.s;
-  d.M = at.M;
-  d.N = at.N;
-  d.TN = (at.N + bn - 1) / bn;
-  d.body = at.body;
-  d.UN = at.body != kBodyVec ? d.TN : (at.N + 127) / 128;
-  d.pad = 0;
-  d.reserved = 0;
-  run_unit<KIND>(d, bm, bn, u - a.start[lo], red);
+    const ArgTensor& at = a.t[lo];
+    Desc d;
+    d.x = at.x;
+    d.q = at.q;
+    d.s = at.s;
+    d.M = at.M;
+    d.N = at.N;
+    d.TN = (at.N + bn - 1) / bn;
+    d.body = at.body;
+    d.UN = at.body != kBodyVec ? d.TN : (at.N + 127) / 128;
+    d.pad = 0;
+    d.reserved = 0;
+    run_unit<KIND>(d, bm, bn, u - a.start[lo], red);
+    __syncthreads();  // red[] is reused by the next round
+  });
 }
 
 // The final cast alone: clamp and convert n floats.

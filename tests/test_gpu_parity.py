@@ -525,6 +525,26 @@ def test_per_tensor_and_large_tiles(gpu_lib):
         assert_properties_gpu(x, q, s, sp.M, sp.N, sp.name)
 
 
+def test_grouped_large_tiles_many_tensors(gpu_lib):
+    """More than 128 tensors with large tiles in one grouped call (several
+    grouped two-pass launches), mixed with ordinary tensors, equal single
+    calls and the oracle."""
+    g = torch.Generator(device=DEV).manual_seed(61)
+    rng = np.random.default_rng(61)
+    mats = []
+    for i in range(300):
+        M, N = int(rng.integers(260, 400)), int(rng.choice([264, 300, 333, 512]))
+        mats.append((torch.randn((M, N), generator=g, device=DEV) * 0.05).to(torch.bfloat16))
+    mats[5] = torch.zeros_like(mats[5])
+    outs = fq.quantize_many(mats, (512, 512))
+    for i, (x, (q, s)) in enumerate(zip(mats, outs)):
+        q1, s1 = fq.quantize(x, (512, 512))
+        assert torch.equal(q1.view(torch.uint8), q.view(torch.uint8)), i
+        assert torch.equal(s1.view(torch.int32), s.view(torch.int32)), i
+    for i in (0, 5, 150, 299):
+        assert_matches_oracle(mats[i], outs[i][0], outs[i][1], 512, 512, f"grouped large [{i}]")
+
+
 def test_per_tensor_vocab_matrix(gpu_lib):
     """One scale for the whole 151937x4096 matrix (1.2 GB): the scale from the
     exact maximum, sampled rows against the oracle, invariants everywhere."""
@@ -538,3 +558,39 @@ def test_per_tensor_vocab_matrix(gpu_lib):
         q_ref, _ = oracle.quantize_with_amax(bits_np(xs), sp.M, sp.N, np.array([[amax]]))
         assert np.array_equal(codes_np(q[r0:r0 + 300].contiguous()), q_ref), r0
     assert_properties_gpu(x, q, s, sp.M, sp.N, "vocab per-tensor")
+
+
+# ------------------------------------------------------------------ maximum sizes
+
+def test_beyond_2_31_elements(gpu_lib):
+    """A 33000x65536 matrix (2.16e9 elements, 4.3 GB) through the [128,128],
+    [1,128] and register-tile kernels and a 1 x (2^31 - 1) row through the
+    general kernel: scales everywhere, tiles past element 2^31 against the
+    oracle, and the dequantized tail."""
+    M, N = 33000, 65536
+    g = torch.Generator(device=DEV).manual_seed(59)
+    x = (torch.randn((M, N), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    x[-1, -5:] = 3.0
+    for block in [(128, 128), (1, 128), (8, 1024)]:
+        bm, bn = block
+        say("2^31+", block)
+        q, s = fq.quantize(x, block)
+        assert_scales_match_oracle(x, s, bm, bn, f"2^31+ {block}")
+        TM, TN = fq.scale_shape(M, N, bm, bn)
+        tiles = [(TM - 1, TN - 1), (TM - 1, 0), ((2 ** 31 // N) // bm + 1, TN // 2), (0, 0)]
+        assert_tiles_match_oracle(x, q, s, bm, bn, tiles, f"2^31+ {block}")
+        tail = fq.dequantize(q[-bm:].contiguous(), s[-1:].contiguous(), block,
+                             out_dtype=torch.bfloat16)
+        want = oracle.dequantize(codes_np(q[-bm:].contiguous()), s[-1:].cpu().numpy(), bm, bn, "bf16")
+        assert np.array_equal(tail.float().cpu().numpy().astype(np.float64), want)
+        del q, s, tail
+    del x
+    torch.cuda.empty_cache()
+    n = 2 ** 31 - 1
+    row = (torch.randn((1, n), generator=g, device=DEV) * 0.02).to(torch.bfloat16)   # N odd: general kernel
+    row[0, n - 1] = -7.0
+    q, s = fq.quantize(row, (1, 128))
+    assert s.shape == (1, -(-n // 128))
+    assert_tiles_match_oracle(row, q, s, 1, 128, [(0, 0), (0, s.shape[1] - 1), (0, s.shape[1] // 2)],
+                              "1 x 2^31-1")
+    assert int(q.view(torch.uint8)[0, n - 1]) == 0xFE
