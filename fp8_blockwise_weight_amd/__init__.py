@@ -131,6 +131,33 @@ def _check_input(x) -> None:
         raise TypeError("x must be contiguous row-major")
 
 
+def _check_buffer(t, shape, elem_size: int, device, what: str) -> None:
+    """A caller-supplied output must match exactly: the kernels write every
+    byte of it, and nothing outside it."""
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.element_size() != elem_size:
+        raise TypeError(f"{what} must have {elem_size}-byte elements, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{what} is on {t.device}, expected {device}")
+
+
+def _check_outputs(out, M: int, N: int, bm: int, bn: int, device) -> None:
+    import torch
+
+    q, s = out
+    _check_buffer(q, (M, N), 1, device, "q")
+    _check_buffer(s, scale_shape(M, N, bm, bn), 4, device, "scale_inv")
+    if s.dtype != torch.float32:
+        raise TypeError("scale_inv must be float32")
+
+
 def _stream(device) -> int:
     import torch
 
@@ -154,6 +181,7 @@ def quantize(x, block_size=(128, 128), out=None):
         q = torch.empty((M, N), dtype=torch.float8_e4m3fn, device=x.device)
         s = torch.empty(scale_shape(M, N, bm, bn), dtype=torch.float32, device=x.device)
     else:
+        _check_outputs(out, M, N, bm, bn, x.device)
         q, s = out
     lib = load_library()
     with torch.cuda.device(x.device):
@@ -200,15 +228,23 @@ def quantize_many(tensors: Sequence, block_size=(128, 128), outputs: Optional[Se
         outputs = [(torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=dev),
                     torch.empty(scale_shape(*x.shape, bm, bn), dtype=torch.float32, device=dev))
                    for x in tensors]
+    else:
+        outputs = list(outputs)
+        if len(outputs) != len(tensors):
+            raise ValueError("outputs must hold one (q, scale_inv) pair per tensor")
+        for x, out in zip(tensors, outputs):
+            _check_outputs(out, *x.shape, bm, bn, dev)
     need = workspace_bytes(len(tensors))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the tensors' device")
     arr = make_entries(tensors, outputs)
     lib = load_library()
     with torch.cuda.device(dev):
         _check("fp8bq_quantize_many",
                lib.fp8bq_quantize_many(arr, len(tensors), bm, bn, workspace.data_ptr(),
-                                       workspace.numel(), _stream(dev)))
+                                       workspace.numel() * workspace.element_size(), _stream(dev)))
     return list(outputs)
 
 
@@ -230,8 +266,14 @@ def dequantize(q, scale_inv, block_size=(128, 128), out_dtype=None, out=None):
     if tuple(scale_inv.shape) != scale_shape(M, N, bm, bn) or scale_inv.dtype != torch.float32 \
             or not scale_inv.is_contiguous():
         raise TypeError("scale_inv must be contiguous float32 [ceil(M/bm), ceil(N/bn)]")
+    if scale_inv.device != q.device:
+        raise ValueError("scale_inv must be on q's device")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=q.device)
+    else:
+        _check_buffer(out, (M, N), 4 if out_dtype == torch.float32 else 2, q.device, "out")
+        if out.dtype != out_dtype:
+            raise TypeError(f"out must be {out_dtype}")
     code = 0 if out_dtype == torch.float32 else 1
     with torch.cuda.device(q.device):
         _check("fp8bq_dequantize",
@@ -260,6 +302,8 @@ def tile_amax(x, block_size=(128, 128), phase=(0, 0), out=None):
     _check_input(x)
     M, N = x.shape
     shape = local_grid(M, N, bm, bn, phase)
+    if out is not None:
+        _check_buffer(out, shape, 4, x.device, "amax")
     amax = out if out is not None else torch.empty(shape, dtype=torch.float32, device=x.device)
     with torch.cuda.device(x.device):
         _check("fp8bq_tile_amax",
@@ -279,13 +323,16 @@ def quantize_with_amax(x, amax, block_size=(128, 128), phase=(0, 0), out=None):
     _check_input(x)
     M, N = x.shape
     shape = local_grid(M, N, bm, bn, phase)
-    if tuple(amax.shape) != shape or amax.dtype != torch.float32 or not amax.is_contiguous():
-        raise TypeError(f"amax must be contiguous float32 {shape}")
+    _check_buffer(amax, shape, 4, x.device, "amax")
+    if amax.dtype != torch.float32:
+        raise TypeError("amax must be float32")
     if out is None:
         q = torch.empty((M, N), dtype=torch.float8_e4m3fn, device=x.device)
         s = torch.empty(shape, dtype=torch.float32, device=x.device)
     else:
         q, s = out
+        _check_buffer(q, (M, N), 1, x.device, "q")
+        _check_buffer(s, shape, 4, x.device, "scale_inv")
     with torch.cuda.device(x.device):
         _check("fp8bq_quantize_amax",
                load_library().fp8bq_quantize_amax(x.data_ptr(), M, N, bm, bn, phase[0], phase[1],

@@ -201,3 +201,24 @@ def test_python_rejects_cpu_tensor():
 def test_entry_layout_matches_header():
     # fp8bq_tensor: three pointers then two int64 -> 40 bytes on LP64
     assert ctypes.sizeof(fq.TensorEntry) == 40
+
+
+def test_python_output_checks():
+    """Caller-supplied outputs are checked before any library call."""
+    import torch
+
+    cpu = torch.device("cpu")
+    q = torch.empty((4, 8), dtype=torch.uint8)
+    s = torch.empty((1, 1), dtype=torch.float32)
+    fq._check_outputs((q, s), 4, 8, 128, 128, cpu)                     # exact match passes
+    with pytest.raises(ValueError):
+        fq._check_outputs((torch.empty((4, 9), dtype=torch.uint8), s), 4, 8, 128, 128, cpu)
+    with pytest.raises(ValueError):
+        fq._check_outputs((q, torch.empty((3, 1))), 4, 8, 2, 128, cpu)  # scale must be (2, 1)
+    fq._check_outputs((q, torch.empty((2, 1))), 4, 8, 2, 128, cpu)
+    with pytest.raises(TypeError):
+        fq._check_outputs((torch.empty((4, 8), dtype=torch.int16), s), 4, 8, 128, 128, cpu)
+    with pytest.raises(TypeError):
+        fq._check_outputs((q, s.to(torch.float64)), 4, 8, 128, 128, cpu)
+    with pytest.raises(ValueError):
+        fq._check_outputs((torch.empty((8, 4), dtype=torch.uint8).t(), s), 4, 8, 128, 128, cpu)
