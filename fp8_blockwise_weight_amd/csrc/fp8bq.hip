@@ -97,9 +97,10 @@ int make_desc(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, void*
   }
   const bool aligned = (N % 8) == 0 && (xa & 15) == 0 && (qa & 7) == 0;
   const bool vec = kind != fp8bq::kGeneral && aligned;
-  // A whole tile fits the register body: at most kRegTile elements, 8-aligned columns.
-  const bool reg = aligned && (bn % 8) == 0 &&
-                   static_cast<int64_t>(bm) * static_cast<int64_t>(bn) <= fp8bq::kRegTile;
+  // 8-aligned tile columns: a whole tile in registers up to kRegTile elements,
+  // two vector passes above that.
+  const bool colvec = aligned && (bn % 8) == 0;
+  const bool reg = colvec && static_cast<int64_t>(bm) * static_cast<int64_t>(bn) <= fp8bq::kRegTile;
   d->x = static_cast<const uint16_t*>(x);
   d->q = static_cast<uint8_t*>(q);
   d->s = s;
@@ -117,7 +118,7 @@ int make_desc(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, void*
   } else {
     if (TN > INT32_MAX) return FP8BQ_ERR_INVALID_ARGUMENT;
     d->UN = static_cast<int32_t>(TN);
-    d->body = reg ? fp8bq::kBodyRegTile : fp8bq::kBodyScalar;
+    d->body = reg ? fp8bq::kBodyRegTile : (colvec ? fp8bq::kBodyLoopVec : fp8bq::kBodyScalar);
     if (TM > kMaxUnits / TN) return FP8BQ_ERR_INVALID_ARGUMENT;
     u = TM * TN;
   }

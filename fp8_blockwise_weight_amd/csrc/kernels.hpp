@@ -67,8 +67,9 @@ struct Desc {
 
 // Unit bodies: the block-shape kernel of the launch (a [128,128], [64,64] or
 // [1,128] unit), a whole tile held in registers (any block of at most
-// kRegTile elements with 8-aligned columns), or a tile element by element.
-enum Body : int { kBodyVec = 0, kBodyScalar = 1, kBodyRegTile = 2 };
+// kRegTile elements with 8-aligned columns), a larger tile in two vector
+// passes (8-aligned columns), or a tile element by element.
+enum Body : int { kBodyVec = 0, kBodyScalar = 1, kBodyRegTile = 2, kBodyLoopVec = 3 };
 constexpr int64_t kRegTile = 16384;
 static_assert(sizeof(Desc) == 64, "descriptor layout is part of the workspace format");
 
@@ -334,8 +335,12 @@ __device__ __forceinline__ void reg_tile(const Desc& d, int32_t bm, int32_t bn, 
   if (t == 0) ((FP8BQ_GLOBAL float*)d.s)[(size_t)ti * d.TN + tj] = s;
 }
 
-// Element-wise tile body: any block size, any alignment.  Pass 1 takes the
-// maximum, pass 2 re-reads the tile and writes one byte per element.
+// Tile body for any block size and alignment: pass 1 takes the maximum,
+// pass 2 re-reads the tile (mostly from cache) and writes it.  When the
+// tile's columns are 8-aligned and the tensor is aligned (body kBodyLoopVec)
+// both passes use 16-byte loads over vector v = (row v / (cols/8), 8-column
+// group v % (cols/8)); otherwise they go element by element.
+template <bool VEC>
 __device__ __forceinline__ void general_tile(const Desc& d, int32_t bm, int32_t bn, int64_t ti,
                                              int64_t tj, uint32_t* red) {
   const int t = threadIdx.x;
@@ -345,11 +350,22 @@ __device__ __forceinline__ void general_tile(const Desc& d, int32_t bm, int32_t 
   const int64_t cols = (d.N - c0) < bn ? (d.N - c0) : bn;
   const int64_t n = rows * cols;
   const FP8BQ_GLOBAL uint16_t* x = (const FP8BQ_GLOBAL uint16_t*)(d.x + (size_t)r0 * d.N + c0);
+  FP8BQ_GLOBAL uint8_t* q = (FP8BQ_GLOBAL uint8_t*)(d.q + (size_t)r0 * d.N + c0);
+  const int64_t vpr = cols / 8;
+  const int64_t nvec = rows * vpr;
   uint32_t m = 0;
-  for (int64_t e = t; e < n; e += kThreads) {
-    const int64_t rr = e / cols;
-    const int64_t cc = e - rr * cols;
-    m = max(m, (uint32_t)(x[(size_t)rr * d.N + cc] & 0x7FFFu));
+  if (VEC) {
+    for (int64_t v = t; v < nvec; v += kThreads) {
+      const int64_t rr = v / vpr;
+      const u32x4 w = *(const FP8BQ_GLOBAL u32x4*)(x + (size_t)rr * d.N + (v - rr * vpr) * 8);
+      m = max(m, halves_max(fold_abs(w)));
+    }
+  } else {
+    for (int64_t e = t; e < n; e += kThreads) {
+      const int64_t rr = e / cols;
+      const int64_t cc = e - rr * cols;
+      m = max(m, (uint32_t)(x[(size_t)rr * d.N + cc] & 0x7FFFu));
+    }
   }
   m = max16(m);
   const uint32_t wm = rows_max<0>(m);
@@ -359,13 +375,21 @@ __device__ __forceinline__ void general_tile(const Desc& d, int32_t bm, int32_t 
   float s, r;
   tile_scale(tm, s, r);
   if (t == 0) ((FP8BQ_GLOBAL float*)d.s)[(size_t)ti * d.TN + tj] = s;
-  FP8BQ_GLOBAL uint8_t* q = (FP8BQ_GLOBAL uint8_t*)(d.q + (size_t)r0 * d.N + c0);
-  for (int64_t e = t; e < n; e += kThreads) {
-    const int64_t rr = e / cols;
-    const int64_t cc = e - rr * cols;
-    const size_t off = (size_t)rr * d.N + cc;
-    const float y = clamp448(__uint_as_float((uint32_t)x[off] << 16) * r);
-    q[off] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xFF);
+  if (VEC) {
+    for (int64_t v = t; v < nvec; v += kThreads) {
+      const int64_t rr = v / vpr;
+      const size_t off = (size_t)rr * d.N + (v - rr * vpr) * 8;
+      const u32x4 w = *(const FP8BQ_GLOBAL u32x4*)(x + off);
+      __builtin_nontemporal_store(quant8(w, r), (FP8BQ_GLOBAL u32x2*)(q + off));
+    }
+  } else {
+    for (int64_t e = t; e < n; e += kThreads) {
+      const int64_t rr = e / cols;
+      const int64_t cc = e - rr * cols;
+      const size_t off = (size_t)rr * d.N + cc;
+      const float y = clamp448(__uint_as_float((uint32_t)x[off] << 16) * r);
+      q[off] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xFF);
+    }
   }
 }
 
@@ -381,8 +405,12 @@ __device__ __forceinline__ void run_unit(const Desc& d, int32_t bm, int32_t bn, 
     reg_tile(d, bm, bn, ur, uc, red);
     return;
   }
+  if (d.body == kBodyLoopVec) {
+    general_tile<true>(d, bm, bn, ur, uc, red);
+    return;
+  }
   if (KIND == kGeneral || d.body == kBodyScalar) {
-    general_tile(d, bm, bn, ur, uc, red);
+    general_tile<false>(d, bm, bn, ur, uc, red);
     return;
   }
   if constexpr (KIND != kGeneral) {

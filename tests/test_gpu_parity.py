@@ -98,10 +98,12 @@ def test_general_path_odd_and_misaligned(gpu_lib, block):
             assert_matches_oracle(x, q, s, bm, bn, f"{M}x{N}/{block}/off{off}")
 
 
-@pytest.mark.parametrize("block", [(1, 4096), (16, 1024), (128, 64), (8, 8), (1, 16384), (32, 512)])
-def test_register_tile_body(gpu_lib, block):
-    """Blocks of at most 16384 elements with 8-aligned columns take the
-    register-resident tile body; ragged edges included."""
+@pytest.mark.parametrize("block", [(1, 4096), (16, 1024), (128, 64), (8, 8), (1, 16384), (32, 512),
+                                   (256, 256), (64, 512), (200, 200)])
+def test_register_and_loop_tile_bodies(gpu_lib, block):
+    """Blocks with 8-aligned columns: up to 16384 elements take the
+    register-resident tile body, up to 65536 the two-pass vector body;
+    ragged edges included."""
     bm, bn = block
     g = torch.Generator(device=DEV).manual_seed(17)
     for M, N in ((77, 128), (1000, 3000), (4097, 1008), (33, 16392)):
