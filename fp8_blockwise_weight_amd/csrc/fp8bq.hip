@@ -32,14 +32,19 @@ constexpr int64_t kMaxUnits = INT32_MAX;  // work units per tensor (32-bit unit 
 // Kernels whose work exceeds the grid cover it in grid-sized rounds.
 constexpr int64_t kMaxGrid = static_cast<int64_t>(UINT32_MAX) / fp8bq::kThreads;
 
-// Dynamic LDS reserved (and left unused) by every vectorized quantize launch
-// so that at most 4 workgroups share a CU (160 KB of LDS per gfx950 CU).
-// With fewer 32 KB tiles in flight per CU the HBM stream runs faster:
-// measured on MI355X, the dense 36-layer set goes from 76.0% to 77.1% of
-// peak and per-layer MoE launches from 73.6% to 76.5% (8 -> 4 per CU).
-constexpr unsigned kVecLds = 36 * 1024;
+// Dynamic LDS reserved (and left unused) by the vectorized quantize launches
+// to cap how many workgroups share a CU (160 KB of LDS per gfx950 CU), i.e.
+// how many bytes are in flight per CU.  Measured on MI355X:
+//   [128,128], 32 KB per unit: 4 per CU is best (dense 36-layer set 76.0% ->
+//     77.1% of peak; per-layer MoE launches 73.6% -> 76.5%);
+//   [64,64] and [1,128], 16 KB per unit: 6 per CU is best (151937x4096:
+//     [64,64] 75% at 4 per CU -> 79.6%, [1,128] 74% -> 77.5%).
+constexpr unsigned kLds4PerCu = 36 * 1024;  // 160 KB / 36 KB -> 4 workgroups
+constexpr unsigned kLds6PerCu = 26 * 1024;  // 160 KB / 26 KB -> 6 workgroups
 
-constexpr unsigned lds_for(int kind) { return kind == fp8bq::kGeneral ? 0u : kVecLds; }
+constexpr unsigned lds_for(int kind) {
+  return kind == fp8bq::kGeneral ? 0u : (kind == fp8bq::kT128 ? kLds4PerCu : kLds6PerCu);
+}
 
 // Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
 std::atomic<int> g_arch_state[kMaxDevices];

@@ -401,15 +401,19 @@ __device__ __forceinline__ void run_unit(const Desc& d, int32_t bm, int32_t bn, 
   const uint32_t un = (uint32_t)d.UN;
   const uint32_t ur = uu / un;
   const uint32_t uc = uu - ur * un;
-  if (d.body == kBodyRegTile) {
-    reg_tile(d, bm, bn, ur, uc, red);
+  if constexpr (KIND == kGeneral) {
+    // Register and loop-vector bodies need aligned tensors, which launches of
+    // a vector kind always give the vector body: compile them here only.
+    if (d.body == kBodyRegTile) {
+      reg_tile(d, bm, bn, ur, uc, red);
+    } else if (d.body == kBodyLoopVec) {
+      general_tile<true>(d, bm, bn, ur, uc, red);
+    } else {
+      general_tile<false>(d, bm, bn, ur, uc, red);
+    }
     return;
   }
-  if (d.body == kBodyLoopVec) {
-    general_tile<true>(d, bm, bn, ur, uc, red);
-    return;
-  }
-  if (KIND == kGeneral || d.body == kBodyScalar) {
+  if (d.body != kBodyVec) {
     general_tile<false>(d, bm, bn, ur, uc, red);
     return;
   }
@@ -444,12 +448,14 @@ __device__ __forceinline__ int64_t xcd_unit(int64_t wg, int64_t n) {
 // Calls f(u) for the units this workgroup owns: units are handed out in
 // rounds of gridDim.x (a dispatch holds at most 2^32 - 1 work-items, i.e.
 // 16,777,215 workgroups of 256), XCD-aware within each round.  Barriers in f
-// are safe: every thread of a workgroup runs the same rounds.
+// are safe: every thread of a workgroup runs the same rounds; a barrier
+// between rounds lets f reuse its LDS scratch.
 template <typename F>
 __device__ __forceinline__ void for_each_unit(int64_t total, F&& f) {
   for (int64_t b0 = 0; b0 < total; b0 += gridDim.x) {
     const int64_t n = (total - b0) < (int64_t)gridDim.x ? (total - b0) : (int64_t)gridDim.x;
     if ((int64_t)blockIdx.x >= n) return;
+    if (b0 > 0) __syncthreads();  // LDS scratch of the previous round is reused
     f(b0 + xcd_unit(blockIdx.x, n));
   }
 }
@@ -462,7 +468,6 @@ __global__ __launch_bounds__(kThreads) void quantize_one(Desc d, int32_t bm, int
   __shared__ uint32_t red[8];
   for_each_unit(total, [&](int64_t u) {
     run_unit<KIND>(d, bm, bn, u, red);
-    __syncthreads();  // red[] is reused by the next round
   });
 }
 
@@ -486,7 +491,6 @@ __global__ __launch_bounds__(kThreads) void quantize_group(const Desc* __restric
     }
     const Desc d = descs[lo];
     run_unit<KIND>(d, bm, bn, u - start[lo], red);
-    __syncthreads();  // red[] is reused by the next round
   });
 }
 
@@ -937,7 +941,6 @@ __global__ __launch_bounds__(kThreads) void quantize_group_args(const GroupArgs<
     d.pad = 0;
     d.reserved = 0;
     run_unit<KIND>(d, bm, bn, u - a.start[lo], red);
-    __syncthreads();  // red[] is reused by the next round
   });
 }
 
