@@ -168,8 +168,49 @@ def test_anchor_sweep_every_bf16(gpu_lib):
         rows = (bits.shape[0] // 128) * 128
         if rows:
             xt = x[:rows].contiguous()
-            q, s = fq.quantize(xt, (128, 128))
-            assert_matches_oracle(xt, q, s, 128, 128, f"anchor tiles {i}")
+            for block in [(128, 128), (64, 64), (32, 128), (7, 64)]:
+                q, s = fq.quantize(xt, block)
+                assert_matches_oracle(xt, q, s, *block, f"anchor tiles {i} {block}")
+
+
+def _double_rounding_rows(min_rows=256):
+    """[1,128] rows: an anchor maximum in column 0 and BF16 values whose
+    scaled product x*r rounds (in float32) exactly onto an e4m3 midpoint
+    without being on it, so the float32 rounding decides the code."""
+    rng = np.random.default_rng(67)
+    pos = np.array([float(v) for v in oracle.e4m3fn.decode_np(np.arange(127, dtype=np.uint8))])
+    mids = (pos[:-1] + pos[1:]) / 2
+    rows = []
+    while len(rows) < min_rows:
+        ab = int(rng.integers(0x2000, 0x6000))
+        a = float(oracle.bf16_bits_to_f64([ab])[0])
+        _, r = oracle.tile_scale(a)
+        xb = np.arange(1, ab, dtype=np.uint16)
+        p = oracle.bf16_bits_to_f64(xb) * r
+        y = p.astype(np.float32).astype(np.float64)
+        hit = xb[np.isin(y, mids) & (p != y)]
+        for i in range(0, hit.size, 63):
+            h = hit[i:i + 63]
+            row = np.zeros(128, dtype=np.uint16)
+            row[0] = ab
+            row[1:1 + h.size] = h
+            row[64:64 + h.size] = h | 0x8000
+            rows.append(row)
+    return np.stack(rows)
+
+
+def test_double_rounding_cases_all_kinds(gpu_lib):
+    """Inputs where the float32 rounding of x*r decides the e4m3 code, through
+    every kernel body: [1,128] rows, [128,128] and [64,64] tiles (re-tiled),
+    the register tile body and the element-wise body."""
+    bits = _double_rounding_rows()
+    rows = (bits.shape[0] // 128) * 128
+    assert rows >= 128, "the search found too few cases"
+    x = bf16_from_bits(bits[:rows])
+    say("double rounding rows", rows)
+    for block in [(1, 128), (128, 128), (64, 64), (16, 128), (3, 5)]:
+        q, s = fq.quantize(x, block)
+        assert_matches_oracle(x, q, s, *block, f"double rounding {block}")
 
 
 def test_encoder_exhaustive_fp32(gpu_lib):
