@@ -296,6 +296,42 @@ def test_determinism_and_canaries(gpu_lib):
         assert torch.equal(results[0][1].view(torch.int32), results[1][1].view(torch.int32))
 
 
+def test_non_finite_input_stays_in_bounds(gpu_lib):
+    """NaN and Inf are outside the contract: their tiles' outputs are
+    unspecified, but every write stays inside q and scale_inv and finite
+    tiles are unaffected."""
+    G = 256
+    g = torch.Generator(device=DEV).manual_seed(71)
+    for M, N, block in ((300, 520, (128, 128)), (300, 520, (64, 64)), (300, 520, (1, 128)),
+                        (300, 520, (16, 64)), (301, 519, (128, 128)), (300, 520, (300, 520))):
+        x = (torch.randn((M, N), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+        x[5, 7] = float("nan")
+        x[200, 300] = float("inf")
+        x[250, 10] = float("-inf")
+        TM, TN = fq.scale_shape(M, N, *block)
+        qb = torch.full((M * N + 2 * G,), 0xA5, dtype=torch.uint8, device=DEV)
+        sb = torch.full((TM * TN + 2 * G,), -7.5, dtype=torch.float32, device=DEV)
+        q, s = qb[G:G + M * N].view(M, N), sb[G:G + TM * TN].view(TM, TN)
+        fq.quantize(x, block, out=(q, s))
+        torch.cuda.synchronize()
+        assert bool((qb[:G] == 0xA5).all()) and bool((qb[G + M * N:] == 0xA5).all()), block
+        assert bool((sb[:G] == -7.5).all()) and bool((sb[G + TM * TN:] == -7.5).all()), block
+        # tiles without a non-finite value match a finite copy quantized alone
+        xf = torch.nan_to_num(x.float(), nan=0.0, posinf=0.0, neginf=0.0).to(torch.bfloat16)
+        q2, s2 = fq.quantize(xf, block)
+        bad_rows = {5 // block[0], 200 // block[0], 250 // block[0]}
+        bad = {(5 // block[0], 7 // block[1]), (200 // block[0], 300 // block[1]),
+               (250 // block[0], 10 // block[1])}
+        for ti in range(TM):
+            for tj in range(TN):
+                if (ti, tj) in bad:
+                    continue
+                r0, c0 = ti * block[0], tj * block[1]
+                assert torch.equal(q[r0:r0 + block[0], c0:c0 + block[1]],
+                                   q2.view(torch.uint8)[r0:r0 + block[0], c0:c0 + block[1]]), (block, ti, tj)
+        assert bad_rows
+
+
 def test_grouped_mixed_list(gpu_lib):
     """One grouped launch over empty, odd-N, misaligned and aligned tensors
     equals single calls and the oracle, for every block kind."""
