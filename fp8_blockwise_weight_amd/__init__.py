@@ -304,6 +304,8 @@ def tile_amax(x, block_size=(128, 128), phase=(0, 0), out=None):
     shape = local_grid(M, N, bm, bn, phase)
     if out is not None:
         _check_buffer(out, shape, 4, x.device, "amax")
+        if out.dtype != torch.float32:
+            raise TypeError("amax must be float32")
     amax = out if out is not None else torch.empty(shape, dtype=torch.float32, device=x.device)
     with torch.cuda.device(x.device):
         _check("fp8bq_tile_amax",
@@ -333,6 +335,8 @@ def quantize_with_amax(x, amax, block_size=(128, 128), phase=(0, 0), out=None):
         q, s = out
         _check_buffer(q, (M, N), 1, x.device, "q")
         _check_buffer(s, shape, 4, x.device, "scale_inv")
+        if s.dtype != torch.float32:
+            raise TypeError("scale_inv must be float32")
     with torch.cuda.device(x.device):
         _check("fp8bq_quantize_amax",
                load_library().fp8bq_quantize_amax(x.data_ptr(), M, N, bm, bn, phase[0], phase[1],

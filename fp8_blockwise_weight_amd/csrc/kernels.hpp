@@ -17,8 +17,14 @@
 //     maximum is reduced inside one 16-lane DPP row, with no LDS and no
 //     barrier, and each lane divides for one row-tile only (DPP quad
 //     broadcast of the reciprocals);
-//   * any other block size, N % 8 != 0 or a misaligned pointer: one tile per
-//     unit, element by element (two passes over the tile), same arithmetic.
+//   * any other block size (one tile per unit): up to 16384 elements with
+//     8-aligned columns, the whole tile in registers; up to 65536, two
+//     16-byte passes over the tile; N % 8 != 0 or a misaligned pointer,
+//     element by element;
+//   * tiles of more than 65536 elements (e.g. one scale per tensor) and
+//     shards that start inside a tile: two passes over chunks, with the
+//     per-tile maxima folded by atomic max (section "large tiles").
+// Every body computes the same arithmetic, so results never depend on it.
 //
 // The tile maximum is an integer max over (bits & 0x7FFF): for finite BF16
 // values magnitude order equals bit-pattern order, so this is exact.
@@ -139,20 +145,17 @@ __device__ __forceinline__ float quad_bcast(float v) {
       __builtin_amdgcn_mov_dpp(__float_as_int(v), K | (K << 2) | (K << 4) | (K << 6), 0xF, 0xF, false));
 }
 
-// Scale and reciprocal from the tile's maximum magnitude bits: two correctly
-// rounded binary32 divisions (this file is built without fast-math).
-__device__ __forceinline__ void tile_scale(uint32_t maxbits, float& s, float& r) {
-  const float amax = __uint_as_float(maxbits << 16);
+// Scale and reciprocal from a tile's maximum magnitude: two correctly rounded
+// binary32 divisions (this file is built without fast-math).
+__device__ __forceinline__ void tile_scale_f(float amax, float& s, float& r) {
   const float a = fmaxf(amax, kEps);
   s = a / kE4m3Max;
   r = 1.0f / s;
 }
 
-// Same from a maximum given as a float (for maxima combined outside a tile).
-__device__ __forceinline__ void tile_scale_f(float amax, float& s, float& r) {
-  const float a = fmaxf(amax, kEps);
-  s = a / kE4m3Max;
-  r = 1.0f / s;
+// Same from the maximum's BF16 magnitude bits (widened exactly to fp32).
+__device__ __forceinline__ void tile_scale(uint32_t maxbits, float& s, float& r) {
+  tile_scale_f(__uint_as_float(maxbits << 16), s, r);
 }
 
 __device__ __forceinline__ float clamp448(float y) {
@@ -411,13 +414,9 @@ __device__ __forceinline__ void run_unit(const Desc& d, int32_t bm, int32_t bn, 
     } else {
       general_tile<false>(d, bm, bn, ur, uc, red);
     }
-    return;
-  }
-  if (d.body != kBodyVec) {
+  } else if (d.body != kBodyVec) {
     general_tile<false>(d, bm, bn, ur, uc, red);
-    return;
-  }
-  if constexpr (KIND != kGeneral) {
+  } else {
     constexpr int R = UnitShape<KIND>::kRows;
     const bool inside = (int64_t)(ur + 1) * R <= d.M && (int64_t)(uc + 1) * 128 <= d.N;
     if (inside) {
@@ -701,9 +700,9 @@ struct BigGroupArgs {
   BigEntry e[CAP];
 };
 
-template <int CAP>
+// Largest t with start[t] <= u (start is non-decreasing, start[0] = 0 <= u).
 __device__ __forceinline__ int big_find(const int32_t* start, int count, int64_t u) {
-  int lo = 0, hi = count - 1;  // largest t with start[t] <= u
+  int lo = 0, hi = count - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (start[mid] <= u) {
@@ -740,7 +739,7 @@ __global__ __launch_bounds__(kThreads) void big_group_tiles(const BigGroupArgs<C
                                                             int32_t total) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (i >= total) return;
-  const int t = big_find<CAP>(a.tile_start, count, i);
+  const int t = big_find(a.tile_start, count, i);
   FP8BQ_GLOBAL float* sp = (FP8BQ_GLOBAL float*)a.e[t].s + (i - a.tile_start[t]);
   if (PHASE == 0) {
     *(FP8BQ_GLOBAL uint32_t*)sp = 0u;
@@ -756,7 +755,7 @@ __global__ __launch_bounds__(kThreads) void big_group_max(const BigGroupArgs<CAP
                                                           int32_t bm, int32_t bn) {
   __shared__ uint32_t red[4];
   for_each_unit(a.max_start[count], [&](int64_t u) {
-    const int t = big_find<CAP>(a.max_start, count, u);
+    const int t = big_find(a.max_start, count, u);
     const Big b = big_of(a.e[t], bm, bn);
     big_max_item(b, (uint32_t*)a.e[t].s, u - a.max_start[t], red);
   });
@@ -766,7 +765,7 @@ template <int CAP>
 __global__ __launch_bounds__(kThreads) void big_group_quant(const BigGroupArgs<CAP> a, int32_t count,
                                                             int32_t bm, int32_t bn) {
   for_each_unit(a.quant_start[count], [&](int64_t u) {
-    const int t = big_find<CAP>(a.quant_start, count, u);
+    const int t = big_find(a.quant_start, count, u);
     const Big b = big_of(a.e[t], bm, bn);
     big_quant_item(b, a.e[t].s, u - a.quant_start[t]);
   });
@@ -802,8 +801,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 enum OutType : int { kOutF32 = 0, kOutBF16 = 1 };
 
-// Round a finite fp32 value to BF16 bits, nearest with ties to even: add
-// half an ulp of the 16 dropped bits (minus one when the kept LSB is 0).
+// Round a finite fp32 value to BF16 bits, nearest with ties to even: adding
+// 0x7FFF plus the kept LSB to the 16 dropped bits carries into the kept part
+// exactly when they are above half, or exactly half with an odd kept LSB.
 __device__ __forceinline__ uint32_t bf16_rne(float y) {
   const uint32_t b = __float_as_uint(y);
   return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
@@ -835,34 +835,34 @@ __global__ __launch_bounds__(kThreads) void dequant_vec(const uint8_t* __restric
   const int64_t per_block = (int64_t)kThreads * kDqUnroll;
   for (int64_t b0 = (int64_t)blockIdx.x * per_block; b0 < groups;
        b0 += (int64_t)gridDim.x * per_block) {
-  const int64_t g0 = b0 + threadIdx.x;
-  QWord w[kDqUnroll];
-  float sc[kDqUnroll];
+    const int64_t g0 = b0 + threadIdx.x;
+    QWord w[kDqUnroll];
+    float sc[kDqUnroll];
 #pragma unroll
-  for (int k = 0; k < kDqUnroll; ++k) {
-    const int64_t g = g0 + (int64_t)k * kThreads;
-    if (g < groups) {
-      const int64_t row = g / gpr;
-      const int64_t col = (g - row * gpr) * G;
-      w[k] = __builtin_nontemporal_load((const FP8BQ_GLOBAL QWord*)(q) + g);
-      sc[k] = ((const FP8BQ_GLOBAL float*)s)[(row / bm) * TN + col / bn];
+    for (int k = 0; k < kDqUnroll; ++k) {
+      const int64_t g = g0 + (int64_t)k * kThreads;
+      if (g < groups) {
+        const int64_t row = g / gpr;
+        const int64_t col = (g - row * gpr) * G;
+        w[k] = __builtin_nontemporal_load((const FP8BQ_GLOBAL QWord*)(q) + g);
+        sc[k] = ((const FP8BQ_GLOBAL float*)s)[(row / bm) * TN + col / bn];
+      }
     }
-  }
 #pragma unroll
-  for (int k = 0; k < kDqUnroll; ++k) {
-    const int64_t g = g0 + (int64_t)k * kThreads;
-    if (g >= groups) continue;
-    if constexpr (OUT == kOutF32) {
-      const f32x4 a = dq4(w[k], sc[k]);
-      __builtin_nontemporal_store(a, (FP8BQ_GLOBAL f32x4*)out + g);
-    } else {
-      const f32x4 a = dq4(w[k].x, sc[k]);
-      const f32x4 b = dq4(w[k].y, sc[k]);
-      const u32x4 p{bf16_rne(a.x) | (bf16_rne(a.y) << 16), bf16_rne(a.z) | (bf16_rne(a.w) << 16),
-                    bf16_rne(b.x) | (bf16_rne(b.y) << 16), bf16_rne(b.z) | (bf16_rne(b.w) << 16)};
-      __builtin_nontemporal_store(p, (FP8BQ_GLOBAL u32x4*)out + g);
+    for (int k = 0; k < kDqUnroll; ++k) {
+      const int64_t g = g0 + (int64_t)k * kThreads;
+      if (g >= groups) continue;
+      if constexpr (OUT == kOutF32) {
+        const f32x4 a = dq4(w[k], sc[k]);
+        __builtin_nontemporal_store(a, (FP8BQ_GLOBAL f32x4*)out + g);
+      } else {
+        const f32x4 a = dq4(w[k].x, sc[k]);
+        const f32x4 b = dq4(w[k].y, sc[k]);
+        const u32x4 p{bf16_rne(a.x) | (bf16_rne(a.y) << 16), bf16_rne(a.z) | (bf16_rne(a.w) << 16),
+                      bf16_rne(b.x) | (bf16_rne(b.y) << 16), bf16_rne(b.z) | (bf16_rne(b.w) << 16)};
+        __builtin_nontemporal_store(p, (FP8BQ_GLOBAL u32x4*)out + g);
+      }
     }
-  }
   }
 }
 
