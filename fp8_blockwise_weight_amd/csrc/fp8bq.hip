@@ -186,38 +186,76 @@ fp8bq::Big make_big(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn,
     b.cpt = ceil_div(rows_max, rows_per);
   }
   b.items = b.TMl * b.TNl * b.cpt;
+  // Chunks per pass-1 item: enough items to fill the chip, but no more than
+  // kChunksPerMax chunks per item (fewer atomics on one address).
+  const int64_t per = b.items / fp8bq::kMaxItemsTarget;
+  b.cpm = static_cast<int32_t>(per < 1 ? 1 : (per > fp8bq::kChunksPerMax ? fp8bq::kChunksPerMax : per));
+  b.pad = 0;
   return b;
 }
+
+// Pass-1 items of a large-tile sub-matrix.
+int64_t big_max_items(const fp8bq::Big& b) { return b.TMl * b.TNl * ceil_div(b.cpt, b.cpm); }
 
 unsigned grid_capped(int64_t n, int64_t per_block) {
   const int64_t blocks = (n + per_block - 1) / per_block;
   return static_cast<unsigned>(blocks < 65536 * 16 ? (blocks < 1 ? 1 : blocks) : 65536 * 16);
 }
 
-// Pass 1 (maxima into `amax`, zeroed first), optional pass 2 and scales.
-// `amax` may be `scale_inv` itself (it then serves as the scratch).
+// Shards: pass 1 with atomic maxima into `amax` (zeroed first).
 void launch_big_amax(const fp8bq::Big& b, float* amax, hipStream_t st) {
   const int64_t nt = b.TMl * b.TNl;
   hipLaunchKernelGGL(fp8bq::fill_zero, dim3(grid_capped(nt, fp8bq::kThreads)), dim3(fp8bq::kThreads),
                      0, st, reinterpret_cast<uint32_t*>(amax), nt);
-  const int64_t items = b.TMl * b.TNl * ceil_div(b.cpt, fp8bq::kChunksPerMax);
-  hipLaunchKernelGGL(fp8bq::big_max, dim3(grid_for(items)), dim3(fp8bq::kThreads), 0, st, b,
+  const int64_t items = big_max_items(b);
+  hipLaunchKernelGGL(fp8bq::big_max<false>, dim3(grid_for(items)), dim3(fp8bq::kThreads), 0, st, b,
                      reinterpret_cast<uint32_t*>(amax), items);
 }
 
+// Shards: pass 2 with given maxima, then the scales.  `amax` may be
+// `scale_inv` itself (converted in place after pass 2 has read it).
 void launch_big_quant(const fp8bq::Big& b, const float* amax, float* scale_inv, hipStream_t st) {
   const int64_t nt = b.TMl * b.TNl;
-  hipLaunchKernelGGL(fp8bq::big_quant, dim3(grid_for(b.items)), dim3(fp8bq::kThreads), 0, st, b,
-                     amax);
+  hipLaunchKernelGGL(fp8bq::big_quant<false>, dim3(grid_for(b.items)), dim3(fp8bq::kThreads), 0, st,
+                     b, amax);
   hipLaunchKernelGGL(fp8bq::finalize_scales, dim3(grid_capped(nt, fp8bq::kThreads)),
                      dim3(fp8bq::kThreads), 0, st, amax, scale_inv, nt);
 }
 
+// A whole tensor's pass-1 slots fit in its q buffer (from the first
+// 4-byte-aligned byte).  Always true for tiles of more than kBigTile
+// elements, since a slot covers at least one chunk; checked anyway.
+bool big_slots_fit(const fp8bq::Big& b) {
+  const uint64_t pad = (4 - (reinterpret_cast<uintptr_t>(b.q) & 3)) & 3;
+  const uint64_t need = 4 * static_cast<uint64_t>(big_max_items(b)) + pad;
+  return need <= static_cast<uint64_t>(b.M) * static_cast<uint64_t>(b.N);
+}
+
+// A whole tensor with large tiles: slots in q, tile scales, then pass 2.
+void launch_big_tensor(const fp8bq::Big& b, float* scale_inv, hipStream_t st) {
+  if (!big_slots_fit(b)) {
+    // scale_inv doubles as the scratch for the per-tile maxima.
+    launch_big_amax(b, scale_inv, st);
+    launch_big_quant(b, scale_inv, scale_inv, st);
+    return;
+  }
+  uint32_t* slots = fp8bq::big_slots(b.q);
+  const int64_t items = big_max_items(b);
+  const int64_t nt = b.TMl * b.TNl;
+  hipLaunchKernelGGL(fp8bq::big_max<true>, dim3(grid_for(items)), dim3(fp8bq::kThreads), 0, st, b,
+                     slots, items);
+  hipLaunchKernelGGL(fp8bq::big_reduce, dim3(grid_for(nt)), dim3(fp8bq::kThreads), 0, st,
+                     static_cast<const uint32_t*>(slots), ceil_div(b.cpt, b.cpm), scale_inv, nt);
+  hipLaunchKernelGGL(fp8bq::big_quant<true>, dim3(grid_for(b.items)), dim3(fp8bq::kThreads), 0, st,
+                     b, static_cast<const float*>(scale_inv));
+}
+
 constexpr int kBigGroupCap = 128;  // tensors per grouped large-tile launch
 
-// Whole tensors with large tiles, up to kBigGroupCap per group: 4 launches per
-// group (zero maxima, maxima, quantize, scales).  Returns false if the
-// group's item counts do not fit 32 bits (the caller then goes per tensor).
+// Whole tensors with large tiles, up to kBigGroupCap per group: 3 launches per
+// group (slot maxima, tile scales, quantize).  Returns false if the group's
+// counts do not fit 32 bits or a tensor's slots do not fit its q (the caller
+// then goes per tensor).
 bool launch_big_group(const fp8bq_tensor* const* ts, int32_t n, int32_t bm, int32_t bn,
                       hipStream_t st) {
   fp8bq::BigGroupArgs<kBigGroupCap> a;
@@ -226,6 +264,7 @@ bool launch_big_group(const fp8bq_tensor* const* ts, int32_t n, int32_t bm, int3
   for (int32_t i = 0; i < n; ++i) {
     const fp8bq_tensor& t = *ts[i];
     const fp8bq::Big b = make_big(t.x, t.M, t.N, bm, bn, 0, 0, t.q);
+    if (!big_slots_fit(b)) return false;
     a.tile_start[i] = static_cast<int32_t>(tiles);
     a.max_start[i] = static_cast<int32_t>(maxi);
     a.quant_start[i] = static_cast<int32_t>(quanti);
@@ -236,8 +275,9 @@ bool launch_big_group(const fp8bq_tensor* const* ts, int32_t n, int32_t bm, int3
     a.e[i].N = static_cast<int32_t>(t.N);
     a.e[i].cpt = static_cast<int32_t>(b.cpt);
     a.e[i].flags = b.flat | (b.vec << 1);
+    a.e[i].cpm = b.cpm;
     tiles += b.TMl * b.TNl;
-    maxi += b.TMl * b.TNl * ceil_div(b.cpt, fp8bq::kChunksPerMax);
+    maxi += big_max_items(b);
     quanti += b.items;
     if (tiles > INT32_MAX || maxi > INT32_MAX || quanti > INT32_MAX || b.cpt > INT32_MAX) {
       return false;
@@ -247,15 +287,12 @@ bool launch_big_group(const fp8bq_tensor* const* ts, int32_t n, int32_t bm, int3
   a.max_start[n] = static_cast<int32_t>(maxi);
   a.quant_start[n] = static_cast<int32_t>(quanti);
   const dim3 blk(fp8bq::kThreads);
-  const dim3 gt(static_cast<unsigned>(ceil_div(tiles, fp8bq::kThreads)));
-  hipLaunchKernelGGL((fp8bq::big_group_tiles<kBigGroupCap, 0>), gt, blk, 0, st, a, n,
-                     static_cast<int32_t>(tiles));
   hipLaunchKernelGGL((fp8bq::big_group_max<kBigGroupCap>), dim3(grid_for(maxi)), blk, 0, st, a, n,
                      bm, bn);
+  hipLaunchKernelGGL((fp8bq::big_group_reduce<kBigGroupCap>), dim3(grid_for(tiles)), blk, 0, st, a,
+                     n);
   hipLaunchKernelGGL((fp8bq::big_group_quant<kBigGroupCap>), dim3(grid_for(quanti)), blk, 0, st, a,
                      n, bm, bn);
-  hipLaunchKernelGGL((fp8bq::big_group_tiles<kBigGroupCap, 1>), gt, blk, 0, st, a, n,
-                     static_cast<int32_t>(tiles));
   return true;
 }
 
@@ -321,10 +358,7 @@ int fp8bq_quantize(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (big_tiles(M, N, bm, bn)) {
-    // scale_inv doubles as the scratch for the per-tile maxima.
-    const fp8bq::Big b = make_big(x, M, N, bm, bn, 0, 0, q);
-    launch_big_amax(b, scale_inv, s);
-    launch_big_quant(b, scale_inv, scale_inv, s);
+    launch_big_tensor(make_big(x, M, N, bm, bn, 0, 0, q), scale_inv, s);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
   }
@@ -387,10 +421,8 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
     auto flush = [&]() {
       if (group.empty()) return;
       if (!launch_big_group(group.data(), static_cast<int32_t>(group.size()), bm, bn, s)) {
-        for (const fp8bq_tensor* t : group) {  // item counts beyond 32 bits: per tensor
-          const fp8bq::Big b = make_big(t->x, t->M, t->N, bm, bn, 0, 0, t->q);
-          launch_big_amax(b, t->scale_inv, s);
-          launch_big_quant(b, t->scale_inv, t->scale_inv, s);
+        for (const fp8bq_tensor* t : group) {  // counts beyond 32 bits: per tensor
+          launch_big_tensor(make_big(t->x, t->M, t->N, bm, bn, 0, 0, t->q), t->scale_inv, s);
         }
       }
       group.clear();

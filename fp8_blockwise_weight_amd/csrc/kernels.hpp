@@ -497,11 +497,16 @@ __global__ __launch_bounds__(kThreads) void quantize_group(const Desc* __restric
 //
 // Tiles too large for one workgroup (per-tensor scales, [1, N] rows of
 // huge N, any tile above kBigTile elements) and sub-matrices that start
-// inside a tile (shards) take two passes: pass 1 reduces chunks of each tile
-// and folds them into a per-tile maximum with an atomic max; pass 2
-// quantizes the chunks with the finished maxima; a last tiny kernel turns
-// maxima into scales.  The sub-matrix's element (0,0) sits at
-// (row_phase, col_phase) inside a tile of the full matrix's grid.
+// inside a tile (shards) take two passes over chunks of each tile.
+//   Whole tensors: pass 1 stores one partial maximum per workgroup in its own
+//   slot, kept in the q buffer that pass 2 overwrites later; a small kernel
+//   reduces each tile's slots to its scale in scale_inv; pass 2 quantizes
+//   with r = 1/s.  No atomics, three launches.
+//   Shards (a sub-matrix whose element (0,0) sits at (row_phase, col_phase)
+//   inside a tile of the full matrix's grid): pass 1 folds partial maxima
+//   into the per-tile maxima with an atomic max (the caller combines shards'
+//   maxima); pass 2 quantizes with given maxima and a last tiny kernel turns
+//   maxima into scales.
 
 constexpr int64_t kBigTile = 65536;     // elements; larger tiles take this path
 constexpr int64_t kChunk = 16384;       // elements per workgroup pass
@@ -521,6 +526,8 @@ struct Big {
   int64_t items; // TMl * TNl * cpt
   int32_t flat;  // tiles cover whole rows: a chunk is one contiguous range
   int32_t vec;   // x 16-byte aligned, q 8-byte aligned, N % 8 == 0
+  int32_t cpm;   // chunks per pass-1 item, 1..kChunksPerMax
+  int32_t pad;
 };
 
 // Rows [r0, r1) and columns [c0, c1) of local tile (ti, tj).
@@ -633,68 +640,116 @@ __device__ __forceinline__ bool big_chunk(const Big& b, int64_t tile, int64_t k,
   return true;
 }
 
-// Pass 1 of the large-tile path: partial maxima (as fp32 bit patterns of the
-// BF16 magnitudes) into amax_bits, which must start at zero.  A workgroup
-// reduces kChunksPerMax chunks of one tile before its single atomic max, and
-// skips the atomic when a coherent read shows the tile maximum is already at
-// least as large: many workgroups folding into one address (one scale per
-// tensor) would otherwise serialize on it.
-constexpr int64_t kChunksPerMax = 16;
+// Pass 1 of the large-tile path.  Item `it` reduces b.cpm chunks of one
+// tile (item it = tile * groups + g, groups = ceil(cpt / cpm)); the host
+// picks b.cpm per tensor so that small tensors still spread over the chip.
+//   SLOTS: the item's maximum magnitude bits go to out[it]: every item
+//     writes its slot (0 for chunks past a short tile's end).
+//   atomic: the maximum, as the fp32 bit pattern of the BF16 magnitude, is
+//     folded into out[tile] (which must start at zero) with an atomic max,
+//     skipped when a coherent read already shows a value at least as large.
+//     Many workgroups folding into one address serialize on it, which is
+//     why whole tensors take the slots.
+constexpr int64_t kChunksPerMax = 16;     // largest b.cpm
+constexpr int64_t kMaxItemsTarget = 2048; // pass-1 items a tensor aims for (8 per CU)
 
-// Item `it` of pass 1 for one tensor: kChunksPerMax chunks of one tile.
-__device__ __forceinline__ void big_max_item(const Big& b, uint32_t* amax_bits, int64_t it,
+// Pass-1 slots of a whole tensor: the first 4-byte-aligned address of q.
+__host__ __device__ inline uint32_t* big_slots(uint8_t* q) {
+  return reinterpret_cast<uint32_t*>((reinterpret_cast<uintptr_t>(q) + 3) & ~uintptr_t(3));
+}
+
+template <bool SLOTS>
+__device__ __forceinline__ void big_max_item(const Big& b, uint32_t* out, int64_t it,
                                              uint32_t* red) {
-  const int64_t groups = (b.cpt + kChunksPerMax - 1) / kChunksPerMax;
+  const int64_t cpm = b.cpm;
+  const int64_t groups = (b.cpt + cpm - 1) / cpm;
   const int64_t tile = it / groups;
   const int64_t g = it - tile * groups;
   uint32_t m = 0;
-  for (int64_t k = g * kChunksPerMax; k < (g + 1) * kChunksPerMax && k < b.cpt; ++k) {
+  for (int64_t k = g * cpm; k < (g + 1) * cpm && k < b.cpt; ++k) {
     if (!big_chunk<0>(b, tile, k, 0.0f, m)) break;
   }
   const uint32_t wm = block_max(m, red);
-  if (threadIdx.x == 0 && wm != 0) {
-    const uint32_t cur = __hip_atomic_load(&amax_bits[tile], __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    if ((wm << 16) > cur) atomicMax(&amax_bits[tile], wm << 16);
+  if (threadIdx.x != 0) return;
+  if constexpr (SLOTS) {
+    ((FP8BQ_GLOBAL uint32_t*)out)[it] = wm;
+  } else if (wm != 0) {
+    const uint32_t cur = __hip_atomic_load(&out[tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((wm << 16) > cur) atomicMax(&out[tile], wm << 16);
   }
 }
 
-// Item `it` of pass 2 for one tensor: one chunk, quantized with its tile's maximum.
-__device__ __forceinline__ void big_quant_item(const Big& b, const float* amax, int64_t it) {
+// Scale of one tile from its `groups` pass-1 slots: s = fl32(max(amax, eps) / 448).
+__device__ __forceinline__ void big_reduce_tile(const uint32_t* slots, int64_t groups,
+                                                int64_t tile, float* scale, uint32_t* red) {
+  const FP8BQ_GLOBAL uint32_t* p = (const FP8BQ_GLOBAL uint32_t*)slots + tile * groups;
+  uint32_t m = 0;
+  for (int64_t i = threadIdx.x; i < groups; i += kThreads) m = max(m, p[i]);
+  m = block_max(m, red);
+  if (threadIdx.x == 0) {
+    float s, r;
+    tile_scale(m, s, r);
+    ((FP8BQ_GLOBAL float*)scale)[tile] = s;
+  }
+}
+
+// Item `it` of pass 2 for one tensor: one chunk, quantized with its tile's
+// scale (FROM_S: v holds s, and r = 1/s) or maximum (v holds amax, and s and
+// r follow from it).  Both give the same r for the same tile.
+template <bool FROM_S>
+__device__ __forceinline__ void big_quant_item(const Big& b, const float* v, int64_t it) {
   const int64_t tile = it / b.cpt;
   const int64_t k = it - tile * b.cpt;
+  const float vt = ((const FP8BQ_GLOBAL float*)v)[tile];
   float s, r;
-  tile_scale_f(((const FP8BQ_GLOBAL float*)amax)[tile], s, r);
+  if constexpr (FROM_S) {
+    s = vt;
+    r = 1.0f / s;
+  } else {
+    tile_scale_f(vt, s, r);
+  }
   uint32_t unused = 0;
   big_chunk<1>(b, tile, k, r, unused);
 }
 
-__global__ __launch_bounds__(kThreads) void big_max(Big b, uint32_t* __restrict__ amax_bits,
+template <bool SLOTS>
+__global__ __launch_bounds__(kThreads) void big_max(Big b, uint32_t* __restrict__ out,
                                                     int64_t items) {
   __shared__ uint32_t red[4];
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) big_max_item(b, amax_bits, it, red);
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) big_max_item<SLOTS>(b, out, it, red);
 }
 
-__global__ __launch_bounds__(kThreads) void big_quant(Big b, const float* __restrict__ amax) {
-  for (int64_t it = blockIdx.x; it < b.items; it += gridDim.x) big_quant_item(b, amax, it);
+// Tile scales of one whole tensor from its pass-1 slots.
+__global__ __launch_bounds__(kThreads) void big_reduce(const uint32_t* __restrict__ slots,
+                                                       int64_t groups, float* __restrict__ scale,
+                                                       int64_t tiles) {
+  __shared__ uint32_t red[4];
+  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) big_reduce_tile(slots, groups, t, scale, red);
+}
+
+template <bool FROM_S>
+__global__ __launch_bounds__(kThreads) void big_quant(Big b, const float* __restrict__ v) {
+  for (int64_t it = blockIdx.x; it < b.items; it += gridDim.x) big_quant_item<FROM_S>(b, v, it);
 }
 
 // Grouped form for a list of whole tensors with large tiles (phase 0): the
 // table rides in the kernel arguments and each kernel covers every tensor,
-// so a group costs 4 launches instead of 4 per tensor.
+// so a group costs 3 launches instead of 3 per tensor.
 struct BigEntry {
   const uint16_t* x;
   uint8_t* q;
-  float* s;        // scale_inv, also the scratch for the maxima
+  float* s;        // scale_inv
   int32_t M;
   int32_t N;
   int32_t cpt;     // chunks per tile
   int32_t flags;   // bit 0: flat, bit 1: vec
+  int32_t cpm;     // chunks per pass-1 item
+  int32_t pad;
 };
 
 template <int CAP>
 struct BigGroupArgs {
-  int32_t tile_start[CAP + 1];   // prefix of tiles (fill and finalize)
+  int32_t tile_start[CAP + 1];   // prefix of tiles (reduce)
   int32_t max_start[CAP + 1];    // prefix of pass-1 items
   int32_t quant_start[CAP + 1];  // prefix of pass-2 items
   BigEntry e[CAP];
@@ -724,30 +779,15 @@ __device__ __forceinline__ Big big_of(const BigEntry& e, int32_t bm, int32_t bn)
   b.bn = bn;
   b.row_phase = 0;
   b.col_phase = 0;
-  b.TMl = (e.M + bm - 1) / bm;
-  b.TNl = (e.N + bn - 1) / bn;
+  b.TMl = ((int64_t)e.M + bm - 1) / bm;
+  b.TNl = ((int64_t)e.N + bn - 1) / bn;
   b.cpt = e.cpt;
   b.items = b.TMl * b.TNl * b.cpt;
   b.flat = e.flags & 1;
   b.vec = (e.flags >> 1) & 1;
+  b.cpm = e.cpm;
+  b.pad = 0;
   return b;
-}
-
-// PHASE 0: zero every tensor's maxima; PHASE 1: maxima -> scales in place.
-template <int CAP, int PHASE>
-__global__ __launch_bounds__(kThreads) void big_group_tiles(const BigGroupArgs<CAP> a, int32_t count,
-                                                            int32_t total) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= total) return;
-  const int t = big_find(a.tile_start, count, i);
-  FP8BQ_GLOBAL float* sp = (FP8BQ_GLOBAL float*)a.e[t].s + (i - a.tile_start[t]);
-  if (PHASE == 0) {
-    *(FP8BQ_GLOBAL uint32_t*)sp = 0u;
-  } else {
-    float s, r;
-    tile_scale_f(*sp, s, r);
-    *sp = s;
-  }
 }
 
 template <int CAP>
@@ -757,7 +797,19 @@ __global__ __launch_bounds__(kThreads) void big_group_max(const BigGroupArgs<CAP
   for_each_unit(a.max_start[count], [&](int64_t u) {
     const int t = big_find(a.max_start, count, u);
     const Big b = big_of(a.e[t], bm, bn);
-    big_max_item(b, (uint32_t*)a.e[t].s, u - a.max_start[t], red);
+    big_max_item<true>(b, big_slots(a.e[t].q), u - a.max_start[t], red);
+  });
+}
+
+template <int CAP>
+__global__ __launch_bounds__(kThreads) void big_group_reduce(const BigGroupArgs<CAP> a,
+                                                             int32_t count) {
+  __shared__ uint32_t red[4];
+  for_each_unit(a.tile_start[count], [&](int64_t u) {
+    const int t = big_find(a.tile_start, count, u);
+    const BigEntry& e = a.e[t];
+    const int64_t groups = ((int64_t)e.cpt + e.cpm - 1) / e.cpm;
+    big_reduce_tile(big_slots(e.q), groups, u - a.tile_start[t], e.s, red);
   });
 }
 
@@ -767,7 +819,7 @@ __global__ __launch_bounds__(kThreads) void big_group_quant(const BigGroupArgs<C
   for_each_unit(a.quant_start[count], [&](int64_t u) {
     const int t = big_find(a.quant_start, count, u);
     const Big b = big_of(a.e[t], bm, bn);
-    big_quant_item(b, a.e[t].s, u - a.quant_start[t]);
+    big_quant_item<true>(b, a.e[t].s, u - a.quant_start[t]);
   });
 }
 
@@ -935,9 +987,9 @@ __global__ __launch_bounds__(kThreads) void quantize_group_args(const GroupArgs<
     d.s = at.s;
     d.M = at.M;
     d.N = at.N;
-    d.TN = (at.N + bn - 1) / bn;
+    d.TN = (int32_t)(((int64_t)at.N + bn - 1) / bn);
     d.body = at.body;
-    d.UN = at.body != kBodyVec ? d.TN : (at.N + 127) / 128;
+    d.UN = at.body != kBodyVec ? d.TN : (int32_t)(((int64_t)at.N + 127) / 128);
     d.pad = 0;
     d.reserved = 0;
     run_unit<KIND>(d, bm, bn, u - a.start[lo], red);

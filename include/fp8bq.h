@@ -41,9 +41,10 @@
  *   - Any block size bm, bn >= 1 and any alignment are accepted.  Blocks
  *     [128,128], [64,64] and [1,128] with N % 8 == 0, a 16-byte aligned x
  *     and an 8-byte aligned q take the vectorized kernels; tiles of more
- *     than 65536 elements take two passes (maxima, then quantization); all
- *     other cases take a general one-workgroup-per-tile kernel.  Results are
- *     identical whichever kernel runs.
+ *     than 65536 elements take two passes (maxima, then quantization), and
+ *     between the passes q holds partial maxima until the codes replace
+ *     them; all other cases take a general one-workgroup-per-tile kernel.
+ *     Results are identical whichever kernel runs.
  *   - Thread safety: calls may be made from several host threads; each
  *     thread has its own fp8bq_last_hip_error().
  */
@@ -118,8 +119,8 @@ size_t fp8bq_many_workspace_bytes(int32_t count);
  *   workspace_bytes  its size
  *   stream           hipStream_t (NULL = null stream)
  * Entries with M == 0 or N == 0 are skipped.  Entries whose tiles exceed
- * 65536 elements are quantized by the two-pass kernels (per entry, before
- * the grouped launch).  Outputs of different entries must not overlap each
+ * 65536 elements are quantized by the two-pass kernels (grouped, up to 128
+ * entries per launch, before the grouped launch of the others).  Outputs of different entries must not overlap each
  * other or any entry's x (not checked across entries).
  * Returns an fp8bq_status; on an argument error nothing is enqueued.
  */
@@ -146,9 +147,11 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
  * place), but must not partly overlap it.  Given the full maxima, every
  * shard's bytes equal the corresponding bytes of quantizing the whole matrix.
  *
- * The same two-pass kernels serve fp8bq_quantize / fp8bq_quantize_many for
- * tiles of more than 65536 elements (e.g. one scale per tensor: bm = M,
- * bn = N), using scale_inv as the scratch for the maxima.
+ * The same two passes serve fp8bq_quantize / fp8bq_quantize_many for tiles
+ * of more than 65536 elements (e.g. one scale per tensor: bm = M, bn = N);
+ * there the partial maxima of pass 1 go to slots in q (one per workgroup,
+ * no atomics), a small kernel reduces them to the scales, and pass 2
+ * overwrites q with the codes.
  * Both calls enqueue on `stream`; the pointers follow the conventions above.
  */
 int fp8bq_tile_amax(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, int32_t row_phase,

@@ -587,6 +587,28 @@ def test_per_tensor_and_large_tiles(gpu_lib):
     x = big[3:3 + 999 * 1001].view(999, 1001)
     q, s = fq.quantize(x, (999, 1001))
     assert_matches_oracle(x, q, s, 999, 1001, "large misaligned")
+    # q at odd byte addresses (pass 1 keeps its partial maxima in q from the
+    # first 4-byte boundary): same bytes, nothing written outside q
+    x = (torch.randn((700, 1200), generator=g, device=DEV) * 0.05).to(torch.bfloat16)
+    q0, s0 = fq.quantize(x, (700, 1200))
+    assert_matches_oracle(x, q0, s0, 700, 1200, "large, aligned q")
+    for off in (1, 3):
+        say("large, q offset", off)
+        buf = torch.full((700 * 1200 + 8,), 0x5A, dtype=torch.uint8, device=DEV)
+        q = buf[off:off + 700 * 1200].view(700, 1200)
+        s = torch.empty((1, 1), dtype=torch.float32, device=DEV)
+        fq.quantize(x, (700, 1200), out=(q, s))
+        assert torch.equal(q, q0.view(torch.uint8)) and torch.equal(s, s0), off
+        buf2 = torch.full_like(buf, 0x5A)
+        q2 = buf2[off:off + 700 * 1200].view(700, 1200)
+        fq.quantize_many([x, x[:350]], (700, 1200),
+                         outputs=[(q2, torch.empty((1, 1), device=DEV)),
+                                  (torch.empty((350, 1200), dtype=torch.uint8, device=DEV),
+                                   torch.empty((1, 1), device=DEV))])
+        assert torch.equal(q2, q0.view(torch.uint8)), off
+        for b in (buf, buf2):
+            rest = torch.cat([b[:off], b[off + 700 * 1200:]])
+            assert bool((rest == 0x5A).all()), off
     # grouped call with per-tensor blocks: one scale per tensor for the C2 layer
     specs = wl.c2()
     xs = [wl.materialize(sp, DEV) for sp in specs]
@@ -673,3 +695,26 @@ def test_beyond_2_31_elements(gpu_lib):
     assert_tiles_match_oracle(row, q, s, 1, 128, [(0, 0), (0, s.shape[1] - 1), (0, s.shape[1] // 2)],
                               "1 x 2^31-1")
     assert int(q.view(torch.uint8)[0, n - 1]) == 0xFE
+    del q, s
+    # the same row in grouped calls: [1,4096] tiles from the kernel-argument
+    # table (N + bn - 1 exceeds 2^31), then one scale for the whole row
+    # (grouped two-pass kernels, and the single call)
+    say("1 x 2^31-1 grouped [1,4096]")
+    ((q, s),) = fq.quantize_many([row], (1, 4096))
+    assert s.shape == (1, -(-n // 4096))
+    assert_tiles_match_oracle(row, q, s, 1, 4096, [(0, 0), (0, s.shape[1] - 1), (0, s.shape[1] // 2)],
+                              "grouped 1 x 2^31-1")
+    del q, s
+    s_ref, _ = oracle.blockwise.tile_scales_np(np.array([[7.0]]))
+    for how in ("grouped", "single"):
+        say("1 x 2^31-1 one scale,", how)
+        if how == "grouped":
+            ((q, s),) = fq.quantize_many([row], (1, n))
+        else:
+            q, s = fq.quantize(row, (1, n))
+        assert np.array_equal(scales_bits(s), scales_bits(s_ref.astype(np.float32))), how
+        for c0 in (0, n // 2 + 5, n - 4099):
+            q_ref, _ = oracle.quantize_with_amax(bits_np(row[:, c0:c0 + 4099].contiguous()), 1, n,
+                                                 np.array([[7.0]]), 0, c0)
+            assert np.array_equal(codes_np(q[:, c0:c0 + 4099].contiguous()), q_ref), (how, c0)
+        del q, s
