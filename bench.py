@@ -33,7 +33,8 @@ HBM_PEAK_GBS = 8000.0
 CPU_SAMPLE_VALUES = 770_000_000
 METRIC = "blockwise FP8 quantize GB/s (bf16 in + fp8/scale out), % of HBM peak, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_t128_dense36_traffic.md")
-KERNEL_SOURCES = ("fp8_blockwise_weight_amd/csrc/kernels.hpp", "fp8_blockwise_weight_amd/csrc/fp8bq.hip")
+KERNEL_SOURCES = ("fp8_blockwise_weight_amd/csrc/kernels.hpp", "fp8_blockwise_weight_amd/csrc/fp8bq.hip",
+                  "fp8_blockwise_weight_amd/csrc/div31.hpp")
 
 
 def log(*a):

@@ -19,7 +19,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "fp8bq.hip")
-DEPS = [SRC, os.path.join(HERE, "csrc", "kernels.hpp"), os.path.join(ROOT, "include", "fp8bq.h")]
+DEPS = [SRC, os.path.join(HERE, "csrc", "kernels.hpp"), os.path.join(HERE, "csrc", "div31.hpp"),
+        os.path.join(ROOT, "include", "fp8bq.h")]
 LIB = os.path.join(HERE, "libfp8bq.so")
 ARCH = "gfx950"
 

@@ -595,13 +595,22 @@ int fp8bq_dequantize(const void* q, const float* scale_inv, int64_t M, int64_t N
   if (vec) {
     const int64_t groups = static_cast<int64_t>(n) / G;
     const int64_t per_block = static_cast<int64_t>(fp8bq::kThreads) * fp8bq::kDqUnroll;
-    const dim3 grid(grid_for((groups + per_block - 1) / per_block));
+    const unsigned grid = grid_for((groups + per_block - 1) / per_block);
+    const int64_t gpr = N / G;  // groups per row, < 2^29
+    const int64_t stride = static_cast<int64_t>(grid) * per_block;
+    const fp8bq::Div31 by_gpr = fp8bq::make_div31(static_cast<uint32_t>(gpr));
+    const fp8bq::Div31 by_bm = fp8bq::make_div31(static_cast<uint32_t>(bm));
+    const fp8bq::Div31 by_bn = fp8bq::make_div31(static_cast<uint32_t>(bn));
+    const int64_t step_rows = stride / gpr;
+    const int32_t step_cols = static_cast<int32_t>(stride % gpr);
     if (out_dtype == FP8BQ_OUT_F32) {
-      hipLaunchKernelGGL(fp8bq::dequant_vec<fp8bq::kOutF32>, grid, dim3(fp8bq::kThreads), 0, s, qb,
-                         scale_inv, N, bm, bn, tn, out, groups);
+      hipLaunchKernelGGL(fp8bq::dequant_vec<fp8bq::kOutF32>, dim3(grid), dim3(fp8bq::kThreads), 0,
+                         s, qb, scale_inv, static_cast<int32_t>(gpr), tn, by_gpr, by_bm, by_bn, out,
+                         groups, step_rows, step_cols);
     } else {
-      hipLaunchKernelGGL(fp8bq::dequant_vec<fp8bq::kOutBF16>, grid, dim3(fp8bq::kThreads), 0, s, qb,
-                         scale_inv, N, bm, bn, tn, out, groups);
+      hipLaunchKernelGGL(fp8bq::dequant_vec<fp8bq::kOutBF16>, dim3(grid), dim3(fp8bq::kThreads), 0,
+                         s, qb, scale_inv, static_cast<int32_t>(gpr), tn, by_gpr, by_bm, by_bn, out,
+                         groups, step_rows, step_cols);
     }
   } else {
     const int64_t blocks = (static_cast<int64_t>(n) + fp8bq::kThreads - 1) / fp8bq::kThreads;

@@ -41,6 +41,8 @@
 #include <type_traits>
 #include <utility>
 
+#include "div31.hpp"
+
 namespace fp8bq {
 
 constexpr float kE4m3Max = 448.0f;
@@ -871,38 +873,53 @@ __device__ __forceinline__ f32x4 dq4(uint32_t w, float s) {
 // Vector dequantization: every lane writes one 16-byte output chunk per
 // group -- 4 codes to 4 fp32, or 8 codes to 8 BF16 -- so each wave store is
 // one contiguous 1 KB run (16 B per lane, lanes adjacent).  A workgroup
-// handles kDqUnroll * 256 groups, all loads issued before the stores.
-// Needs N % G == 0, bn % G == 0 (a group never straddles a row or a tile),
-// q aligned to G bytes and out to 16 bytes (G = 4 for fp32, 8 for BF16).
-constexpr int kDqUnroll = 4;
+// handles blocks of kDqUnroll * 256 consecutive groups, all loads issued
+// before the stores.  Needs N % G == 0, bn % G == 0 (a group never straddles
+// a row or a tile), q aligned to G bytes and out to 16 bytes (G = 4 for
+// fp32, 8 for BF16).
+//
+// Index math: (row0, col0) of a block's first group is divided out once per
+// workgroup and then advanced by the grid stride (step_rows, step_cols);
+// inside a block every numerator is below 2^31, so group -> row, column and
+// tile indices are multiply-and-shift divisions by the invariant gpr (groups
+// per row), bm and bn.
+constexpr int kDqUnroll = 2;
 
 template <int OUT>
 __global__ __launch_bounds__(kThreads) void dequant_vec(const uint8_t* __restrict__ q,
-                                                        const float* __restrict__ s, int64_t N,
-                                                        int32_t bm, int32_t bn, int32_t TN,
-                                                        void* __restrict__ out, int64_t groups) {
+                                                        const float* __restrict__ s, int32_t gpr,
+                                                        int32_t TN, Div31 by_gpr, Div31 by_bm,
+                                                        Div31 by_bn, void* __restrict__ out,
+                                                        int64_t groups, int64_t step_rows,
+                                                        int32_t step_cols) {
   constexpr int G = OUT == kOutF32 ? 4 : 8;
   typedef typename std::conditional<G == 4, uint32_t, u32x2>::type QWord;
-  const int64_t gpr = N / G;  // groups per row
   const int64_t per_block = (int64_t)kThreads * kDqUnroll;
-  for (int64_t b0 = (int64_t)blockIdx.x * per_block; b0 < groups;
-       b0 += (int64_t)gridDim.x * per_block) {
-    const int64_t g0 = b0 + threadIdx.x;
+  int64_t b0 = (int64_t)blockIdx.x * per_block;
+  if (b0 >= groups) return;
+  int64_t row0 = b0 / gpr;            // once per workgroup
+  int32_t col0 = (int32_t)(b0 - row0 * gpr);
+  for (; b0 < groups; b0 += (int64_t)gridDim.x * per_block) {
     QWord w[kDqUnroll];
     float sc[kDqUnroll];
 #pragma unroll
     for (int k = 0; k < kDqUnroll; ++k) {
-      const int64_t g = g0 + (int64_t)k * kThreads;
+      const uint32_t o = threadIdx.x + k * kThreads;
+      const int64_t g = b0 + o;
       if (g < groups) {
-        const int64_t row = g / gpr;
-        const int64_t col = (g - row * gpr) * G;
+        // col0 < gpr < 2^29 and o < 256 * kDqUnroll: c < 2^31; row < M, col * G < N.
+        const uint32_t c = (uint32_t)col0 + o;
+        const uint32_t dr = div31(c, by_gpr);
+        const uint32_t col = c - dr * (uint32_t)gpr;
+        const uint32_t row = (uint32_t)row0 + dr;
         w[k] = __builtin_nontemporal_load((const FP8BQ_GLOBAL QWord*)(q) + g);
-        sc[k] = ((const FP8BQ_GLOBAL float*)s)[(row / bm) * TN + col / bn];
+        sc[k] = ((const FP8BQ_GLOBAL float*)s)[(int64_t)div31(row, by_bm) * TN +
+                                                div31(col * G, by_bn)];
       }
     }
 #pragma unroll
     for (int k = 0; k < kDqUnroll; ++k) {
-      const int64_t g = g0 + (int64_t)k * kThreads;
+      const int64_t g = b0 + threadIdx.x + k * kThreads;
       if (g >= groups) continue;
       if constexpr (OUT == kOutF32) {
         const f32x4 a = dq4(w[k], sc[k]);
@@ -914,6 +931,12 @@ __global__ __launch_bounds__(kThreads) void dequant_vec(const uint8_t* __restric
                       bf16_rne(b.x) | (bf16_rne(b.y) << 16), bf16_rne(b.z) | (bf16_rne(b.w) << 16)};
         __builtin_nontemporal_store(p, (FP8BQ_GLOBAL u32x4*)out + g);
       }
+    }
+    row0 += step_rows;
+    col0 += step_cols;
+    if (col0 >= gpr) {
+      col0 -= gpr;
+      ++row0;
     }
   }
 }
