@@ -344,31 +344,33 @@ __device__ __forceinline__ void reg_tile(const Desc& d, int32_t bm, int32_t bn, 
 // pass 2 re-reads the tile (mostly from cache) and writes it.  When the
 // tile's columns are 8-aligned and the tensor is aligned (body kBodyLoopVec)
 // both passes use 16-byte loads over vector v = (row v / (cols/8), 8-column
-// group v % (cols/8)); otherwise they go element by element.
+// group v % (cols/8)); otherwise they go element by element.  Tiles here
+// hold at most kBigTile = 65536 elements (larger ones take the two-pass
+// kernels), so in-tile indices use 32-bit arithmetic.
 template <bool VEC>
 __device__ __forceinline__ void general_tile(const Desc& d, int32_t bm, int32_t bn, int64_t ti,
                                              int64_t tj, uint32_t* red) {
-  const int t = threadIdx.x;
+  const uint32_t t = threadIdx.x;
   const int64_t r0 = ti * bm;
   const int64_t c0 = tj * bn;
-  const int64_t rows = (d.M - r0) < bm ? (d.M - r0) : bm;
-  const int64_t cols = (d.N - c0) < bn ? (d.N - c0) : bn;
-  const int64_t n = rows * cols;
+  const uint32_t rows = (uint32_t)((d.M - r0) < bm ? (d.M - r0) : bm);
+  const uint32_t cols = (uint32_t)((d.N - c0) < bn ? (d.N - c0) : bn);
+  const uint32_t n = rows * cols;
   const FP8BQ_GLOBAL uint16_t* x = (const FP8BQ_GLOBAL uint16_t*)(d.x + (size_t)r0 * d.N + c0);
   FP8BQ_GLOBAL uint8_t* q = (FP8BQ_GLOBAL uint8_t*)(d.q + (size_t)r0 * d.N + c0);
-  const int64_t vpr = cols / 8;
-  const int64_t nvec = rows * vpr;
+  const uint32_t vpr = cols / 8;
+  const uint32_t nvec = rows * vpr;
   uint32_t m = 0;
   if (VEC) {
-    for (int64_t v = t; v < nvec; v += kThreads) {
-      const int64_t rr = v / vpr;
+    for (uint32_t v = t; v < nvec; v += kThreads) {
+      const uint32_t rr = v / vpr;
       const u32x4 w = *(const FP8BQ_GLOBAL u32x4*)(x + (size_t)rr * d.N + (v - rr * vpr) * 8);
       m = max(m, halves_max(fold_abs(w)));
     }
   } else {
-    for (int64_t e = t; e < n; e += kThreads) {
-      const int64_t rr = e / cols;
-      const int64_t cc = e - rr * cols;
+    for (uint32_t e = t; e < n; e += kThreads) {
+      const uint32_t rr = e / cols;
+      const uint32_t cc = e - rr * cols;
       m = max(m, (uint32_t)(x[(size_t)rr * d.N + cc] & 0x7FFFu));
     }
   }
@@ -381,16 +383,16 @@ __device__ __forceinline__ void general_tile(const Desc& d, int32_t bm, int32_t 
   tile_scale(tm, s, r);
   if (t == 0) ((FP8BQ_GLOBAL float*)d.s)[(size_t)ti * d.TN + tj] = s;
   if (VEC) {
-    for (int64_t v = t; v < nvec; v += kThreads) {
-      const int64_t rr = v / vpr;
+    for (uint32_t v = t; v < nvec; v += kThreads) {
+      const uint32_t rr = v / vpr;
       const size_t off = (size_t)rr * d.N + (v - rr * vpr) * 8;
       const u32x4 w = *(const FP8BQ_GLOBAL u32x4*)(x + off);
       __builtin_nontemporal_store(quant8(w, r), (FP8BQ_GLOBAL u32x2*)(q + off));
     }
   } else {
-    for (int64_t e = t; e < n; e += kThreads) {
-      const int64_t rr = e / cols;
-      const int64_t cc = e - rr * cols;
+    for (uint32_t e = t; e < n; e += kThreads) {
+      const uint32_t rr = e / cols;
+      const uint32_t cc = e - rr * cols;
       const size_t off = (size_t)rr * d.N + cc;
       const float y = clamp448(__uint_as_float((uint32_t)x[off] << 16) * r);
       q[off] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xFF);
