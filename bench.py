@@ -230,6 +230,8 @@ def main():
                   f"({'one launch' if launches == 1 else f'{launches} launches'} per step)",
         "bytes_per_launch": bytes_per_launch,
         "mean_launch_ms": round(mean_launch_ms, 4),
+        "median_launch_ms": round(sorted(ev_ms)[len(ev_ms) // 2] / launches, 4),
+        "min_launch_ms": round(min(ev_ms) / launches, 4),
     }
 
     cpu = None
