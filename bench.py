@@ -18,7 +18,11 @@ Reported value: algorithmic GB/s = (2 B read + 1 B written per element +
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3]
                        [--workload dense|dense-layer|moe|ragged|vocab] [--block bm,bn]
-                       [--per-tensor] [--no-cpu-baseline] [--calibrate-copy]
+                       [--per-tensor] [--no-cpu-baseline] [--calibrate-copy] [--input-sha]
+
+The CPU sample's inputs are hashed (SHA-256 per tensor on stderr, and a
+digest of those in cpu_baseline.sample_sha256); --input-sha hashes every
+input of the workload.
 """
 
 import argparse
@@ -122,6 +126,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of known size (for counter calibration)")
+    ap.add_argument("--input-sha", action="store_true",
+                    help="log the SHA-256 of every input tensor (copies the whole workload to the host)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -163,6 +169,10 @@ def main():
         n_tensors += len(specs)
     torch.cuda.synchronize()
     log(f"generated {n_tensors} tensors, {n_elems / 1e9:.3f} G values in {time.perf_counter() - t0:.1f}s")
+    if args.input_sha:
+        for (xs, _), specs in zip(keep, groups):
+            for x, sp in zip(xs, specs):
+                log(f"input sha256 {sp.name} {sp.M}x{sp.N} {tensor_sha256(x)}")
 
     stream = torch.cuda.current_stream(dev)
     sptr = ctypes.c_void_p(stream.cuda_stream)
@@ -356,6 +366,14 @@ def time_per_tensor(lib, keep, groups, bm, bn, stream, sptr, reps=3):
     return res
 
 
+def tensor_sha256(x):
+    """SHA-256 of a tensor's bytes (copied to the host)."""
+    import numpy as np
+    import torch
+
+    return hashlib.sha256(x.view(torch.int16).cpu().numpy().view(np.uint8).tobytes()).hexdigest()
+
+
 def cpu_baseline(xs, specs, bm, bn):
     """The CPU oracle (as it is, single process) on a bounded sample of the workload."""
     import numpy as np
@@ -364,6 +382,11 @@ def cpu_baseline(xs, specs, bm, bn):
     import oracle
 
     host = [x.view(torch.int16).cpu().numpy().view(np.uint16) for x in xs]
+    digest = hashlib.sha256()
+    for h, sp in zip(host, specs):
+        one = hashlib.sha256(h.tobytes()).hexdigest()
+        digest.update(bytes.fromhex(one))
+        log(f"input sha256 {sp.name} {sp.M}x{sp.N} {one}")
     nbytes = sum(algorithmic_bytes(sp.M, sp.N, bm, bn) for sp in specs)
     nel = sum(sp.M * sp.N for sp in specs)
     t0 = time.perf_counter()
@@ -378,6 +401,7 @@ def cpu_baseline(xs, specs, bm, bn):
         "kind": "oracle",
         "sample": f"first {len(host)} tensors ({nel} values) of the benchmarked workload, "
                   f"numpy oracle in one process, {dt:.1f} s",
+        "sample_sha256": digest.hexdigest(),
     }
 
 
