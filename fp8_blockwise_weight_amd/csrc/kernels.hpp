@@ -474,6 +474,23 @@ __global__ __launch_bounds__(kThreads) void quantize_one(Desc d, int32_t bm, int
   });
 }
 
+// Tensor that owns global unit u: the largest t < count with start[t] <= u
+// (start[0] = 0 <= u, non-decreasing).  start is uniform, so the search runs
+// on scalar loads.
+template <typename T>
+__device__ __forceinline__ int find_tensor(const T* start, int count, int64_t u) {
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (start[mid] <= u) {
+      lo = mid;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  return lo;
+}
+
 // A list of tensors: start[t] is the first global unit of tensor t
 // (start[0] = 0, strictly increasing: empty tensors are not listed).
 template <int KIND>
@@ -483,15 +500,7 @@ __global__ __launch_bounds__(kThreads) void quantize_group(const Desc* __restric
                                                            int64_t total) {
   __shared__ uint32_t red[8];
   for_each_unit(total, [&](int64_t u) {
-    int lo = 0, hi = count - 1;  // largest t with start[t] <= u
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (start[mid] <= u) {
-        lo = mid;
-      } else {
-        hi = mid - 1;
-      }
-    }
+    const int lo = find_tensor(start, count, u);
     const Desc d = descs[lo];
     run_unit<KIND>(d, bm, bn, u - start[lo], red);
   });
@@ -759,20 +768,6 @@ struct BigGroupArgs {
   BigEntry e[CAP];
 };
 
-// Largest t with start[t] <= u (start is non-decreasing, start[0] = 0 <= u).
-__device__ __forceinline__ int big_find(const int32_t* start, int count, int64_t u) {
-  int lo = 0, hi = count - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (start[mid] <= u) {
-      lo = mid;
-    } else {
-      hi = mid - 1;
-    }
-  }
-  return lo;
-}
-
 __device__ __forceinline__ Big big_of(const BigEntry& e, int32_t bm, int32_t bn) {
   Big b;
   b.x = e.x;
@@ -799,7 +794,7 @@ __global__ __launch_bounds__(kThreads) void big_group_max(const BigGroupArgs<CAP
                                                           int32_t bm, int32_t bn) {
   __shared__ uint32_t red[4];
   for_each_unit(a.max_start[count], [&](int64_t u) {
-    const int t = big_find(a.max_start, count, u);
+    const int t = find_tensor(a.max_start, count, u);
     const Big b = big_of(a.e[t], bm, bn);
     big_max_item<true>(b, big_slots(a.e[t].q), u - a.max_start[t], red);
   });
@@ -810,7 +805,7 @@ __global__ __launch_bounds__(kThreads) void big_group_reduce(const BigGroupArgs<
                                                              int32_t count) {
   __shared__ uint32_t red[4];
   for_each_unit(a.tile_start[count], [&](int64_t u) {
-    const int t = big_find(a.tile_start, count, u);
+    const int t = find_tensor(a.tile_start, count, u);
     const BigEntry& e = a.e[t];
     const int64_t groups = ((int64_t)e.cpt + e.cpm - 1) / e.cpm;
     big_reduce_tile(big_slots(e.q), groups, u - a.tile_start[t], e.s, red);
@@ -821,7 +816,7 @@ template <int CAP>
 __global__ __launch_bounds__(kThreads) void big_group_quant(const BigGroupArgs<CAP> a, int32_t count,
                                                             int32_t bm, int32_t bn) {
   for_each_unit(a.quant_start[count], [&](int64_t u) {
-    const int t = big_find(a.quant_start, count, u);
+    const int t = find_tensor(a.quant_start, count, u);
     const Big b = big_of(a.e[t], bm, bn);
     big_quant_item<true>(b, a.e[t].s, u - a.quant_start[t]);
   });
@@ -996,15 +991,7 @@ __global__ __launch_bounds__(kThreads) void quantize_group_args(const GroupArgs<
                                                                 int32_t bn, int32_t total) {
   __shared__ uint32_t red[8];
   for_each_unit(total, [&](int64_t u) {
-    int lo = 0, hi = count - 1;  // largest t with start[t] <= u
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.start[mid] <= u) {
-        lo = mid;
-      } else {
-        hi = mid - 1;
-      }
-    }
+    const int lo = find_tensor(a.start, count, u);
     const ArgTensor& at = a.t[lo];
     Desc d;
     d.x = at.x;
