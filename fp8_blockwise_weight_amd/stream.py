@@ -9,13 +9,14 @@ the quantized tensor under its own name followed by its descale under
 raises when no block size is configured and squeezes a trailing singleton
 off the scale.
 
-Here consecutive FP8 weights are batched into one grouped launch
-(``quantize_many``), bounded by ``group_bytes`` of BF16 input and
-``group_max`` tensors, so thousands of small expert matrices cost a handful
-of launches.  Output order is the input order.  Which weights are FP8 is a
-caller predicate (the pages ask the inference engine's module types; this
-library has no engine, so the default is "a 2-D tensor whose name ends in
-``weight``").
+Here FP8 weights are batched into one grouped launch (``quantize_many``),
+bounded by ``group_bytes`` of BF16 input and ``group_max`` tensors, so
+thousands of small expert matrices cost a handful of launches.  Pass-through
+pairs (norms, biases) wait in the queue beside them instead of cutting the
+group, so a decoder layer's projections share a launch.  Output order is
+the input order.  Which weights are FP8 is a caller predicate (the pages ask
+the inference engine's module types; this library has no engine, so the
+default is "a 2-D tensor whose name ends in ``weight``").
 """
 
 from typing import Callable, Iterable, Iterator, Tuple
@@ -47,30 +48,37 @@ def quant_weights(weights: Iterable[Tuple[str, object]], block_size=(128, 128),
 
     bm, bn = block_shape(block_size)  # raises ValueError when the block size is missing
     dtype = dtype or torch.bfloat16
-    pending = []
-    state = {"bytes": 0}
+    pending = []     # (name, tensor, quantize?) in input order
+    state = {"bytes": 0, "count": 0}
 
     def flush():
         if not pending:
             return
-        names = [n for n, _ in pending]
-        xs = [x for _, x in pending]
+        items = list(pending)
         pending.clear()
-        state["bytes"] = 0
-        outs = quantize_many(xs, (bm, bn))
+        state["bytes"] = state["count"] = 0
+        xs = [x for _, x, fp8 in items if fp8]
+        outs = iter(quantize_many(xs, (bm, bn)) if xs else [])
         del xs
-        for name, (q, s) in zip(names, outs):
+        items = [(name, None if fp8 else x, fp8) for name, x, fp8 in items]  # drop BF16 inputs
+        for name, x, fp8 in items:
+            if not fp8:
+                yield name, x
+                continue
+            q, s = next(outs)
             yield name, q
             yield name + SCALE_SUFFIX, (s.squeeze(-1) if squeeze_scale and s.shape[-1] == 1 else s)
 
     for name, t in weights:
         if not is_fp8(name, t):
-            yield from flush()
-            yield name, t
+            pending.append((name, t, False))
+            if not state["count"]:
+                yield from flush()   # nothing to wait for
             continue
         x = t if (t.dtype == dtype and t.is_contiguous()) else t.to(dtype).contiguous()
-        pending.append((name, x))
+        pending.append((name, x, True))
+        state["count"] += 1
         state["bytes"] += x.numel() * x.element_size()
-        if len(pending) >= group_max or state["bytes"] >= group_bytes:
+        if state["count"] >= group_max or state["bytes"] >= group_bytes:
             yield from flush()
     yield from flush()

@@ -42,8 +42,8 @@ def test_order_names_and_passthrough(monkeypatch):
     for n, v in got:
         if n.endswith("bias"):
             assert v.dim() == 1
-    # a pass-through tensor flushes the pending group, so groups split at biases
-    assert sum(fake.calls) == 7 and max(fake.calls) <= 3
+    # pass-through tensors wait beside the FP8 ones: the 7 weights share one launch
+    assert fake.calls == [7]
 
 
 def test_grouping_limits(monkeypatch):
@@ -58,6 +58,24 @@ def test_grouping_limits(monkeypatch):
     fake.calls.clear()
     list(stream.quant_weights(ws, (128, 128), group_bytes=3 * 64))   # 64 B per tensor
     assert fake.calls == [3, 3, 3, 1]
+
+
+def test_passthrough_order_with_group_limits(monkeypatch):
+    """Group limits cut the queue while pass-through pairs wait in it: every
+    pair still comes out in input order, and a leading pass-through is not
+    held back."""
+    fake = FakeGroup()
+    monkeypatch.setattr(stream, "quantize_many", fake)
+    ws = [("embed.scale", torch.zeros(3))] + _weights(9, bias_every=2)
+    it = stream.quant_weights(ws, (128, 128), group_max=4)
+    assert next(it)[0] == "embed.scale"
+    assert fake.calls == []
+    got = [n for n, _ in it]
+    want = []
+    for n, _ in ws[1:]:
+        want += [n, n + "_scale_inv"] if n.endswith("weight") else [n]
+    assert got == want
+    assert fake.calls == [4, 4, 1]
 
 
 def test_missing_block_size_raises(monkeypatch):
