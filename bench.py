@@ -119,8 +119,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense")
     ap.add_argument("--block", default=None, help="bm,bn for the ragged/vocab workloads")
-    ap.add_argument("--op", default="quantize", choices=["quantize", "dequant-f32", "dequant-bf16"],
-                    help="quantize (default) or time fp8bq_dequantize on the quantized workload")
+    ap.add_argument("--op", default="quantize",
+                    choices=["quantize", "dequant-f32", "dequant-bf16", "stream"],
+                    help="quantize (default); time fp8bq_dequantize on the quantized workload; "
+                         "or time the streaming quant_weights loop over the workload in model "
+                         "order with norm weights passed through")
     ap.add_argument("--per-tensor", action="store_true",
                     help="also time one fp8bq_quantize call per tensor (HIP events per call)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -219,6 +222,9 @@ def main():
         torch.cuda.synchronize()
         log("calibration copy: 3 x 1 GiB device-to-device")
 
+    if args.op == "stream":
+        time_stream(keep, groups, bm, bn, args, desc)
+        return
     if args.op != "quantize":
         time_dequant(lib, keep, groups, bm, bn, args, stream, sptr, desc)
         return
@@ -327,6 +333,56 @@ def time_dequant(lib, keep, groups, bm, bn, args, stream, sptr, desc):
                       "bytes_per_step": nbytes, "ms_per_step": round(ms, 4),
                       "GBps": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}),
           flush=True)
+
+
+def time_stream(keep, groups, bm, bn, args, desc):
+    """stream.quant_weights over the workload's weights in model order, with a
+    1-D norm weight (passed through) before each layer's attention and MLP
+    blocks, as a decoder's named parameters come; every yielded pair is
+    consumed.  Reports algorithmic GB/s of the FP8 weights, wall clock."""
+    import torch
+
+    import fp8_blockwise_weight_amd as fq
+    from fp8_blockwise_weight_amd.stream import quant_weights
+
+    dev = torch.device("cuda:0")
+    pairs = []
+    nbytes = 0
+    layer = None
+    for (xs, _), specs in zip(keep, groups):
+        for x, sp in zip(xs, specs):
+            prefix = ".".join(sp.name.split(".")[:2])      # "layers.<i>"
+            if prefix != layer:
+                layer = prefix
+                pairs.append((f"{layer}.input_layernorm.weight",
+                              torch.ones(x.shape[1], dtype=torch.bfloat16, device=dev)))
+            if sp.name.endswith("gate_proj"):
+                pairs.append((f"{layer}.post_attention_layernorm.weight",
+                              torch.ones(x.shape[1], dtype=torch.bfloat16, device=dev)))
+            pairs.append((f"{sp.name}.weight", x))
+            nbytes += algorithmic_bytes(sp.M, sp.N, bm, bn)
+    fq.load_library()
+
+    def step():
+        n = 0
+        for _name, _t in quant_weights(pairs, (bm, bn)):
+            n += 1
+        return n
+
+    for _ in range(args.warmup):
+        yielded = step()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for _ in range(args.steps):
+        yielded = step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - w0) * 1e3 / args.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"stream: {len(pairs)} pairs in, {yielded} out per step, wall {ms:.3f} ms/step; "
+        f"{gbs:.1f} GB/s = {100 * gbs / HBM_PEAK_GBS:.1f}% of peak")
+    print(json.dumps({"op": "stream", "workload": desc, "pairs_in": len(pairs), "pairs_out": yielded,
+                      "bytes_per_step": nbytes, "ms_per_step": round(ms, 4), "GBps": round(gbs, 1),
+                      "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}), flush=True)
 
 
 def time_per_tensor(lib, keep, groups, bm, bn, stream, sptr, reps=3):

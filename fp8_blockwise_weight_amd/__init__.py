@@ -14,6 +14,7 @@ form of the per-weight loop of the page "vllm_fp8_utils.py" (section 3).
 
 import ctypes
 import os
+import struct
 from typing import List, Optional, Sequence, Tuple
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,7 +45,7 @@ EXPORTS = (
 
 
 class TensorEntry(ctypes.Structure):
-    """``fp8bq_tensor`` of include/fp8bq.h."""
+    """``fp8bq_tensor`` of include/fp8bq.h (40 bytes, no padding)."""
 
     _fields_ = [
         ("x", ctypes.c_void_p),
@@ -195,23 +196,50 @@ def workspace_bytes(count: int) -> int:
     return int(load_library().fp8bq_many_workspace_bytes(int(count)))
 
 
+_ENTRY = struct.Struct("=QQQqq")  # fp8bq_tensor: x, q, scale_inv, M, N
+
+
 def make_entries(tensors: Sequence, outputs: Sequence) -> ctypes.Array:
-    arr = (TensorEntry * len(tensors))()
-    for i, (x, (q, s)) in enumerate(zip(tensors, outputs)):
-        arr[i].x = x.data_ptr()
-        arr[i].q = q.data_ptr()
-        arr[i].scale_inv = s.data_ptr()
-        arr[i].M, arr[i].N = x.shape
-    return arr
+    """The host ``fp8bq_tensor`` array of a grouped call."""
+    buf = bytearray(_ENTRY.size * len(tensors))
+    off = 0
+    for x, (q, s) in zip(tensors, outputs):
+        M, N = x.shape
+        _ENTRY.pack_into(buf, off, x.data_ptr(), q.data_ptr(), s.data_ptr(), M, N)
+        off += _ENTRY.size
+    return (TensorEntry * len(tensors)).from_buffer(buf)
+
+
+def _group_outputs(tensors: Sequence, bm: int, bn: int, device) -> List:
+    """Outputs for a grouped call: one q buffer and one scale buffer per
+    distinct row length N, cut into per-tensor [M, N] / [TM, TN] views by
+    row (contiguous, disjoint, in input order).  Two allocations per row
+    length instead of two per tensor: for lists of thousands of small
+    matrices the allocations, not the kernel, set the pace."""
+    import torch
+
+    by_n = {}
+    for i, x in enumerate(tensors):
+        by_n.setdefault(x.shape[1], []).append(i)
+    outs = [None] * len(tensors)
+    for N, idx in by_n.items():
+        ms = [tensors[i].shape[0] for i in idx]
+        tms = [-(-m // bm) for m in ms]
+        qbuf = torch.empty((sum(ms), N), dtype=torch.float8_e4m3fn, device=device)
+        sbuf = torch.empty((sum(tms), -(-N // bn)), dtype=torch.float32, device=device)
+        for i, q, s in zip(idx, qbuf.split(ms), sbuf.split(tms)):
+            outs[i] = (q, s)
+    return outs
 
 
 def quantize_many(tensors: Sequence, block_size=(128, 128), outputs: Optional[Sequence] = None,
                   workspace=None) -> List:
     """Quantize a list of BF16 GPU tensors (same device, one block size) in one launch.
 
-    Returns a list of ``(q, scale_inv)`` pairs in input order.  ``outputs``
-    and ``workspace`` (a uint8 GPU tensor of at least ``workspace_bytes``)
-    may be preallocated.
+    Returns a list of ``(q, scale_inv)`` pairs in input order.  Outputs the
+    call allocates are row views into one buffer per distinct N (a view
+    keeps its buffer alive).  ``outputs`` and ``workspace`` (a uint8 GPU
+    tensor of at least ``workspace_bytes``) may be preallocated.
     """
     import torch
 
@@ -225,9 +253,7 @@ def quantize_many(tensors: Sequence, block_size=(128, 128), outputs: Optional[Se
         if x.device != dev:
             raise ValueError("all tensors of one grouped call must be on the same device")
     if outputs is None:
-        outputs = [(torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=dev),
-                    torch.empty(scale_shape(*x.shape, bm, bn), dtype=torch.float32, device=dev))
-                   for x in tensors]
+        outputs = _group_outputs(tensors, bm, bn, dev)
     else:
         outputs = list(outputs)
         if len(outputs) != len(tensors):

@@ -33,7 +33,7 @@ def default_is_fp8(name: str, tensor) -> bool:
 
 def quant_weights(weights: Iterable[Tuple[str, object]], block_size=(128, 128),
                   is_fp8: Callable[[str, object], bool] = default_is_fp8, dtype=None,
-                  group_bytes: int = 256 << 20, group_max: int = 512,
+                  group_bytes: int = 1 << 30, group_max: int = 512,
                   squeeze_scale: bool = False) -> Iterator[Tuple[str, object]]:
     """Yield ``(name, tensor)`` pairs with every FP8 weight quantized.
 

@@ -222,3 +222,24 @@ def test_python_output_checks():
         fq._check_outputs((q, s.to(torch.float64)), 4, 8, 128, 128, cpu)
     with pytest.raises(ValueError):
         fq._check_outputs((torch.empty((8, 4), dtype=torch.uint8).t(), s), 4, 8, 128, 128, cpu)
+
+
+def test_group_outputs_layout():
+    """Outputs a grouped call allocates: per tensor, a contiguous [M, N] e4m3
+    view and a [TM, TN] fp32 view, in input order, pairwise disjoint, empty
+    shapes included (host logic, CPU tensors)."""
+    import torch
+
+    shapes = [(5, 8), (3, 16), (0, 8), (7, 8), (2, 0), (130, 16), (1, 24)]
+    xs = [torch.empty(sh, dtype=torch.bfloat16) for sh in shapes]
+    outs = fq._group_outputs(xs, 4, 8, torch.device("cpu"))
+    spans = []
+    for x, (q, s) in zip(xs, outs):
+        assert q.shape == x.shape and q.dtype == torch.float8_e4m3fn and q.is_contiguous()
+        assert tuple(s.shape) == fq.scale_shape(*x.shape, 4, 8)
+        assert s.dtype == torch.float32 and s.is_contiguous()
+        for t in (q, s):
+            if t.numel():
+                spans.append((t.data_ptr(), t.data_ptr() + t.numel() * t.element_size()))
+    spans.sort()
+    assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
