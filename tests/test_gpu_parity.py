@@ -347,7 +347,7 @@ def test_grouped_mixed_list(gpu_lib):
         torch.empty((5, 0), dtype=torch.bfloat16, device=DEV),
         (torch.randn((1537, 2048), generator=g, device=DEV) * 0.03).to(torch.bfloat16),
     ]
-    for block in BLOCKS + [(3, 5)]:
+    for block in BLOCKS + [(3, 5), (1024, 1024)]:   # the last: large tiles, grouped two-pass kernels
         say("mixed", block)
         outs = fq.quantize_many(mats, block)
         for i, (x, (q, s)) in enumerate(zip(mats, outs)):
@@ -368,7 +368,9 @@ def test_grouped_workspace_path(gpu_lib):
         M, N = int(rng.integers(1, 300)), int(rng.choice([8, 64, 136, 256, 264, 7, 99]))
         mats.append((torch.randn((M, N), generator=g, device=DEV) * 0.03).to(torch.bfloat16))
     assert fq.workspace_bytes(len(mats)) > 0
-    for block in BLOCKS + [(5, 3)]:
+    # (300, 300): tensors with more than 65536 elements per tile take the
+    # grouped two-pass kernels, the rest the workspace path, in one call
+    for block in BLOCKS + [(5, 3), (300, 300)]:
         say("workspace path", block)
         outs = fq.quantize_many(mats, block)
         for i, (x, (q, s)) in enumerate(zip(mats, outs)):
