@@ -1,0 +1,48 @@
+"""bench.py keeps its output contract: one JSON line with the required keys
+(GPU), and a refusal with a message for more than one GPU (CPU)."""
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+BENCH = os.path.join(ROOT, "bench.py")
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, BENCH, "--gpus", "2"], capture_output=True, text=True,
+                         timeout=120, cwd=ROOT)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
+    assert res.stdout.strip() == ""
+
+
+@pytest.mark.gpu
+def test_bench_json_line(gpu_lib):
+    """A short run on one dense layer: the last stdout line is the JSON
+    record with every key the contract names, consistent with itself."""
+    print("bench.py --workload dense-layer --steps 3 --warmup 1", flush=True)
+    res = subprocess.run([sys.executable, BENCH, "--workload", "dense-layer", "--steps", "3",
+                          "--warmup", "1", "--no-cpu-baseline"],
+                         capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert res.returncode == 0, res.stderr[-2000:]
+    rec = json.loads(res.stdout.strip().splitlines()[-1])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline"):
+        assert key in rec, key
+    assert rec["n_gpus"] == 1 and rec["steps"] == 3 and rec["warmup"] == 1
+    assert rec["unit"] == "GB/s" and rec["higher_is_better"] is True
+    assert "workload" in rec["config"] and rec["config"]["tensors"] == 7
+    roof = rec["roofline"]
+    for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
+        assert key in roof, key
+    assert roof["bound"] == "hbm" and roof["peak"] == 8000.0
+    assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    assert 0 < roof["frac"] < 1
+    # value = algorithmic bytes / wall time per step
+    want = rec["config"]["algorithmic_bytes_per_step"] / (rec["ms_per_step"] * 1e-3) / 1e9
+    assert abs(rec["value"] - want) / want < 1e-3
