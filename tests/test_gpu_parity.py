@@ -648,6 +648,34 @@ def test_grouped_large_tiles_many_tensors(gpu_lib):
         assert_matches_oracle(mats[i], outs[i][0], outs[i][1], 512, 512, f"grouped large [{i}]")
 
 
+@pytest.mark.parametrize("M,N,bm,bn", [(6145, 16384, 6145, 16384),    # 3 chunks per pass-1 item, last item 1
+                                      (4096, 16384, 4096, 16384),    # 2 chunks per item
+                                      (8192, 8192, 4096, 2048)])     # 8 tiles of row runs, 2 per item
+def test_large_tiles_chunk_grouping(gpu_lib, M, N, bm, bn):
+    """Large tiles where pass-1 workgroups take several chunks each (the
+    host's chunks-per-workgroup above 1): single and grouped calls agree,
+    every scale comes from the exact tile maximum, and sampled row bands of
+    each tile match the oracle given that maximum."""
+    say("chunk grouping", M, N, bm, bn)
+    g = torch.Generator(device=DEV).manual_seed(M + N)
+    x = (torch.randn((M, N), generator=g, device=DEV) * 0.03).to(torch.bfloat16)
+    x[M - 1, N - 1] = -2.5                                 # in the last chunk of the last tile
+    q, s = fq.quantize(x, (bm, bn))
+    ((qg, sg),) = fq.quantize_many([x], (bm, bn))
+    assert torch.equal(q.view(torch.uint8), qg.view(torch.uint8))
+    assert torch.equal(s.view(torch.int32), sg.view(torch.int32))
+    assert_scales_match_oracle(x, s, bm, bn, f"chunk grouping {M}x{N}")
+    amax = x.abs().float().view(-(-M // bm), bm, -(-N // bn), bn).amax(dim=(1, 3)).double().cpu().numpy()
+    for ti in range(amax.shape[0]):
+        for tj in range(amax.shape[1]):
+            for r0 in (ti * bm, ti * bm + bm // 2, (ti + 1) * bm - 8):
+                band = x[r0:r0 + 8, tj * bn:(tj + 1) * bn].contiguous()
+                q_ref, _ = oracle.quantize_with_amax(bits_np(band), 8, band.shape[1],
+                                                     np.array([[amax[ti, tj]]]))
+                got = codes_np(q[r0:r0 + 8, tj * bn:(tj + 1) * bn].contiguous())
+                assert np.array_equal(got, q_ref), (ti, tj, r0)
+
+
 def test_per_tensor_vocab_matrix(gpu_lib):
     """One scale for the whole 151937x4096 matrix (1.2 GB): the scale from the
     exact maximum, sampled rows against the oracle, invariants everywhere."""
