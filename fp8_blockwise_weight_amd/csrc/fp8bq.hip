@@ -159,6 +159,14 @@ bool big_tiles(int64_t M, int64_t N, int32_t bm, int32_t bn) {
   return rows * cols > fp8bq::kBigTile;
 }
 
+// Chunks per pass-1 item for about `target` items, between 1 and
+// kChunksPerMax.  Pass 2 does not depend on it.
+fp8bq::Big with_cpm(fp8bq::Big b, int64_t target) {
+  const int64_t per = b.items / target;
+  b.cpm = static_cast<int32_t>(per < 1 ? 1 : (per > fp8bq::kChunksPerMax ? fp8bq::kChunksPerMax : per));
+  return b;
+}
+
 // Describes a sub-matrix at tile phase (rp, cp) for the two-pass kernels.
 fp8bq::Big make_big(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, int32_t rp,
                     int32_t cp, void* q) {
@@ -186,12 +194,9 @@ fp8bq::Big make_big(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn,
     b.cpt = ceil_div(rows_max, rows_per);
   }
   b.items = b.TMl * b.TNl * b.cpt;
-  // Chunks per pass-1 item: enough items to fill the chip, but no more than
-  // kChunksPerMax chunks per item (fewer atomics on one address).
-  const int64_t per = b.items / fp8bq::kMaxItemsTarget;
-  b.cpm = static_cast<int32_t>(per < 1 ? 1 : (per > fp8bq::kChunksPerMax ? fp8bq::kChunksPerMax : per));
+  b.cpm = 1;
   b.pad = 0;
-  return b;
+  return with_cpm(b, fp8bq::kMaxItemsTarget);
 }
 
 // Pass-1 items of a large-tile sub-matrix.
@@ -202,13 +207,16 @@ unsigned grid_capped(int64_t n, int64_t per_block) {
   return static_cast<unsigned>(blocks < 65536 * 16 ? (blocks < 1 ? 1 : blocks) : 65536 * 16);
 }
 
-// Shards: pass 1 with atomic maxima into `amax` (zeroed first).
+// Shards: pass 1 with atomic maxima into `amax` (zeroed first), with fewer,
+// larger items than the slot form: 4096x4096 as one tile took 28 us at
+// ~2048 items and 17 us at ~256 on MI355X.
 void launch_big_amax(const fp8bq::Big& b, float* amax, hipStream_t st) {
-  const int64_t nt = b.TMl * b.TNl;
+  const fp8bq::Big a = with_cpm(b, fp8bq::kAtomicItemsTarget);
+  const int64_t nt = a.TMl * a.TNl;
   hipLaunchKernelGGL(fp8bq::fill_zero, dim3(grid_capped(nt, fp8bq::kThreads)), dim3(fp8bq::kThreads),
                      0, st, reinterpret_cast<uint32_t*>(amax), nt);
-  const int64_t items = big_max_items(b);
-  hipLaunchKernelGGL(fp8bq::big_max<false>, dim3(grid_for(items)), dim3(fp8bq::kThreads), 0, st, b,
+  const int64_t items = big_max_items(a);
+  hipLaunchKernelGGL(fp8bq::big_max<false>, dim3(grid_for(items)), dim3(fp8bq::kThreads), 0, st, a,
                      reinterpret_cast<uint32_t*>(amax), items);
 }
 

@@ -663,8 +663,10 @@ __device__ __forceinline__ bool big_chunk(const Big& b, int64_t tile, int64_t k,
 //     skipped when a coherent read already shows a value at least as large.
 //     Many workgroups folding into one address serialize on it, which is
 //     why whole tensors take the slots.
-constexpr int64_t kChunksPerMax = 16;     // largest b.cpm
-constexpr int64_t kMaxItemsTarget = 2048; // pass-1 items a tensor aims for (8 per CU)
+constexpr int64_t kChunksPerMax = 16;       // largest b.cpm
+constexpr int64_t kMaxItemsTarget = 2048;   // pass-1 items a tensor aims for (8 per CU)
+constexpr int64_t kAtomicItemsTarget = 256; // the same with atomic maxima (1 per CU):
+                                            // fewer workgroups folding into one address
 
 // Pass-1 slots of a whole tensor: the first 4-byte-aligned address of q.
 __host__ __device__ inline uint32_t* big_slots(uint8_t* q) {
