@@ -50,11 +50,38 @@ def algorithmic_bytes(M, N, bm, bn):
     return 3 * M * N + 4 * TM * TN
 
 
+def _code_only(text):
+    """C++ source without comments, whitespace runs collapsed: comment and
+    layout edits leave the kernels, and so the fingerprint, unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"' or c == "'":                     # string or character literal
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_sha():
+    """Fingerprint of the kernel sources' code (comments excluded)."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

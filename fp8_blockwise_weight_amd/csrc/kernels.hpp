@@ -22,9 +22,12 @@
 //     16-byte passes over the tile; N % 8 != 0 or a misaligned pointer,
 //     element by element;
 //   * tiles of more than 65536 elements (e.g. one scale per tensor) and
-//     shards that start inside a tile: two passes over chunks, with the
-//     per-tile maxima folded by atomic max (section "large tiles").
+//     shards that start inside a tile: two passes over chunks of each tile
+//     (section "large tiles"): per-workgroup maxima in slots of q and a
+//     reduce kernel for whole tensors, atomic maxima for shards.
 // Every body computes the same arithmetic, so results never depend on it.
+// The file also holds dequantization (decode(q) * s, section
+// "dequantization") and the final cast on its own.
 //
 // The tile maximum is an integer max over (bits & 0x7FFF): for finite BF16
 // values magnitude order equals bit-pattern order, so this is exact.

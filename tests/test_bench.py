@@ -46,3 +46,18 @@ def test_bench_json_line(gpu_lib):
     # value = algorithmic bytes / wall time per step
     want = rec["config"]["algorithmic_bytes_per_step"] / (rec["ms_per_step"] * 1e-3) / 1e9
     assert abs(rec["value"] - want) / want < 1e-3
+
+
+def test_kernel_fingerprint_ignores_comments_only():
+    """The counter record is tied to the kernels' code: comment and layout
+    edits keep the fingerprint, code edits change it."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    base = 'int f(int a) {  // twice\n  return a * 2; /* doubled */ }\nconst char* s = "//x";\n'
+    same = '// header\nint f(int a) {\n    return a * 2;\n}\nconst char* s = "//x";  /* note */\n'
+    other = 'int f(int a) { return a * 3; }\nconst char* s = "//x";\n'
+    assert bench._code_only(base) == bench._code_only(same)
+    assert bench._code_only(base) != bench._code_only(other)
+    assert bench._code_only('const char* s = "//x";') == 'const char* s = "//x";'
+    assert len(bench.kernel_sha()) == 16
