@@ -53,6 +53,66 @@ def test_c1_matches_oracle_and_closed_forms(gpu_lib):
     assert np.all(codes[128:, 128:] == 0)
 
 
+# ------------------------------------------------------------------ seeded fuzz over every path
+
+def _fuzz_bits(rng, M, N, family):
+    """BF16 bit patterns [M, N] of one value family (all finite)."""
+    if family == "bits":                       # any finite BF16: exponents 0..254
+        b = rng.integers(0, 1 << 16, (M, N), dtype=np.uint32).astype(np.uint16)
+        exp = (b >> 7) & 0xFF
+        b[exp == 0xFF] &= 0x807F                # exponent 255 (Inf/NaN) -> 0
+        return b
+    sigma = {"normal": 10.0 ** rng.uniform(-30, 30), "tiny": 1e-13, "unit": 1.0}[family]
+    v = (rng.standard_normal((M, N)) * sigma).astype(np.float32)
+    if rng.random() < 0.3:
+        v[rng.integers(0, M, max(1, M // 10))] = 0.0      # zero rows
+    b = v.view(np.uint32)
+    b = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)   # RNE to BF16
+    return b
+
+
+def test_seeded_fuzz_all_paths(gpu_lib):
+    """160 seeded random configurations through fp8bq_quantize, each against
+    the oracle bit for bit, then the same tensors per block size through
+    fp8bq_quantize_many (equal to the single calls).  Shapes 1..600 with N
+    8-aligned or not, the three vector block kinds and random blocks up to
+    [300, 300] (register, loop-vector, element and two-pass bodies), x as a
+    misaligned view in a third of the cases, and value families from random
+    finite bit patterns to tiles below eps."""
+    rng = np.random.default_rng(20240607)
+    cases = []
+    for i in range(160):
+        M = int(rng.integers(1, 601))
+        N = int(rng.integers(1, 76)) * 8 if rng.random() < 0.6 else int(rng.integers(1, 601))
+        r = rng.random()
+        if r < 0.35:
+            block = BLOCKS[int(rng.integers(0, 3))]
+        elif r < 0.5:
+            block = (int(rng.integers(256, 301)), int(rng.integers(256, 301)))   # large tiles when M, N allow
+        else:
+            block = (int(rng.integers(1, 301)), int(rng.integers(1, 301)))
+        family = ["normal", "bits", "tiny", "unit"][int(rng.integers(0, 4))]
+        bits = _fuzz_bits(rng, M, N, family)
+        off = int(rng.integers(1, 8)) if rng.random() < 0.33 else 0
+        flat = np.zeros(M * N + 8, dtype=np.uint16)
+        flat[off:off + M * N] = bits.reshape(-1)
+        base = torch.from_numpy(flat.view(np.int16)).to(DEV).view(torch.bfloat16)
+        x = base[off:off + M * N].view(M, N)
+        what = f"fuzz[{i}] {M}x{N} block {block} {family} offset {off}"
+        say(what)
+        q, s = fq.quantize(x, block)
+        assert_matches_oracle(x, q, s, *block, what)
+        cases.append((x, block, q, s))
+    by_block = {}
+    for x, block, q, s in cases:
+        by_block.setdefault(block, []).append((x, q, s))
+    for block, items in by_block.items():
+        outs = fq.quantize_many([x for x, _, _ in items], block)
+        for (x, q, s), (qg, sg) in zip(items, outs):
+            assert torch.equal(qg.view(torch.uint8), q.view(torch.uint8)), block
+            assert torch.equal(sg.view(torch.int32), s.view(torch.int32)), block
+
+
 # ------------------------------------------------------------------ shapes and tails
 
 @pytest.mark.parametrize("bm,bn", BLOCKS)
