@@ -543,6 +543,35 @@ def test_dequant_matches_oracle(gpu_lib, out_dtype):
         assert torch.equal(o2.float(), xh.float())
 
 
+def test_dequant_seeded_fuzz(gpu_lib):
+    """120 seeded random dequantizations (random codes without NaN, random
+    positive scales per tile over 2^-30..2^30) against the oracle, fp32 and
+    BF16: shapes up to 700 x 1600, N and bn multiples of 8 in most cases
+    (the vector kernel, whose row, tile-row and tile-column indices come from
+    multiply-and-shift divisions) and arbitrary otherwise."""
+    rng = np.random.default_rng(4242)
+    for i in range(120):
+        out_dtype = "f32" if i % 2 == 0 else "bf16"
+        tdt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+        vec = rng.random() < 0.75
+        M = int(rng.integers(1, 701))
+        N = int(rng.integers(1, 201)) * 8 if vec else int(rng.integers(1, 1601))
+        bm = int(rng.integers(1, 301))
+        bn = int(rng.integers(1, 41)) * 8 if vec else int(rng.integers(1, 301))
+        TM, TN = -(-M // bm), -(-N // bn)
+        codes = rng.integers(0, 256, (M, N), dtype=np.int64).astype(np.uint8)
+        codes[(codes & 0x7F) == 0x7F] ^= 0x01                  # no NaN codes
+        scales = np.exp2(rng.uniform(-30, 30, (TM, TN))).astype(np.float32)
+        q = torch.from_numpy(codes).to(DEV)
+        s = torch.from_numpy(scales).to(DEV)
+        say("dequant fuzz", i, M, N, (bm, bn), out_dtype)
+        xh = fq.dequantize(q, s, (bm, bn), out_dtype=tdt)
+        want = oracle.dequantize(codes, scales, bm, bn, out_dtype)
+        got = xh.float().cpu().numpy().astype(np.float64)
+        bad = np.nonzero(got != want)
+        assert bad[0].size == 0, (i, M, N, bm, bn, out_dtype, bad[0].size)
+
+
 def test_dequant_roundtrip_bound_layer(gpu_lib):
     """I4 over a whole Qwen3-8B-shaped layer on the GPU: |x - dequant(q)| is
     within half an e4m3 ulp of the scaled value times s (+ fp32 rounding)."""
