@@ -16,7 +16,7 @@ import oracle
 from fp8_blockwise_weight_amd import workloads as wl
 from gpu_helpers import (assert_matches_oracle, assert_properties_gpu,
                          assert_scales_match_oracle, assert_tiles_match_oracle, bits_np,
-                         codes_np, sample_tiles, scales_bits)
+                         codes_np, sample_tiles, scales_bits, tile_amax_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -648,10 +648,15 @@ def test_shards_equal_whole(gpu_lib):
     max, then shard-wise quantization reproduce the whole-matrix bytes."""
     g = torch.Generator(device=DEV).manual_seed(43)
     rng = np.random.default_rng(43)
+    # the last two: large tiles whose maxima pass groups several chunks per
+    # workgroup (one tile per tensor: 4 chunks per item; 1024 x 2000 tiles)
     for M, N, block in [(1000, 3000, (128, 128)), (4097, 1024, (64, 64)), (300, 640, (1, 128)),
-                        (1536, 2048, (128, 128))]:
+                        (1536, 2048, (128, 128)), (4096, 4096, (4096, 4096)),
+                        (3000, 2000, (1024, 2000))]:
         x = (torch.randn((M, N), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
         q_ref, s_ref = fq.quantize(x, block)
+        a = fq.tile_amax(x, block)                          # whole matrix, phase (0, 0)
+        assert np.array_equal(a.cpu().numpy().astype(np.float64), tile_amax_gpu(x, *block))
         for _ in range(4):
             rc = sorted(set(int(v) for v in rng.integers(1, M, rng.integers(1, 5))))
             cc = sorted(set(int(v) for v in rng.integers(1, N, rng.integers(0, 3))))
