@@ -104,7 +104,8 @@ size_t fp8bq_many_workspace_bytes(int32_t count);
 
 /*
  * Quantize a list of BF16 matrices that share one block size, in one kernel
- * launch (the grouped form of the per-weight loop).
+ * launch (the grouped form of the per-weight loop); entries with tiles of
+ * more than 65536 elements add three launches per 128 such entries.
  *   list             HOST array of `count` entries; its contents are captured
  *                    before the call returns (into the kernel arguments, or
  *                    copied into `workspace` on `stream`), so the caller may
@@ -120,8 +121,9 @@ size_t fp8bq_many_workspace_bytes(int32_t count);
  *   stream           hipStream_t (NULL = null stream)
  * Entries with M == 0 or N == 0 are skipped.  Entries whose tiles exceed
  * 65536 elements are quantized by the two-pass kernels (grouped, up to 128
- * entries per launch, before the grouped launch of the others).  Outputs of different entries must not overlap each
- * other or any entry's x (not checked across entries).
+ * entries per launch, before the grouped launch of the others).  Outputs of
+ * different entries must not overlap each other or any entry's x (not
+ * checked across entries).
  * Returns an fp8bq_status; on an argument error nothing is enqueued.
  */
 int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int32_t bn,
