@@ -170,7 +170,9 @@ def main():
     import torch
 
     import fp8_blockwise_weight_amd as fq
+    from fp8_blockwise_weight_amd import build as _build
 
+    _build.ensure_built()  # load what is built; build only when nothing is
     lib = fq.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -53,16 +53,26 @@ def command(out: str = LIB, extra=()) -> list:
 
 def build(verbose: bool = False) -> str:
     """Compile the library (always; a stale .so is replaced atomically)."""
-    tmp = LIB + ".tmp"
+    tmp = f"{LIB}.tmp{os.getpid()}"  # per process: concurrent builds never share a file
     cmd = command(tmp)
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln and ln.strip()]
     if res.returncode != 0:
+        if os.path.exists(tmp):
+            os.remove(tmp)
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
     os.replace(tmp, LIB)
+    return LIB
+
+
+def ensure_built() -> str:
+    """Build the library only when none is there (a fresh checkout); an
+    existing build is loaded as it is."""
+    if not os.path.exists(LIB):
+        return build()
     return LIB
 
 

@@ -16,6 +16,13 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long-running CPU test")
 
 
+def pytest_sessionstart(session):
+    # Load what is built; build only when nothing is (a fresh checkout).
+    from fp8_blockwise_weight_amd import build
+
+    build.ensure_built()
+
+
 @pytest.fixture(scope="session")
 def gpu_lib():
     """The loaded HIP library; GPU tests fail loudly when it is missing."""
