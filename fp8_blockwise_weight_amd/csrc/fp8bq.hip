@@ -340,6 +340,46 @@ void launch_args_kind(const std::vector<Desc>& ds, const std::vector<int64_t>& s
   }
 }
 
+// A table larger than the kernel-argument capacity, without the host-to-device
+// copy: one launch per run of at most kArgsMax tensors whose units fit in 32
+// bits (a single tensor always does).  Serves calls made under graph capture,
+// where a copy from the library's staging memory would be replayed from a
+// buffer the library reuses.
+template <int KIND>
+void launch_args_chunks(const std::vector<Desc>& ds, const std::vector<int64_t>& st, int32_t bm,
+                        int32_t bn, int64_t total, hipStream_t s) {
+  std::vector<Desc> cd;
+  std::vector<int64_t> cs;
+  const size_t n = ds.size();
+  size_t i = 0;
+  while (i < n) {
+    cd.clear();
+    cs.clear();
+    const int64_t base = st[i];
+    size_t j = i;
+    while (j < n && cd.size() < static_cast<size_t>(fp8bq::kArgsMax)) {
+      const int64_t end = j + 1 < n ? st[j + 1] : total;
+      if (!cd.empty() && end - base > INT32_MAX) break;
+      cd.push_back(ds[j]);
+      cs.push_back(st[j] - base);
+      ++j;
+    }
+    const int64_t end = j < n ? st[j] : total;
+    launch_args_kind<KIND>(cd, cs, bm, bn, end - base, s);
+    i = j;
+  }
+}
+
+// False only when the stream is known not to be capturing a graph.
+bool maybe_capturing(hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;
+  }
+  return cs != hipStreamCaptureStatusNone;
+}
+
 // Host copies of a grouped call's table, reused per thread.
 thread_local std::vector<Desc> g_descs;
 thread_local std::vector<int64_t> g_starts;
@@ -463,6 +503,14 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
         case fp8bq::kR128: launch_one<fp8bq::kR128>(d, bm, bn, units, s); break;
         default: launch_one<fp8bq::kGeneral>(d, bm, bn, units, s); break;
       }
+    }
+  } else if (n > 0 && maybe_capturing(s)) {
+    // Under graph capture: several launches with the table in their arguments.
+    switch (kind) {
+      case fp8bq::kT128: launch_args_chunks<fp8bq::kT128>(g_descs, g_starts, bm, bn, total, s); break;
+      case fp8bq::kT64: launch_args_chunks<fp8bq::kT64>(g_descs, g_starts, bm, bn, total, s); break;
+      case fp8bq::kR128: launch_args_chunks<fp8bq::kR128>(g_descs, g_starts, bm, bn, total, s); break;
+      default: launch_args_chunks<fp8bq::kGeneral>(g_descs, g_starts, bm, bn, total, s); break;
     }
   } else if (n > 0) {
     // Larger groups: the table is copied into the workspace on the stream.

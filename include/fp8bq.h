@@ -109,7 +109,12 @@ size_t fp8bq_many_workspace_bytes(int32_t count);
  *   list             HOST array of `count` entries; its contents are captured
  *                    before the call returns (into the kernel arguments, or
  *                    copied into `workspace` on `stream`), so the caller may
- *                    reuse or free it afterwards
+ *                    reuse or free it afterwards.  While `stream` is
+ *                    capturing a graph, a call of more than
+ *                    FP8BQ_MANY_ARGS_MAX entries enqueues no copy: it
+ *                    launches once per run of at most that many entries,
+ *                    each with its table in the kernel arguments (the
+ *                    workspace is then left untouched)
  *   count            number of entries (>= 0)
  *   bm, bn           block size shared by every entry
  *   workspace        device buffer of at least

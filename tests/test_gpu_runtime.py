@@ -60,6 +60,53 @@ def test_graph_capture_replays_match_eager(gpu_lib, block):
     assert_matches_oracle(xs[0], outs[0][0], outs[0][1], *block, "graph replay")
 
 
+@pytest.mark.parametrize("block", [(128, 128), (64, 64), (1, 128), (5, 3)])
+def test_graph_capture_beyond_argument_table(gpu_lib, block):
+    """More tensors than the kernel arguments hold (700), captured in a HIP
+    graph: under capture the call enqueues several launches of at most 512
+    tensors each instead of copying the table into the workspace, and every
+    replay, with eager work in between, equals eager single calls."""
+    g = torch.Generator(device=DEV).manual_seed(29)
+    rng = np.random.default_rng(29)
+    xs = []
+    for _ in range(700):
+        M, N = int(rng.integers(1, 300)), int(rng.choice([8, 64, 136, 256, 264, 7, 99]))
+        xs.append((torch.randn((M, N), generator=g, device=DEV) * 0.03).to(torch.bfloat16))
+    assert fq.workspace_bytes(len(xs)) > 0
+    outs = [(torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=DEV),
+             torch.empty(fq.scale_shape(*x.shape, *block), dtype=torch.float32, device=DEV))
+            for x in xs]
+    ws = torch.empty(fq.workspace_bytes(len(xs)), dtype=torch.uint8, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fq.quantize_many(xs, block, outputs=outs, workspace=ws)   # eager: workspace path
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ws.fill_(0x5A)                                         # the graph must never write it
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fq.quantize_many(xs, block, outputs=outs, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        _say("replay beyond the argument table", block, rep)
+        for x in xs:                                       # eager work between replays
+            x.neg_()
+        for q, s in outs:
+            q.view(torch.uint8).fill_(0xA5)
+            s.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (x, (q, s)) in enumerate(zip(xs, outs)):
+            q1, s1 = fq.quantize(x, block)
+            assert torch.equal(q1.view(torch.uint8), q.view(torch.uint8)), (block, rep, i)
+            assert torch.equal(s1.view(torch.int32), s.view(torch.int32)), (block, rep, i)
+    assert bool((ws == 0x5A).all()), "a captured call copied its table into the workspace"
+    for i in (0, 511, 512, 699):
+        assert_matches_oracle(xs[i], outs[i][0], outs[i][1], *block, f"graph beyond table [{i}]")
+
+
 def test_non_default_streams(gpu_lib):
     """Work is enqueued on the caller's current stream and ordered with it."""
     x = wl.materialize(wl.c2()[0], DEV)
