@@ -662,11 +662,11 @@ int fp8bq_dequantize(const void* q, const float* scale_inv, int64_t M, int64_t N
     if (out_dtype == FP8BQ_OUT_F32) {
       hipLaunchKernelGGL(fp8bq::dequant_vec<fp8bq::kOutF32>, dim3(grid), dim3(fp8bq::kThreads), 0,
                          s, qb, scale_inv, static_cast<int32_t>(gpr), tn, by_gpr, by_bm, by_bn, out,
-                         groups, step_rows, step_cols);
+                         groups, static_cast<int32_t>(M - 1), step_rows, step_cols);
     } else {
       hipLaunchKernelGGL(fp8bq::dequant_vec<fp8bq::kOutBF16>, dim3(grid), dim3(fp8bq::kThreads), 0,
                          s, qb, scale_inv, static_cast<int32_t>(gpr), tn, by_gpr, by_bm, by_bn, out,
-                         groups, step_rows, step_cols);
+                         groups, static_cast<int32_t>(M - 1), step_rows, step_cols);
     }
   } else {
     const int64_t blocks = (static_cast<int64_t>(n) + fp8bq::kThreads - 1) / fp8bq::kThreads;
