@@ -210,26 +210,48 @@ def make_entries(tensors: Sequence, outputs: Sequence) -> ctypes.Array:
     return (TensorEntry * len(tensors)).from_buffer(buf)
 
 
-def _group_outputs(tensors: Sequence, bm: int, bn: int, device) -> List:
+def _group_outputs(tensors: Sequence, bm: int, bn: int, device, entries=None):
     """Outputs for a grouped call: one q buffer and one scale buffer per
-    distinct row length N, cut into per-tensor [M, N] / [TM, TN] views by
-    row (contiguous, disjoint, in input order).  Two allocations per row
-    length instead of two per tensor: for lists of thousands of small
-    matrices the allocations, not the kernel, set the pace."""
+    distinct row length N, holding the tensors' [M, N] / [TM, TN] outputs
+    one after another in input order (contiguous and disjoint).  Two
+    allocations per row length instead of two per tensor: for lists of
+    thousands of small matrices the allocations, not the kernel, set the
+    pace.  Fills ``entries`` (a bytearray of the ``fp8bq_tensor`` array)
+    from the buffers' addresses when given.  Returns a function that cuts
+    the per-tensor views; calling it after the launch lets the device start
+    while the host builds them."""
     import torch
 
     by_n = {}
     for i, x in enumerate(tensors):
-        by_n.setdefault(x.shape[1], []).append(i)
-    outs = [None] * len(tensors)
-    for N, idx in by_n.items():
-        ms = [tensors[i].shape[0] for i in idx]
+        M, N = x.shape
+        g = by_n.get(N)
+        if g is None:
+            by_n[N] = g = ([], [])
+        g[0].append(i)
+        g[1].append(M)
+    plan = []
+    for N, (idx, ms) in by_n.items():
         tms = [-(-m // bm) for m in ms]
+        TN = -(-N // bn)
         qbuf = torch.empty((sum(ms), N), dtype=torch.float8_e4m3fn, device=device)
-        sbuf = torch.empty((sum(tms), -(-N // bn)), dtype=torch.float32, device=device)
-        for i, q, s in zip(idx, qbuf.split(ms), sbuf.split(tms)):
-            outs[i] = (q, s)
-    return outs
+        sbuf = torch.empty((sum(tms), TN), dtype=torch.float32, device=device)
+        if entries is not None:
+            qp, sp = qbuf.data_ptr(), sbuf.data_ptr()
+            for i, m, tm in zip(idx, ms, tms):
+                _ENTRY.pack_into(entries, _ENTRY.size * i, tensors[i].data_ptr(), qp, sp, m, N)
+                qp += m * N
+                sp += 4 * tm * TN
+        plan.append((idx, qbuf, sbuf, ms, tms))
+
+    def views() -> List:
+        outs = [None] * len(tensors)
+        for idx, qbuf, sbuf, ms, tms in plan:
+            for i, q, s in zip(idx, torch.split_with_sizes(qbuf, ms), torch.split_with_sizes(sbuf, tms)):
+                outs[i] = (q, s)
+        return outs
+
+    return views
 
 
 def quantize_many(tensors: Sequence, block_size=(128, 128), outputs: Optional[Sequence] = None,
@@ -248,30 +270,41 @@ def quantize_many(tensors: Sequence, block_size=(128, 128), outputs: Optional[Se
     if not tensors:
         return []
     dev = tensors[0].device
+    index = tensors[0].get_device()
+    bf16 = torch.bfloat16
     for x in tensors:
-        _check_input(x)
-        if x.device != dev:
+        # the common case in one expression; _check_input names what is wrong
+        if not (isinstance(x, torch.Tensor) and x.dtype is bf16 and x.dim() == 2 and x.is_cuda
+                and x.is_contiguous()):
+            _check_input(x)
+        if x.get_device() != index:
             raise ValueError("all tensors of one grouped call must be on the same device")
+    n = len(tensors)
     if outputs is None:
-        outputs = _group_outputs(tensors, bm, bn, dev)
+        entries = bytearray(_ENTRY.size * n)
+        views = _group_outputs(tensors, bm, bn, dev, entries)
+        arr = (TensorEntry * n).from_buffer(entries)
     else:
         outputs = list(outputs)
-        if len(outputs) != len(tensors):
+        if len(outputs) != n:
             raise ValueError("outputs must hold one (q, scale_inv) pair per tensor")
         for x, out in zip(tensors, outputs):
             _check_outputs(out, *x.shape, bm, bn, dev)
-    need = workspace_bytes(len(tensors))
+        views = None
+        arr = make_entries(tensors, outputs)
+    lib = load_library()
+    need = int(lib.fp8bq_many_workspace_bytes(n))
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     elif workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on the tensors' device")
-    arr = make_entries(tensors, outputs)
-    lib = load_library()
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     with torch.cuda.device(dev):
         _check("fp8bq_quantize_many",
-               lib.fp8bq_quantize_many(arr, len(tensors), bm, bn, workspace.data_ptr(),
-                                       workspace.numel() * workspace.element_size(), _stream(dev)))
-    return list(outputs)
+               lib.fp8bq_quantize_many(arr, n, bm, bn, ws_ptr, ws_bytes, _stream(dev)))
+    return views() if views is not None else outputs
 
 
 def dequantize(q, scale_inv, block_size=(128, 128), out_dtype=None, out=None):

@@ -24,6 +24,7 @@ from typing import Callable, Iterable, Iterator, Tuple
 from . import block_shape, quantize_many
 
 SCALE_SUFFIX = "_scale_inv"
+_FP8 = object()  # placeholder for a weight that is being quantized
 
 
 def default_is_fp8(name: str, tensor) -> bool:
@@ -48,21 +49,20 @@ def quant_weights(weights: Iterable[Tuple[str, object]], block_size=(128, 128),
 
     bm, bn = block_shape(block_size)  # raises ValueError when the block size is missing
     dtype = dtype or torch.bfloat16
-    pending = []     # (name, tensor, quantize?) in input order
-    state = {"bytes": 0, "count": 0}
+    pending = []   # (name, tensor) in input order; _FP8 marks a weight in `xs`
+    xs = []        # the FP8 weights of the pending group, in order
+    nbytes = 0
 
     def flush():
+        nonlocal pending, xs, nbytes
         if not pending:
             return
-        items = list(pending)
-        pending.clear()
-        state["bytes"] = state["count"] = 0
-        xs = [x for _, x, fp8 in items if fp8]
-        outs = iter(quantize_many(xs, (bm, bn)) if xs else [])
-        del xs
-        items = [(name, None if fp8 else x, fp8) for name, x, fp8 in items]  # drop BF16 inputs
-        for name, x, fp8 in items:
-            if not fp8:
+        items, group = pending, xs
+        pending, xs, nbytes = [], [], 0
+        outs = iter(quantize_many(group, (bm, bn)) if group else ())
+        del group      # the BF16 inputs go once the launch is enqueued
+        for name, x in items:
+            if x is not _FP8:
                 yield name, x
                 continue
             q, s = next(outs)
@@ -71,14 +71,14 @@ def quant_weights(weights: Iterable[Tuple[str, object]], block_size=(128, 128),
 
     for name, t in weights:
         if not is_fp8(name, t):
-            pending.append((name, t, False))
-            if not state["count"]:
+            pending.append((name, t))
+            if not xs:
                 yield from flush()   # nothing to wait for
             continue
-        x = t if (t.dtype == dtype and t.is_contiguous()) else t.to(dtype).contiguous()
-        pending.append((name, x, True))
-        state["count"] += 1
-        state["bytes"] += x.numel() * x.element_size()
-        if state["count"] >= group_max or state["bytes"] >= group_bytes:
+        x = t if (t.dtype is dtype and t.is_contiguous()) else t.to(dtype).contiguous()
+        pending.append((name, _FP8))
+        xs.append(x)
+        nbytes += x.numel() * x.element_size()
+        if len(xs) >= group_max or nbytes >= group_bytes:
             yield from flush()
     yield from flush()

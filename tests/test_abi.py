@@ -232,12 +232,18 @@ def test_group_outputs_layout():
 
     shapes = [(5, 8), (3, 16), (0, 8), (7, 8), (2, 0), (130, 16), (1, 24)]
     xs = [torch.empty(sh, dtype=torch.bfloat16) for sh in shapes]
-    outs = fq._group_outputs(xs, 4, 8, torch.device("cpu"))
+    entries = bytearray(ctypes.sizeof(fq.TensorEntry) * len(xs))
+    outs = fq._group_outputs(xs, 4, 8, torch.device("cpu"), entries)()
+    table = (fq.TensorEntry * len(xs)).from_buffer(entries)
     spans = []
-    for x, (q, s) in zip(xs, outs):
+    for x, (q, s), e in zip(xs, outs, table):
         assert q.shape == x.shape and q.dtype == torch.float8_e4m3fn and q.is_contiguous()
         assert tuple(s.shape) == fq.scale_shape(*x.shape, 4, 8)
         assert s.dtype == torch.float32 and s.is_contiguous()
+        # the table the library receives points at exactly these views
+        assert (e.x or 0, e.M, e.N) == (x.data_ptr(), x.shape[0], x.shape[1])
+        if x.numel():
+            assert (e.q, e.scale_inv) == (q.data_ptr(), s.data_ptr())
         for t in (q, s):
             if t.numel():
                 spans.append((t.data_ptr(), t.data_ptr() + t.numel() * t.element_size()))
