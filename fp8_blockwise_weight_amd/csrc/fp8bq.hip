@@ -230,6 +230,44 @@ void launch_big_quant(const fp8bq::Big& b, const float* amax, float* scale_inv, 
                      dim3(fp8bq::kThreads), 0, st, amax, scale_inv, nt);
 }
 
+// Shards whose tiles hold at most kRegTile elements and whose tile columns
+// start on 8-element boundaries take the one-workgroup-per-tile kernels
+// (maxima stored directly, quantize and scales in one launch).
+bool shard_small_ok(const fp8bq::Big& b) {
+  const int64_t rows = b.M < b.bm ? b.M : b.bm;
+  const int64_t cols = b.N < b.bn ? b.N : b.bn;
+  return b.vec != 0 && (b.bn % 8) == 0 && (b.col_phase % 8) == 0 && rows * cols <= fp8bq::kRegTile;
+}
+
+// One-row tiles of at most 128 columns take 64-row units (16 row-tiles per
+// wave) instead of one workgroup per tile.
+bool shard_rows_ok(const fp8bq::Big& b) { return shard_small_ok(b) && b.bm == 1 && b.bn <= 128; }
+
+// Pass 0: amax of every local tile into `out`.  Pass 1: quantize with the
+// given `amax` and write the scales to `out` (which may be `amax`).
+void launch_shard_small(int pass, const fp8bq::Big& b, const float* amax, float* out,
+                        hipStream_t st) {
+  if (shard_rows_ok(b)) {
+    const int64_t units = ceil_div(b.M, 64) * b.TNl;
+    if (pass == 0) {
+      hipLaunchKernelGGL(fp8bq::shard_rows<0>, dim3(grid_for(units)), dim3(fp8bq::kThreads), 0, st,
+                         b, amax, out, units);
+    } else {
+      hipLaunchKernelGGL(fp8bq::shard_rows<1>, dim3(grid_for(units)), dim3(fp8bq::kThreads), 0, st,
+                         b, amax, out, units);
+    }
+    return;
+  }
+  const int64_t tiles = b.TMl * b.TNl;
+  if (pass == 0) {
+    hipLaunchKernelGGL(fp8bq::shard_small<0>, dim3(grid_for(tiles)), dim3(fp8bq::kThreads), 0, st,
+                       b, amax, out, tiles);
+  } else {
+    hipLaunchKernelGGL(fp8bq::shard_small<1>, dim3(grid_for(tiles)), dim3(fp8bq::kThreads), 0, st,
+                       b, amax, out, tiles);
+  }
+}
+
 // A whole tensor's pass-1 slots fit in its q buffer (from the first
 // 4-byte-aligned byte).  Always true for tiles of more than kBigTile
 // elements, since a slot covers at least one chunk; checked anyway.
@@ -558,7 +596,11 @@ int fp8bq_tile_amax(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn,
   if (st != FP8BQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  launch_big_amax(b, amax, s);
+  if (shard_small_ok(b)) {
+    launch_shard_small(0, b, nullptr, amax, s);
+  } else {
+    launch_big_amax(b, amax, s);
+  }
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
 }
@@ -594,7 +636,11 @@ int fp8bq_quantize_amax(const void* x, int64_t M, int64_t N, int32_t bm, int32_t
   if (st != FP8BQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  launch_big_quant(b, amax, scale_inv, s);
+  if (shard_small_ok(b)) {
+    launch_shard_small(1, b, amax, scale_inv, s);
+  } else {
+    launch_big_quant(b, amax, scale_inv, s);
+  }
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
 }

@@ -828,6 +828,142 @@ __global__ __launch_bounds__(kThreads) void big_group_quant(const BigGroupArgs<C
 }
 
 // out[i] = 0 for i < n.
+// ---------------------------------------------------------------- small tiles of shards
+//
+// Shards whose tiles hold at most kRegTile elements, with tile columns that
+// start on 8-element boundaries inside the shard (x 16-byte and q 8-byte
+// aligned; N, bn and col_phase multiples of 8).  One workgroup owns one
+// local tile, so pass 1 stores the tile's maximum directly (no atomics, no
+// zero fill) and pass 2 quantizes with the given maximum and stores the
+// scale (no finalize launch).  The tile's part inside the shard sits in
+// registers, 16-byte vector v = (row v / (cols/8), 8-column group v % (cols/8)),
+// as in reg_tile.
+
+// PASS 0: out[tile] = max |x| over the tile's part (fp32 of the BF16
+// magnitude).  PASS 1: quantize with a = amax[tile], out[tile] = s.  `amax`
+// may be `out` itself: every thread takes a from LDS after a barrier, so the
+// tile's entry is read before thread 0 overwrites it.
+template <int PASS>
+__device__ __forceinline__ void shard_small_tile(const Big& b, int64_t tile, const float* amax,
+                                                 float* out, uint32_t* red) {
+  const int t = threadIdx.x;
+  const int64_t ti = tile / b.TNl;
+  const int64_t tj = tile - ti * b.TNl;
+  int64_t r0, r1, c0, c1;
+  big_rect(b, ti, tj, r0, r1, c0, c1);
+  const uint32_t vpr = (uint32_t)(c1 - c0) / 8;
+  const uint32_t nvec = (uint32_t)(r1 - r0) * vpr;  // <= kRegTile / 8 = 8 per thread
+  const size_t base = (size_t)r0 * b.N + c0;
+  const FP8BQ_GLOBAL uint16_t* x = (const FP8BQ_GLOBAL uint16_t*)(b.x + base);
+  float sc = 0.0f, r = 0.0f;
+  if (PASS == 1) {
+    if (t == 0) red[4] = __float_as_uint(((const FP8BQ_GLOBAL float*)amax)[tile]);
+  }
+  u32x4 v[8];
+  size_t off[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t vi = (uint32_t)t + (uint32_t)k * kThreads;
+    if (vi < nvec) {
+      const uint32_t rr = vi / vpr;
+      off[k] = (size_t)rr * b.N + (size_t)(vi - rr * vpr) * 8;
+      v[k] = __builtin_nontemporal_load((const FP8BQ_GLOBAL u32x4*)(x + off[k]));
+    } else {
+      v[k] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  if (PASS == 0) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = pk_max_u16(m, fold_abs(v[k]));
+    m = max16(halves_max(m));
+    const uint32_t wm = rows_max<0>(m);
+    if ((t & 63) == 0) red[t >> 6] = wm;
+    __syncthreads();
+    const uint32_t tm = max(max(red[0], red[1]), max(red[2], red[3]));
+    if (t == 0) ((FP8BQ_GLOBAL float*)out)[tile] = __uint_as_float(tm << 16);
+  } else {
+    __syncthreads();
+    tile_scale_f(__uint_as_float(red[4]), sc, r);
+    FP8BQ_GLOBAL uint8_t* q = (FP8BQ_GLOBAL uint8_t*)(b.q + base);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t vi = (uint32_t)t + (uint32_t)k * kThreads;
+      if (vi < nvec) __builtin_nontemporal_store(quant8(v[k], r), (FP8BQ_GLOBAL u32x2*)(q + off[k]));
+    }
+    if (t == 0) ((FP8BQ_GLOBAL float*)out)[tile] = sc;
+  }
+}
+
+// Shards with one-row tiles of at most 128 columns ([1, bn], bn <= 128 and a
+// multiple of 8; the row phase is then 0): a workgroup takes 64 rows of one
+// tile column, as the [1,128] unit does.  Lane `c` of each 16-lane DPP row
+// holds columns 8c..8c+7 of the tile, so a row-tile's maximum is reduced
+// inside its DPP row; in pass 2 each lane computes the scale of one of its 4
+// row-tiles and the quad shares the reciprocals.  A row-tile's given maximum
+// is read by the lanes of its quad before the one lane that writes its
+// scale does, so `amax` may be `out`.
+template <int PASS>
+__device__ __forceinline__ void shard_rows_unit(const Big& b, int64_t u, const float* amax,
+                                                float* out) {
+  const int t = threadIdx.x;
+  const int chunk = t & 15;
+  const int prow = t >> 4;
+  const int64_t rb = u / b.TNl;
+  const int64_t tj = u - rb * b.TNl;
+  int64_t c0 = tj * b.bn - b.col_phase;
+  int64_t c1 = c0 + b.bn;
+  c0 = c0 < 0 ? 0 : c0;
+  c1 = c1 > b.N ? b.N : c1;
+  const int64_t col = c0 + chunk * 8;
+  const bool col_ok = col < c1;
+  const int64_t row0 = rb * 64 + prow;
+  u32x4 v[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t row = row0 + k * 16;
+    v[k] = (col_ok && row < b.M)
+               ? __builtin_nontemporal_load((const FP8BQ_GLOBAL u32x4*)(b.x + row * b.N + col))
+               : u32x4{0u, 0u, 0u, 0u};
+  }
+  if constexpr (PASS == 0) {
+    static_for<4>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      const uint32_t m = max16(halves_max(fold_abs(v[k])));
+      const int64_t row = row0 + k * 16;
+      if (chunk == 0 && row < b.M) ((FP8BQ_GLOBAL float*)out)[row * b.TNl + tj] = __uint_as_float(m << 16);
+    });
+  } else {
+    const int mine = chunk & 3;
+    const int64_t rm = row0 + mine * 16;
+    const float a = rm < b.M ? ((const FP8BQ_GLOBAL float*)amax)[rm * b.TNl + tj] : 0.0f;
+    float ssel, rsel;
+    tile_scale_f(a, ssel, rsel);
+    static_for<4>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      const float r = quad_bcast<k>(rsel);
+      const int64_t row = row0 + k * 16;
+      if (col_ok && row < b.M) {
+        __builtin_nontemporal_store(quant8(v[k], r), (FP8BQ_GLOBAL u32x2*)(b.q + row * b.N + col));
+      }
+    });
+    if (chunk < 4 && rm < b.M) ((FP8BQ_GLOBAL float*)out)[rm * b.TNl + tj] = ssel;
+  }
+}
+
+template <int PASS>
+__global__ __launch_bounds__(kThreads) void shard_rows(Big b, const float* amax, float* out,
+                                                       int64_t units) {
+  for_each_unit(units, [&](int64_t u) { shard_rows_unit<PASS>(b, u, amax, out); });
+}
+
+template <int PASS>
+__global__ __launch_bounds__(kThreads) void shard_small(Big b, const float* amax, float* out,
+                                                        int64_t tiles) {
+  __shared__ uint32_t red[8];
+  for_each_unit(tiles, [&](int64_t tile) { shard_small_tile<PASS>(b, tile, amax, out, red); });
+}
+
 __global__ __launch_bounds__(kThreads) void fill_zero(uint32_t* __restrict__ out, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {

@@ -643,6 +643,39 @@ def test_tile_amax_and_quantize_amax_match_oracle(gpu_lib):
             assert np.array_equal(scales_bits(s), scales_bits(s_ref))
 
 
+def test_shard_small_tile_kernels(gpu_lib):
+    """Shards whose tiles hold at most 16,384 elements and whose tile columns
+    start on 8-element boundaries (one workgroup per tile, or 64 one-row
+    tiles per workgroup for [1, <=128] blocks: maxima stored directly,
+    quantize and scales in one launch), at random row phases and 8-aligned
+    column phases; also with the maxima converted in place (amax passed as
+    scale_inv)."""
+    g = torch.Generator(device=DEV).manual_seed(47)
+    rng = np.random.default_rng(47)
+    for M, N, block in [(300, 520, (128, 128)), (1000, 3000, (64, 64)), (257, 384, (32, 128)),
+                        (129, 256, (1, 128)), (50, 64, (8, 8)), (2000, 1024, (128, 64)),
+                        (3, 4096, (2, 4096)), (127, 8, (127, 8)), (300, 1000, (1, 64)),
+                        (17, 40, (1, 8)), (70, 1024, (1, 120))]:
+        bm, bn = block
+        for _ in range(3):
+            ph = (int(rng.integers(bm)), 8 * int(rng.integers(bn // 8)))
+            say("small-tile shard", M, N, block, ph)
+            x = (torch.randn((M, N), generator=g, device=DEV) * 0.05).to(torch.bfloat16)
+            xb = bits_np(x)
+            a = fq.tile_amax(x, block, ph)
+            a_ref = oracle.tile_amax(xb, bm, bn, *ph)
+            assert np.array_equal(a.cpu().numpy().astype(np.float64), a_ref), (M, N, block, ph)
+            q, s = fq.quantize_with_amax(x, a, block, ph)
+            q_ref, s_ref = oracle.quantize_with_amax(xb, bm, bn, a_ref, *ph)
+            assert np.array_equal(codes_np(q), q_ref), (M, N, block, ph)
+            assert np.array_equal(scales_bits(s), scales_bits(s_ref)), (M, N, block, ph)
+            a2 = a.clone()
+            q2 = torch.empty_like(q)
+            fq.quantize_with_amax(x, a2, block, ph, out=(q2, a2))    # maxima -> scales in place
+            assert torch.equal(q2.view(torch.uint8), q.view(torch.uint8))
+            assert torch.equal(a2.view(torch.int32), s.view(torch.int32))
+
+
 def test_shards_equal_whole(gpu_lib):
     """Cuts anywhere (inside tiles too): shard-wise maxima, exchanged as a
     max, then shard-wise quantization reproduce the whole-matrix bytes."""
