@@ -147,10 +147,14 @@ def main():
     ap.add_argument("--workload", default="dense")
     ap.add_argument("--block", default=None, help="bm,bn for the ragged/vocab workloads")
     ap.add_argument("--op", default="quantize",
-                    choices=["quantize", "dequant-f32", "dequant-bf16", "stream"],
+                    choices=["quantize", "dequant-f32", "dequant-bf16", "stream", "shard"],
                     help="quantize (default); time fp8bq_dequantize on the quantized workload; "
-                         "or time the streaming quant_weights loop over the workload in model "
-                         "order with norm weights passed through")
+                         "time the streaming quant_weights loop over the workload in model "
+                         "order with norm weights passed through; or treat every tensor as a "
+                         "shard at --phase and time fp8bq_tile_amax + fp8bq_quantize_amax")
+    ap.add_argument("--phase", default=None,
+                    help="row,col tile phase of each shard for --op shard (default bm/2,0: "
+                         "row cuts in the middle of a tile row)")
     ap.add_argument("--per-tensor", action="store_true",
                     help="also time one fp8bq_quantize call per tensor (HIP events per call)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -253,6 +257,9 @@ def main():
 
     if args.op == "stream":
         time_stream(keep, groups, bm, bn, args, desc)
+        return
+    if args.op == "shard":
+        time_shard(lib, keep, groups, bm, bn, args, stream, sptr, desc)
         return
     if args.op != "quantize":
         time_dequant(lib, keep, groups, bm, bn, args, stream, sptr, desc)
@@ -362,6 +369,58 @@ def time_dequant(lib, keep, groups, bm, bn, args, stream, sptr, desc):
                       "bytes_per_step": nbytes, "ms_per_step": round(ms, 4),
                       "GBps": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}),
           flush=True)
+
+
+def time_shard(lib, keep, groups, bm, bn, args, stream, sptr, desc):
+    """Every tensor of the workload as a shard at a tile phase: per tensor,
+    fp8bq_tile_amax (the shard's partial maxima; the exchange between shards
+    would sit here) then fp8bq_quantize_amax with the maxima turned into the
+    scales in place.  Reports GB/s of the bytes the two passes move (x read
+    twice, q written, maxima and scales) and of the quantizer's algorithmic
+    bytes."""
+    import torch
+
+    import fp8_blockwise_weight_amd as fq
+
+    rp, cp = (int(v) for v in args.phase.split(",")) if args.phase else (bm // 2, 0)
+    items = []
+    moved = algorithmic = 0
+    for (xs, outs), specs in zip(keep, groups):
+        for x, (q, _), sp in zip(xs, outs, specs):
+            tm, tn = fq.local_grid(sp.M, sp.N, bm, bn, (rp, cp))
+            a = torch.empty((tm, tn), dtype=torch.float32, device=x.device)
+            items.append((sp, x, q, a))
+            moved += 5 * sp.M * sp.N + 3 * 4 * tm * tn
+            algorithmic += 3 * sp.M * sp.N + 4 * tm * tn
+
+    def step():
+        for sp, x, q, a in items:
+            st = lib.fp8bq_tile_amax(x.data_ptr(), sp.M, sp.N, bm, bn, rp, cp, a.data_ptr(), sptr)
+            if st == 0:
+                st = lib.fp8bq_quantize_amax(x.data_ptr(), sp.M, sp.N, bm, bn, rp, cp, a.data_ptr(),
+                                             q.data_ptr(), a.data_ptr(), sptr)
+            if st != 0:
+                raise RuntimeError(f"shard path failed: {st}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - w0) * 1e3 / args.steps
+    gbs = moved / (ms * 1e-3) / 1e9
+    alg = algorithmic / (ms * 1e-3) / 1e9
+    log(f"shard at phase ({rp},{cp}): {2 * len(items)} launches/step, wall {ms:.3f} ms/step; "
+        f"{gbs:.1f} GB/s moved = {100 * gbs / HBM_PEAK_GBS:.1f}% of peak, "
+        f"{alg:.1f} GB/s algorithmic = {100 * alg / HBM_PEAK_GBS:.1f}%")
+    print(json.dumps({"op": "shard", "workload": desc, "phase": [rp, cp],
+                      "launches_per_step": 2 * len(items), "bytes_moved_per_step": moved,
+                      "algorithmic_bytes_per_step": algorithmic, "ms_per_step": round(ms, 4),
+                      "GBps_moved": round(gbs, 1), "pct_of_hbm_peak_moved": round(100 * gbs / HBM_PEAK_GBS, 2),
+                      "GBps_algorithmic": round(alg, 1),
+                      "pct_of_hbm_peak_algorithmic": round(100 * alg / HBM_PEAK_GBS, 2)}), flush=True)
 
 
 def time_stream(keep, groups, bm, bn, args, desc):

@@ -48,6 +48,30 @@ def test_bench_json_line(gpu_lib):
     assert abs(rec["value"] - want) / want < 1e-3
 
 
+@pytest.mark.gpu
+def test_bench_shard_mode(gpu_lib):
+    """--op shard on one dense layer: every tensor as a shard at a tile phase
+    through tile_amax and quantize_amax; the record's byte counts follow the
+    two-pass formula."""
+    print("bench.py --workload dense-layer --op shard --phase 64,0", flush=True)
+    res = subprocess.run([sys.executable, BENCH, "--workload", "dense-layer", "--op", "shard",
+                          "--phase", "64,0", "--steps", "2", "--warmup", "1", "--no-cpu-baseline"],
+                         capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert res.returncode == 0, res.stderr[-2000:]
+    rec = json.loads(res.stdout.strip().splitlines()[-1])
+    assert rec["op"] == "shard" and rec["phase"] == [64, 0] and rec["launches_per_step"] == 14
+    sys.path.insert(0, ROOT)
+    from fp8_blockwise_weight_amd import workloads as wl
+
+    moved = alg = 0
+    for sp in wl.c2():
+        tm, tn = -(-(64 + sp.M) // 128), -(-sp.N // 128)
+        moved += 5 * sp.M * sp.N + 12 * tm * tn
+        alg += 3 * sp.M * sp.N + 4 * tm * tn
+    assert rec["bytes_moved_per_step"] == moved and rec["algorithmic_bytes_per_step"] == alg
+    assert 0 < rec["pct_of_hbm_peak_moved"] < 100
+
+
 def test_kernel_fingerprint_ignores_comments_only():
     """The counter record is tied to the kernels' code: comment and layout
     edits keep the fingerprint, code edits change it."""
