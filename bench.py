@@ -151,7 +151,8 @@ def main():
                     help="quantize (default); time fp8bq_dequantize on the quantized workload; "
                          "time the streaming quant_weights loop over the workload in model "
                          "order with norm weights passed through; or treat every tensor as a "
-                         "shard at --phase and time fp8bq_tile_amax + fp8bq_quantize_amax")
+                         "shard at --phase and time fp8bq_tile_amax_many + "
+                         "fp8bq_quantize_amax_many per group")
     ap.add_argument("--phase", default=None,
                     help="row,col tile phase of each shard for --op shard (default bm/2,0: "
                          "row cuts in the middle of a tile row)")
@@ -372,33 +373,37 @@ def time_dequant(lib, keep, groups, bm, bn, args, stream, sptr, desc):
 
 
 def time_shard(lib, keep, groups, bm, bn, args, stream, sptr, desc):
-    """Every tensor of the workload as a shard at a tile phase: per tensor,
-    fp8bq_tile_amax (the shard's partial maxima; the exchange between shards
-    would sit here) then fp8bq_quantize_amax with the maxima turned into the
-    scales in place.  Reports GB/s of the bytes the two passes move (x read
-    twice, q written, maxima and scales) and of the quantizer's algorithmic
-    bytes."""
+    """Every tensor of the workload as a shard at a tile phase: per group of
+    the workload, fp8bq_tile_amax_many (the shards' partial maxima; the
+    exchange between shards would sit here) then fp8bq_quantize_amax_many
+    with the maxima turned into the scales in place.  Reports GB/s of the
+    bytes the two passes move (x read twice, q written, maxima and scales)
+    and of the quantizer's algorithmic bytes."""
     import torch
 
     import fp8_blockwise_weight_amd as fq
 
     rp, cp = (int(v) for v in args.phase.split(",")) if args.phase else (bm // 2, 0)
-    items = []
+    tables = []
+    hold = []
     moved = algorithmic = 0
     for (xs, outs), specs in zip(keep, groups):
-        for x, (q, _), sp in zip(xs, outs, specs):
+        arr = (fq.ShardEntry * len(xs))()
+        for e, x, (q, _), sp in zip(arr, xs, outs, specs):
             tm, tn = fq.local_grid(sp.M, sp.N, bm, bn, (rp, cp))
             a = torch.empty((tm, tn), dtype=torch.float32, device=x.device)
-            items.append((sp, x, q, a))
+            hold.append(a)
+            e.x, e.q, e.amax, e.scale_inv = x.data_ptr(), q.data_ptr(), a.data_ptr(), a.data_ptr()
+            e.M, e.N, e.row_phase, e.col_phase = sp.M, sp.N, rp, cp
             moved += 5 * sp.M * sp.N + 3 * 4 * tm * tn
             algorithmic += 3 * sp.M * sp.N + 4 * tm * tn
+        tables.append((arr, len(xs)))
 
     def step():
-        for sp, x, q, a in items:
-            st = lib.fp8bq_tile_amax(x.data_ptr(), sp.M, sp.N, bm, bn, rp, cp, a.data_ptr(), sptr)
+        for arr, n in tables:
+            st = lib.fp8bq_tile_amax_many(arr, n, bm, bn, sptr)
             if st == 0:
-                st = lib.fp8bq_quantize_amax(x.data_ptr(), sp.M, sp.N, bm, bn, rp, cp, a.data_ptr(),
-                                             q.data_ptr(), a.data_ptr(), sptr)
+                st = lib.fp8bq_quantize_amax_many(arr, n, bm, bn, sptr)
             if st != 0:
                 raise RuntimeError(f"shard path failed: {st}")
 
@@ -412,11 +417,11 @@ def time_shard(lib, keep, groups, bm, bn, args, stream, sptr, desc):
     ms = (time.perf_counter() - w0) * 1e3 / args.steps
     gbs = moved / (ms * 1e-3) / 1e9
     alg = algorithmic / (ms * 1e-3) / 1e9
-    log(f"shard at phase ({rp},{cp}): {2 * len(items)} launches/step, wall {ms:.3f} ms/step; "
+    log(f"shard at phase ({rp},{cp}): {2 * len(tables)} grouped calls/step, wall {ms:.3f} ms/step; "
         f"{gbs:.1f} GB/s moved = {100 * gbs / HBM_PEAK_GBS:.1f}% of peak, "
         f"{alg:.1f} GB/s algorithmic = {100 * alg / HBM_PEAK_GBS:.1f}%")
     print(json.dumps({"op": "shard", "workload": desc, "phase": [rp, cp],
-                      "launches_per_step": 2 * len(items), "bytes_moved_per_step": moved,
+                      "calls_per_step": 2 * len(tables), "bytes_moved_per_step": moved,
                       "algorithmic_bytes_per_step": algorithmic, "ms_per_step": round(ms, 4),
                       "GBps_moved": round(gbs, 1), "pct_of_hbm_peak_moved": round(100 * gbs / HBM_PEAK_GBS, 2),
                       "GBps_algorithmic": round(alg, 1),

@@ -39,6 +39,8 @@ EXPORTS = (
     "fp8bq_dequantize",
     "fp8bq_tile_amax",
     "fp8bq_quantize_amax",
+    "fp8bq_tile_amax_many",
+    "fp8bq_quantize_amax_many",
     "fp8bq_status_string",
     "fp8bq_last_hip_error",
 )
@@ -62,6 +64,21 @@ class Fp8bqError(RuntimeError):
         self.hip_error = hip_error
         text = load_library().fp8bq_status_string(status).decode()
         super().__init__(f"{where}: {text} (status {status}, hip error {hip_error})")
+
+
+class ShardEntry(ctypes.Structure):
+    """``fp8bq_shard`` of include/fp8bq.h (56 bytes, no padding)."""
+
+    _fields_ = [
+        ("x", ctypes.c_void_p),
+        ("q", ctypes.c_void_p),
+        ("amax", ctypes.c_void_p),
+        ("scale_inv", ctypes.c_void_p),
+        ("M", ctypes.c_int64),
+        ("N", ctypes.c_int64),
+        ("row_phase", ctypes.c_int32),
+        ("col_phase", ctypes.c_int32),
+    ]
 
 
 _lib = None
@@ -92,6 +109,9 @@ def load_library() -> ctypes.CDLL:
     lib.fp8bq_quantize_amax.argtypes = [c_vp, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_vp,
                                         c_vp, c_vp, c_vp]
     lib.fp8bq_quantize_amax.restype = ctypes.c_int
+    for name in ("fp8bq_tile_amax_many", "fp8bq_quantize_amax_many"):
+        getattr(lib, name).argtypes = [ctypes.POINTER(ShardEntry), c_i32, c_i32, c_i32, c_vp]
+        getattr(lib, name).restype = ctypes.c_int
     lib.fp8bq_encode_e4m3.argtypes = [c_vp, c_vp, c_i64, c_vp]
     lib.fp8bq_encode_e4m3.restype = ctypes.c_int
     lib.fp8bq_status_string.argtypes = [ctypes.c_int]
@@ -404,6 +424,72 @@ def quantize_with_amax(x, amax, block_size=(128, 128), phase=(0, 0), out=None):
     return q, s
 
 
+def _shard_table(xs, phases, qs, amaxs, scales) -> ctypes.Array:
+    arr = (ShardEntry * len(xs))()
+    for e, x, ph, q, a, s in zip(arr, xs, phases, qs, amaxs, scales):
+        e.x, e.amax = x.data_ptr(), a.data_ptr()
+        e.q = q.data_ptr() if q is not None else None
+        e.scale_inv = s.data_ptr() if s is not None else None
+        e.M, e.N = x.shape
+        e.row_phase, e.col_phase = ph
+    return arr
+
+
+def _shard_inputs(xs, block_size, phases):
+    bm, bn = block_shape(block_size)
+    xs = list(xs)
+    phases = [tuple(int(v) for v in p) for p in (phases if phases is not None else [(0, 0)] * len(xs))]
+    if len(phases) != len(xs):
+        raise ValueError("phases must hold one (row_phase, col_phase) per shard")
+    dev = xs[0].device if xs else None
+    for x in xs:
+        _check_input(x)
+        if x.device != dev:
+            raise ValueError("all shards of one grouped call must be on the same device")
+    grids = [local_grid(*x.shape, bm, bn, p) for x, p in zip(xs, phases)]
+    return bm, bn, xs, phases, dev, grids
+
+
+def tile_amax_many(xs: Sequence, block_size=(128, 128), phases=None) -> List:
+    """``tile_amax`` of every shard of a list (one block size), in grouped launches."""
+    import torch
+
+    bm, bn, xs, phases, dev, grids = _shard_inputs(xs, block_size, phases)
+    if not xs:
+        return []
+    amaxs = [torch.empty(g, dtype=torch.float32, device=dev) for g in grids]
+    arr = _shard_table(xs, phases, [None] * len(xs), amaxs, [None] * len(xs))
+    with torch.cuda.device(dev):
+        _check("fp8bq_tile_amax_many",
+               load_library().fp8bq_tile_amax_many(arr, len(xs), bm, bn, _stream(dev)))
+    return amaxs
+
+
+def quantize_with_amax_many(xs: Sequence, amaxs: Sequence, block_size=(128, 128),
+                            phases=None) -> List:
+    """``quantize_with_amax`` of every shard of a list, in grouped launches.
+    Returns ``(q, scale_inv)`` pairs in input order."""
+    import torch
+
+    bm, bn, xs, phases, dev, grids = _shard_inputs(xs, block_size, phases)
+    amaxs = list(amaxs)
+    if len(amaxs) != len(xs):
+        raise ValueError("amaxs must hold one maxima tensor per shard")
+    if not xs:
+        return []
+    for a, g in zip(amaxs, grids):
+        _check_buffer(a, g, 4, dev, "amax")
+        if a.dtype != torch.float32:
+            raise TypeError("amax must be float32")
+    qs = [torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=dev) for x in xs]
+    scales = [torch.empty(g, dtype=torch.float32, device=dev) for g in grids]
+    arr = _shard_table(xs, phases, qs, amaxs, scales)
+    with torch.cuda.device(dev):
+        _check("fp8bq_quantize_amax_many",
+               load_library().fp8bq_quantize_amax_many(arr, len(xs), bm, bn, _stream(dev)))
+    return list(zip(qs, scales))
+
+
 def encode_e4m3(y):
     """The final cast alone: float32 GPU tensor -> e4m3fn codes (uint8), clamped to +-448."""
     import torch
@@ -420,6 +506,7 @@ def encode_e4m3(y):
 
 __all__ = [
     "EXPORTS", "Fp8bqError", "TensorEntry", "block_shape", "dequantize", "encode_e4m3",
-    "load_library", "local_grid", "quantize_with_amax", "tile_amax",
+    "load_library", "local_grid", "quantize_with_amax", "quantize_with_amax_many", "tile_amax",
+    "tile_amax_many", "ShardEntry",
     "make_entries", "quantize", "quantize_many", "scale_shape", "workspace_bytes",
 ]

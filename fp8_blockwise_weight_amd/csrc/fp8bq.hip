@@ -433,6 +433,133 @@ size_t descs_bytes(int32_t count) { return align_up(sizeof(Desc) * static_cast<s
 // Host staging of one grouped call's descriptor table, reused per thread.
 thread_local std::vector<unsigned char> g_stage;
 
+// Checks one shard call's arguments (QUANT: fp8bq_quantize_amax, else
+// fp8bq_tile_amax) before any HIP call and describes the shard in *b.
+// *empty is set for M == 0 or N == 0, which is not an error.
+int check_shard(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, int32_t row_phase,
+                int32_t col_phase, const float* amax, void* q, float* scale_inv, bool quant,
+                fp8bq::Big* b, bool* empty) {
+  *empty = false;
+  if (M < 0 || N < 0 || M > INT32_MAX || N > INT32_MAX || bm < 1 || bn < 1) {
+    return FP8BQ_ERR_INVALID_ARGUMENT;
+  }
+  if (row_phase < 0 || row_phase >= bm || col_phase < 0 || col_phase >= bn) {
+    return FP8BQ_ERR_INVALID_ARGUMENT;
+  }
+  if (M == 0 || N == 0) {
+    *empty = true;
+    return FP8BQ_OK;
+  }
+  if (x == nullptr || amax == nullptr) return FP8BQ_ERR_INVALID_ARGUMENT;
+  if (quant && (q == nullptr || scale_inv == nullptr)) return FP8BQ_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(x) & 1) != 0 || (reinterpret_cast<uintptr_t>(amax) & 3) != 0 ||
+      (quant && (reinterpret_cast<uintptr_t>(scale_inv) & 3) != 0)) {
+    return FP8BQ_ERR_INVALID_ARGUMENT;
+  }
+  *b = make_big(x, M, N, bm, bn, row_phase, col_phase, quant ? q : nullptr);
+  const uint64_t n = static_cast<uint64_t>(M) * static_cast<uint64_t>(N);
+  const uint64_t nt = 4 * static_cast<uint64_t>(b->TMl * b->TNl);
+  if (!quant) return overlap(x, 2 * n, amax, nt) ? FP8BQ_ERR_INVALID_ARGUMENT : FP8BQ_OK;
+  // amax may be scale_inv itself (converted in place), but not partly overlap it.
+  const bool same = static_cast<const void*>(amax) == static_cast<const void*>(scale_inv);
+  if (overlap(x, 2 * n, q, n) || overlap(x, 2 * n, scale_inv, nt) || overlap(q, n, scale_inv, nt) ||
+      overlap(x, 2 * n, amax, nt) || overlap(q, n, amax, nt) ||
+      (!same && overlap(amax, nt, scale_inv, nt))) {
+    return FP8BQ_ERR_INVALID_ARGUMENT;
+  }
+  return FP8BQ_OK;
+}
+
+template <int PASS, bool ROWS>
+void launch_shard_group(const fp8bq::ShardGroupArgs<fp8bq::kShardArgsMax>& a, int32_t n,
+                        int32_t bm, int32_t bn, int64_t total, unsigned lds, hipStream_t st) {
+  hipLaunchKernelGGL((fp8bq::shard_group<PASS, ROWS, fp8bq::kShardArgsMax>), dim3(grid_for(total)),
+                     dim3(fp8bq::kThreads), lds, st, a, n, bm, bn, static_cast<int32_t>(total));
+}
+
+// Grouped shard calls: every entry is checked first (nothing is enqueued on
+// an argument error); entries that take the small-tile kernels go in
+// launches of up to kShardArgsMax entries with the table in the kernel
+// arguments, the others in their own two-pass launches, all on `stream`.
+int shard_many(const fp8bq_shard* list, int32_t count, int32_t bm, int32_t bn, void* stream,
+               int pass) {
+  if (count < 0 || bm < 1 || bn < 1) return FP8BQ_ERR_INVALID_ARGUMENT;
+  if (count == 0) return FP8BQ_OK;
+  if (list == nullptr) return FP8BQ_ERR_INVALID_ARGUMENT;
+  thread_local std::vector<fp8bq::Big> bigs;
+  thread_local std::vector<int32_t> which;
+  bigs.clear();
+  which.clear();
+  for (int32_t i = 0; i < count; ++i) {
+    const fp8bq_shard& t = list[i];
+    fp8bq::Big b;
+    bool empty = false;
+    const int st = check_shard(t.x, t.M, t.N, bm, bn, t.row_phase, t.col_phase, t.amax, t.q,
+                               t.scale_inv, pass == 1, &b, &empty);
+    if (st != FP8BQ_OK) return st;
+    if (empty) continue;
+    bigs.push_back(b);
+    which.push_back(i);
+  }
+  if (bigs.empty()) return FP8BQ_OK;
+  int st = device_check();
+  if (st != FP8BQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const bool rows = bm == 1 && bn <= 128;
+  const unsigned lds =
+      pass == 1 && static_cast<int64_t>(bm) * static_cast<int64_t>(bn) >= fp8bq::kRegTile ? kLds4PerCu : 0u;
+  fp8bq::ShardGroupArgs<fp8bq::kShardArgsMax> a;
+  int32_t n = 0;
+  int64_t total = 0;
+  auto flush = [&]() {
+    if (n == 0) return;
+    a.start[n] = static_cast<int32_t>(total);
+    if (pass == 0) {
+      if (rows) launch_shard_group<0, true>(a, n, bm, bn, total, lds, s);
+      else launch_shard_group<0, false>(a, n, bm, bn, total, lds, s);
+    } else {
+      if (rows) launch_shard_group<1, true>(a, n, bm, bn, total, lds, s);
+      else launch_shard_group<1, false>(a, n, bm, bn, total, lds, s);
+    }
+    n = 0;
+    total = 0;
+  };
+  for (size_t k = 0; k < bigs.size(); ++k) {
+    const fp8bq::Big& b = bigs[k];
+    const fp8bq_shard& t = list[which[k]];
+    if (!shard_small_ok(b)) {  // large or unaligned tiles: this entry's own launches
+      if (pass == 0) {
+        launch_big_amax(b, t.amax, s);
+      } else {
+        launch_big_quant(b, t.amax, t.scale_inv, s);
+      }
+      continue;
+    }
+    const int64_t units = rows ? ceil_div(b.M, 64) * b.TNl : b.TMl * b.TNl;
+    if (n == fp8bq::kShardArgsMax || total + units > INT32_MAX) flush();
+    if (units > INT32_MAX) {  // a single entry beyond 32-bit units: its own launch
+      launch_shard_small(pass, b, t.amax, pass == 0 ? t.amax : t.scale_inv, s);
+      continue;
+    }
+    fp8bq::ShardEntry& e = a.e[n];
+    e.x = b.x;
+    e.q = b.q;
+    e.amax = t.amax;
+    e.out = pass == 0 ? t.amax : t.scale_inv;
+    e.M = static_cast<int32_t>(b.M);
+    e.N = static_cast<int32_t>(b.N);
+    e.row_phase = b.row_phase;
+    e.col_phase = b.col_phase;
+    a.start[n] = static_cast<int32_t>(total);
+    total += units;
+    ++n;
+  }
+  flush();
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -582,23 +709,12 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
 
 int fp8bq_tile_amax(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, int32_t row_phase,
                     int32_t col_phase, float* amax, void* stream) {
-  if (M < 0 || N < 0 || M > INT32_MAX || N > INT32_MAX || bm < 1 || bn < 1) {
-    return FP8BQ_ERR_INVALID_ARGUMENT;
-  }
-  if (row_phase < 0 || row_phase >= bm || col_phase < 0 || col_phase >= bn) {
-    return FP8BQ_ERR_INVALID_ARGUMENT;
-  }
-  if (M == 0 || N == 0) return FP8BQ_OK;
-  if (x == nullptr || amax == nullptr) return FP8BQ_ERR_INVALID_ARGUMENT;
-  if ((reinterpret_cast<uintptr_t>(x) & 1) != 0 || (reinterpret_cast<uintptr_t>(amax) & 3) != 0) {
-    return FP8BQ_ERR_INVALID_ARGUMENT;
-  }
-  const fp8bq::Big b = make_big(x, M, N, bm, bn, row_phase, col_phase, nullptr);
-  const uint64_t n = static_cast<uint64_t>(M) * static_cast<uint64_t>(N);
-  if (overlap(x, 2 * n, amax, 4 * static_cast<uint64_t>(b.TMl * b.TNl))) {
-    return FP8BQ_ERR_INVALID_ARGUMENT;
-  }
-  const int st = device_check();
+  fp8bq::Big b;
+  bool empty = false;
+  int st = check_shard(x, M, N, bm, bn, row_phase, col_phase, amax, nullptr, nullptr, false, &b,
+                       &empty);
+  if (st != FP8BQ_OK || empty) return st;
+  st = device_check();
   if (st != FP8BQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
@@ -614,31 +730,11 @@ int fp8bq_tile_amax(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn,
 int fp8bq_quantize_amax(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn,
                         int32_t row_phase, int32_t col_phase, const float* amax, void* q,
                         float* scale_inv, void* stream) {
-  if (M < 0 || N < 0 || M > INT32_MAX || N > INT32_MAX || bm < 1 || bn < 1) {
-    return FP8BQ_ERR_INVALID_ARGUMENT;
-  }
-  if (row_phase < 0 || row_phase >= bm || col_phase < 0 || col_phase >= bn) {
-    return FP8BQ_ERR_INVALID_ARGUMENT;
-  }
-  if (M == 0 || N == 0) return FP8BQ_OK;
-  if (x == nullptr || amax == nullptr || q == nullptr || scale_inv == nullptr) {
-    return FP8BQ_ERR_INVALID_ARGUMENT;
-  }
-  if ((reinterpret_cast<uintptr_t>(x) & 1) != 0 || (reinterpret_cast<uintptr_t>(amax) & 3) != 0 ||
-      (reinterpret_cast<uintptr_t>(scale_inv) & 3) != 0) {
-    return FP8BQ_ERR_INVALID_ARGUMENT;
-  }
-  const fp8bq::Big b = make_big(x, M, N, bm, bn, row_phase, col_phase, q);
-  const uint64_t n = static_cast<uint64_t>(M) * static_cast<uint64_t>(N);
-  const uint64_t nt = 4 * static_cast<uint64_t>(b.TMl * b.TNl);
-  // amax may be scale_inv itself (converted in place), but not partly overlap it.
-  const bool same = static_cast<const void*>(amax) == static_cast<const void*>(scale_inv);
-  if (overlap(x, 2 * n, q, n) || overlap(x, 2 * n, scale_inv, nt) || overlap(q, n, scale_inv, nt) ||
-      overlap(x, 2 * n, amax, nt) || overlap(q, n, amax, nt) ||
-      (!same && overlap(amax, nt, scale_inv, nt))) {
-    return FP8BQ_ERR_INVALID_ARGUMENT;
-  }
-  const int st = device_check();
+  fp8bq::Big b;
+  bool empty = false;
+  int st = check_shard(x, M, N, bm, bn, row_phase, col_phase, amax, q, scale_inv, true, &b, &empty);
+  if (st != FP8BQ_OK || empty) return st;
+  st = device_check();
   if (st != FP8BQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
@@ -649,6 +745,16 @@ int fp8bq_quantize_amax(const void* x, int64_t M, int64_t N, int32_t bm, int32_t
   }
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
+}
+
+int fp8bq_tile_amax_many(const fp8bq_shard* list, int32_t count, int32_t bm, int32_t bn,
+                         void* stream) {
+  return shard_many(list, count, bm, bn, stream, 0);
+}
+
+int fp8bq_quantize_amax_many(const fp8bq_shard* list, int32_t count, int32_t bm, int32_t bn,
+                             void* stream) {
+  return shard_many(list, count, bm, bn, stream, 1);
 }
 
 int fp8bq_encode_e4m3(const float* y, void* q, int64_t n, void* stream) {

@@ -1176,6 +1176,65 @@ __global__ __launch_bounds__(kThreads) void quantize_group_args(const GroupArgs<
   });
 }
 
+// ---------------------------------------------------------------- grouped shards, table in the arguments
+//
+// A list of shards that share one block size and take the small-tile
+// kernels, in one launch per pass: unit u belongs to the entry whose first
+// unit start[e] is the largest <= u (units: local tiles, or 64-row units
+// for one-row tiles).
+
+constexpr int kShardArgsMax = 256;
+
+struct ShardEntry {
+  const uint16_t* x;
+  uint8_t* q;
+  const float* amax;  // pass 1: the given maxima
+  float* out;         // pass 0: the maxima; pass 1: the scales (may be amax)
+  int32_t M;
+  int32_t N;
+  int32_t row_phase;
+  int32_t col_phase;
+};
+
+template <int CAP>
+struct ShardGroupArgs {
+  int32_t start[CAP + 1];
+  ShardEntry e[CAP];
+};
+
+template <int PASS, bool ROWS, int CAP>
+__global__ __launch_bounds__(kThreads) void shard_group(const ShardGroupArgs<CAP> a, int32_t count,
+                                                        int32_t bm, int32_t bn, int32_t total) {
+  __shared__ uint32_t red[8];
+  for_each_unit(total, [&](int64_t u) {
+    const int i = find_tensor(a.start, count, u);
+    const ShardEntry& en = a.e[i];
+    Big b;
+    b.x = en.x;
+    b.q = en.q;
+    b.M = en.M;
+    b.N = en.N;
+    b.bm = bm;
+    b.bn = bn;
+    b.row_phase = en.row_phase;
+    b.col_phase = en.col_phase;
+    b.TMl = ((int64_t)en.row_phase + en.M + bm - 1) / bm;
+    b.TNl = ((int64_t)en.col_phase + en.N + bn - 1) / bn;
+    b.cpt = 1;
+    b.items = b.TMl * b.TNl;
+    b.flat = 0;
+    b.vec = 1;
+    b.cpm = 1;
+    b.pad = 0;
+    const int64_t lu = u - a.start[i];
+    if constexpr (ROWS) {
+      shard_rows_unit<PASS>(b, lu, en.amax, en.out);
+    } else {
+      shard_small_tile<PASS>(b, lu, en.amax, en.out, red);
+    }
+  });
+}
+
 // The final cast alone: clamp and convert n floats.
 __global__ __launch_bounds__(kThreads) void encode_e4m3(const float* __restrict__ y,
                                                         uint8_t* __restrict__ q, int64_t n) {

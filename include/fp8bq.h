@@ -167,6 +167,46 @@ int fp8bq_quantize_amax(const void* x, int64_t M, int64_t N, int32_t bm, int32_t
                         int32_t row_phase, int32_t col_phase, const float* amax, void* q,
                         float* scale_inv, void* stream);
 
+/* One shard of a grouped shard call (fields as in fp8bq_tile_amax and
+ * fp8bq_quantize_amax; TMl x TNl is the shard's local tile grid). */
+typedef struct fp8bq_shard {
+  const void* x;     /* BF16 [M, N] row-major */
+  void* q;           /* e4m3fn [M, N]; written by fp8bq_quantize_amax_many only */
+  float* amax;       /* fp32 [TMl, TNl]: written by fp8bq_tile_amax_many, read by
+                        fp8bq_quantize_amax_many */
+  float* scale_inv;  /* fp32 [TMl, TNl]; written by fp8bq_quantize_amax_many only,
+                        may be the same array as amax */
+  int64_t M;
+  int64_t N;
+  int32_t row_phase;
+  int32_t col_phase;
+} fp8bq_shard;
+
+/*
+ * Grouped forms of fp8bq_tile_amax and fp8bq_quantize_amax over a list of
+ * shards that share one block size: the same results as one call per entry,
+ * in fewer launches.  For the quantize-before-gather of sharded weights
+ * (every rank quantizes its own slabs; only tiles cut by a slab boundary
+ * need their partial maxima exchanged), which the sharding discussion of
+ * the page "Using FP8 inference in long response vllm rollouts" points to.
+ *   list    HOST array of `count` entries, read before the call returns
+ *   count   number of entries (>= 0); entries with M == 0 or N == 0 are skipped
+ *   bm, bn  block size shared by every entry
+ *   stream  hipStream_t (NULL = null stream)
+ * Every entry is checked as the single call checks it before anything is
+ * enqueued.  Entries whose tiles hold at most 16,384 elements, with tile
+ * columns on 8-element boundaries (x 16-byte and q 8-byte aligned; N, bn and
+ * col_phase multiples of 8), share launches of up to 256 entries with the
+ * table in the kernel arguments (graph-capturable, no workspace); other
+ * entries take their own two-pass launches.  Outputs of different entries
+ * must not overlap each other or any entry's x (not checked across entries).
+ * Returns an fp8bq_status.
+ */
+int fp8bq_tile_amax_many(const fp8bq_shard* list, int32_t count, int32_t bm, int32_t bn,
+                         void* stream);
+int fp8bq_quantize_amax_many(const fp8bq_shard* list, int32_t count, int32_t bm, int32_t bn,
+                             void* stream);
+
 /* Output element type of fp8bq_dequantize. */
 enum fp8bq_out_dtype {
   FP8BQ_OUT_F32 = 0,  /* float32 */

@@ -127,6 +127,53 @@ def test_quantize_many_rejects(lib):
     assert f(bad, 1, 128, 128, W, need, None) == INVALID
 
 
+def _shards(rows):
+    arr = (fq.ShardEntry * len(rows))()
+    for e, (x, q, a, sc, M, N, rp, cp) in zip(arr, rows):
+        e.x, e.q, e.amax, e.scale_inv, e.M, e.N, e.row_phase, e.col_phase = x, q, a, sc, M, N, rp, cp
+    return arr
+
+
+def test_shard_entry_layout_matches_header():
+    # fp8bq_shard: four pointers, two int64, two int32 -> 56 bytes on LP64
+    assert ctypes.sizeof(fq.ShardEntry) == 56
+
+
+def test_shard_many_rejects(lib):
+    """Grouped shard calls check every entry as the single calls do, before
+    anything is enqueued (no device needed to reject)."""
+    A = S + 0x100000
+    good = [(X, Q, A, S, 256, 256, 64, 0)]
+    for f, quant in ((lib.fp8bq_tile_amax_many, False), (lib.fp8bq_quantize_amax_many, True)):
+        assert f(_shards(good), -1, 128, 128, None) == INVALID           # count < 0
+        assert f(None, 1, 128, 128, None) == INVALID                     # null list
+        assert f(_shards(good), 1, 0, 128, None) == INVALID              # bm < 1
+        assert f(_shards(good), 1, 128, 0, None) == INVALID              # bn < 1
+        for bad in [(X, Q, A, S, -1, 256, 0, 0),                         # negative M
+                    (X, Q, A, S, 256, 256, 128, 0),                      # row phase >= bm
+                    (X, Q, A, S, 256, 256, 0, -1),                       # negative column phase
+                    (None, Q, A, S, 256, 256, 0, 0),                     # null x
+                    (X, Q, None, S, 256, 256, 0, 0),                     # null amax
+                    (X + 1, Q, A, S, 256, 256, 0, 0),                    # x not 2-byte aligned
+                    (X, Q, A + 2, S, 256, 256, 0, 0),                    # amax not 4-byte aligned
+                    (X, Q, X + 8, S, 256, 256, 0, 0)]:                   # amax overlaps x
+            # one bad entry after a good one rejects the whole call
+            assert f(_shards(good + [bad]), 2, 128, 128, None) == INVALID, (quant, bad)
+        if quant:
+            for bad in [(X, None, A, S, 256, 256, 0, 0),                 # null q
+                        (X, Q, A, None, 256, 256, 0, 0),                 # null scale_inv
+                        (X, X + 64, A, S, 256, 256, 0, 0),               # q overlaps x
+                        (X, Q, A, A + 4, 256, 256, 0, 0)]:               # amax partly overlaps scale
+                assert f(_shards(good + [bad]), 2, 128, 128, None) == INVALID, bad
+
+
+def test_shard_many_empty_is_ok_without_device(lib):
+    empty = _shards([(None, None, None, None, 0, 8, 0, 0), (None, None, None, None, 8, 0, 0, 0)])
+    assert lib.fp8bq_tile_amax_many(empty, 2, 128, 128, None) == fq.OK
+    assert lib.fp8bq_quantize_amax_many(empty, 2, 128, 128, None) == fq.OK
+    assert lib.fp8bq_tile_amax_many(None, 0, 128, 128, None) == fq.OK
+
+
 def test_quantize_many_empty_is_ok_without_device(lib):
     assert lib.fp8bq_quantize_many(None, 0, 128, 128, None, 0, None) == fq.OK
     empty = _entries([(None, None, None, 0, 4096), (None, None, None, 7, 0)])

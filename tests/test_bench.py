@@ -51,15 +51,15 @@ def test_bench_json_line(gpu_lib):
 @pytest.mark.gpu
 def test_bench_shard_mode(gpu_lib):
     """--op shard on one dense layer: every tensor as a shard at a tile phase
-    through tile_amax and quantize_amax; the record's byte counts follow the
-    two-pass formula."""
+    through the grouped tile_amax and quantize_amax calls; the record's byte
+    counts follow the two-pass formula."""
     print("bench.py --workload dense-layer --op shard --phase 64,0", flush=True)
     res = subprocess.run([sys.executable, BENCH, "--workload", "dense-layer", "--op", "shard",
                           "--phase", "64,0", "--steps", "2", "--warmup", "1", "--no-cpu-baseline"],
                          capture_output=True, text=True, timeout=240, cwd=ROOT)
     assert res.returncode == 0, res.stderr[-2000:]
     rec = json.loads(res.stdout.strip().splitlines()[-1])
-    assert rec["op"] == "shard" and rec["phase"] == [64, 0] and rec["launches_per_step"] == 14
+    assert rec["op"] == "shard" and rec["phase"] == [64, 0] and rec["calls_per_step"] == 2
     sys.path.insert(0, ROOT)
     from fp8_blockwise_weight_amd import workloads as wl
 

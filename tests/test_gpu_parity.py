@@ -676,6 +676,66 @@ def test_shard_small_tile_kernels(gpu_lib):
             assert torch.equal(a2.view(torch.int32), s.view(torch.int32))
 
 
+@pytest.mark.parametrize("block", [(128, 128), (64, 64), (1, 128), (32, 96)])
+def test_shard_many_matches_single_calls(gpu_lib, block):
+    """Grouped shard calls over 300 shards (more than one 256-entry launch)
+    mixing small aligned tiles with entries that take their own launches
+    (N % 8 != 0, a misaligned x, odd column phases) and empty shards: every
+    maximum, code and scale equals the single calls'; maxima converted in
+    place (amax passed as scale_inv) give the same scales."""
+    import ctypes
+
+    bm, bn = block
+    g = torch.Generator(device=DEV).manual_seed(53)
+    rng = np.random.default_rng(53)
+    xs, phases = [], []
+    for i in range(300):
+        M = int(rng.integers(0 if i % 97 == 0 else 1, 300))
+        N = int(rng.choice([8, 64, 128, 136, 256, 520, 77]))
+        cp = 8 * int(rng.integers(max(1, bn // 8))) if i % 5 else int(rng.integers(bn))
+        ph = (int(rng.integers(bm)), min(cp, bn - 1))
+        flat = (torch.randn(M * N + 1, generator=g, device=DEV) * 0.03).to(torch.bfloat16)
+        # every 11th shard starts 2 bytes past a 16-byte boundary (contiguous view)
+        xs.append(flat[1:].view(M, N) if i % 11 == 0 else flat[:-1].view(M, N))
+        phases.append(ph)
+    say("shard many", block, len(xs))
+    amaxs = fq.tile_amax_many(xs, block, phases)
+    outs = fq.quantize_with_amax_many(xs, amaxs, block, phases)
+    for i, (x, ph, a, (q, s)) in enumerate(zip(xs, phases, amaxs, outs)):
+        if x.numel() == 0:
+            continue                          # an empty shard writes nothing
+        a1 = fq.tile_amax(x, block, ph)
+        assert torch.equal(a.view(torch.int32), a1.view(torch.int32)), (block, i)
+        q1, s1 = fq.quantize_with_amax(x, a1, block, ph)
+        assert torch.equal(q.view(torch.uint8), q1.view(torch.uint8)), (block, i)
+        assert torch.equal(s.view(torch.int32), s1.view(torch.int32)), (block, i)
+    for i in (0, 1, 150, 299):
+        xb = bits_np(xs[i])
+        if xb.size == 0:
+            continue
+        a_ref = oracle.tile_amax(xb, bm, bn, *phases[i])
+        q_ref, s_ref = oracle.quantize_with_amax(xb, bm, bn, a_ref, *phases[i])
+        assert np.array_equal(codes_np(outs[i][0]), q_ref) and np.array_equal(
+            scales_bits(outs[i][1]), scales_bits(s_ref)), (block, i)
+    # in place: scale_inv is amax itself, through the C ABI
+    inplace = [a.clone() for a in amaxs]
+    qs = [torch.empty_like(q) for q, _ in outs]
+    arr = (fq.ShardEntry * len(xs))()
+    for e, x, ph, a, q in zip(arr, xs, phases, inplace, qs):
+        e.x, e.q, e.amax, e.scale_inv = x.data_ptr(), q.data_ptr(), a.data_ptr(), a.data_ptr()
+        e.M, e.N = x.shape
+        e.row_phase, e.col_phase = ph
+    st = gpu_lib.load_library().fp8bq_quantize_amax_many(
+        arr, len(xs), bm, bn, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    torch.cuda.synchronize()
+    for i, (x, a, q, (q1, s1)) in enumerate(zip(xs, inplace, qs, outs)):
+        if x.numel() == 0:
+            continue
+        assert torch.equal(a.view(torch.int32), s1.view(torch.int32)), (block, i)
+        assert torch.equal(q.view(torch.uint8), q1.view(torch.uint8)), (block, i)
+
+
 def test_shards_equal_whole(gpu_lib):
     """Cuts anywhere (inside tiles too): shard-wise maxima, exchanged as a
     max, then shard-wise quantization reproduce the whole-matrix bytes."""
