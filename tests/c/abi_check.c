@@ -42,6 +42,18 @@ int main(void) {
          "phase out of range");
   expect(fp8bq_quantize_amax(X, 128, 128, 128, 128, 0, 0, NULL, Q, S, NULL),
          FP8BQ_ERR_INVALID_ARGUMENT, "null amax");
+  {
+    fp8bq_shard sh[2];
+    sh[0].x = X; sh[0].q = Q; sh[0].amax = S; sh[0].scale_inv = S;
+    sh[0].M = 256; sh[0].N = 256; sh[0].row_phase = 64; sh[0].col_phase = 0;
+    sh[1] = sh[0];
+    sh[1].row_phase = 128;
+    expect(fp8bq_tile_amax_many(sh, 2, 128, 128, NULL), FP8BQ_ERR_INVALID_ARGUMENT,
+           "shard phase out of range");
+    expect(fp8bq_quantize_amax_many(NULL, 1, 128, 128, NULL), FP8BQ_ERR_INVALID_ARGUMENT,
+           "null shard list");
+    expect(fp8bq_quantize_amax_many(sh, 0, 128, 128, NULL), FP8BQ_OK, "no shards");
+  }
   expect(fp8bq_encode_e4m3(NULL, Q, 4, NULL), FP8BQ_ERR_INVALID_ARGUMENT, "null y");
   expect(fp8bq_last_hip_error(), 0, "no HIP call made");
   if (failures == 0) printf("abi ok\n");
