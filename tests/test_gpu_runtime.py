@@ -107,6 +107,59 @@ def test_graph_capture_beyond_argument_table(gpu_lib, block):
         assert_matches_oracle(xs[i], outs[i][0], outs[i][1], *block, f"graph beyond table [{i}]")
 
 
+def test_graph_capture_of_grouped_shard_calls(gpu_lib):
+    """Grouped shard calls (maxima, then quantize with the maxima converted
+    in place) captured in one HIP graph: every replay, with the inputs
+    changed eagerly in between, equals the eager calls."""
+    import ctypes
+
+    g = torch.Generator(device=DEV).manual_seed(59)
+    shapes = [(300, 520), (1536, 2048), (77, 128), (2048, 768), (5, 8)] * 60   # 300 shards
+    xs = [(torch.randn(sh, generator=g, device=DEV) * 0.02).to(torch.bfloat16) for sh in shapes]
+    phases = [(64 if i % 2 else 0, 8 * (i % 3)) for i in range(len(xs))]
+    block = (128, 128)
+    grids = [fq.local_grid(*x.shape, *block, ph) for x, ph in zip(xs, phases)]
+    amaxs = [torch.empty(gr, dtype=torch.float32, device=DEV) for gr in grids]
+    qs = [torch.empty(x.shape, dtype=torch.uint8, device=DEV) for x in xs]
+    arr = (fq.ShardEntry * len(xs))()
+    for e, x, ph, a, q in zip(arr, xs, phases, amaxs, qs):
+        e.x, e.q, e.amax, e.scale_inv = x.data_ptr(), q.data_ptr(), a.data_ptr(), a.data_ptr()
+        e.M, e.N = x.shape
+        e.row_phase, e.col_phase = ph
+    lib = gpu_lib.load_library()
+
+    def calls():
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        assert lib.fp8bq_tile_amax_many(arr, len(xs), *block, st) == 0
+        assert lib.fp8bq_quantize_amax_many(arr, len(xs), *block, st) == 0
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()                                            # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        _say("shard graph replay", rep)
+        for x in xs:
+            x.mul_(2.0 if rep % 2 else 0.5)                # exact: powers of two
+        for q, a in zip(qs, amaxs):
+            q.fill_(0xA5)
+            a.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for x, ph, a, q in zip(xs, phases, amaxs, qs):
+            a1 = fq.tile_amax(x, block, ph)
+            q1, s1 = fq.quantize_with_amax(x, a1, block, ph)
+            assert torch.equal(q, q1.view(torch.uint8)), rep
+            assert torch.equal(a.view(torch.int32), s1.view(torch.int32)), rep
+
+
 def test_non_default_streams(gpu_lib):
     """Work is enqueued on the caller's current stream and ordered with it."""
     x = wl.materialize(wl.c2()[0], DEV)
