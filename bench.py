@@ -100,11 +100,14 @@ def committed_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
-def group_kernel_name(kind, count):
+def group_kernel_name(kind, count, flat=False):
     """Kernel a grouped call of `count` tensors launches (table in the kernel
-    arguments up to 512 tensors, else in a workspace)."""
+    arguments up to 512 tensors, else in a workspace); `flat`: [1,128]
+    tensors whose widths are all multiples of 128."""
     if count <= 512:
         cap = 8 if count <= 8 else (64 if count <= 64 else 512)
+        if flat:
+            return f"fp8bq::quantize_group_args_flat<{cap}>"
         return f"fp8bq::quantize_group_args<{kind},{cap}>"
     return f"fp8bq::quantize_group<{kind}>"
 
@@ -272,6 +275,7 @@ def main():
 
     traffic = committed_traffic() if args.workload == "dense" else None
     kind = {(128, 128): "kT128", (64, 64): "kT64", (1, 128): "kR128"}.get((bm, bn), "kGeneral")
+    flat = kind == "kR128" and all(sp.N % 128 == 0 for specs in groups for sp in specs)
     roofline = {
         "bound": "hbm",
         "achieved": round(achieved, 1),
@@ -279,7 +283,7 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": traffic,
-        "kernel": f"{group_kernel_name(kind, max(c for _, c, _ in calls))} "
+        "kernel": f"{group_kernel_name(kind, max(c for _, c, _ in calls), flat)} "
                   f"({'one launch' if launches == 1 else f'{launches} launches'} per step)",
         "bytes_per_launch": bytes_per_launch,
         "mean_launch_ms": round(mean_launch_ms, 4),

@@ -115,7 +115,12 @@ int make_desc(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, void*
   d->pad = 0;
   d->reserved = 0;
   int64_t u;
-  if (vec) {
+  if (vec && kind == fp8bq::kR128 && (N % 128) == 0) {
+    // [1,128] tiles are consecutive 128-element runs: 64 of them per unit
+    d->UN = static_cast<int32_t>(TN);
+    d->body = fp8bq::kBodyFlat;
+    u = ceil_div(M * (N / 128), 64);
+  } else if (vec) {
     const int64_t rows = kind == fp8bq::kT128 ? 128 : 64;
     d->UN = static_cast<int32_t>(ceil_div(N, 128));
     d->body = fp8bq::kBodyVec;
@@ -136,19 +141,40 @@ unsigned grid_for(int64_t units) {
   return static_cast<unsigned>(units < kMaxGrid ? units : kMaxGrid);
 }
 
+// Flat [1,128] units stream 16 KB contiguous runs; they run best at 4
+// workgroups per CU (151937x4096: 80.6% at 6 per CU, 83.1% at 4), while the
+// 64-row [1,128] units of other widths keep 6 per CU.
+bool is_flat(const Desc& d) { return d.body == fp8bq::kBodyFlat; }
+
+// LDS reserve of a launch whose tensors all have flat bodies (all_flat) or not.
+unsigned lds_of(int kind, bool all_flat) {
+  return kind == fp8bq::kR128 && all_flat ? kLds4PerCu : lds_for(kind);
+}
+
+bool all_flat(const std::vector<Desc>& ds) {
+  for (const Desc& d : ds) {
+    if (!is_flat(d)) return false;
+  }
+  return !ds.empty();
+}
+
 template <int KIND>
 void launch_one(const Desc& d, int32_t bm, int32_t bn, int64_t units, hipStream_t st) {
+  if (is_flat(d)) {
+    hipLaunchKernelGGL(fp8bq::quantize_flat_one, dim3(grid_for(units)), dim3(fp8bq::kThreads),
+                       kLds4PerCu, st, d, units);
+    return;
+  }
   hipLaunchKernelGGL(fp8bq::quantize_one<KIND>, dim3(grid_for(units)), dim3(fp8bq::kThreads),
-                     lds_for(KIND),
+                     lds_of(KIND, is_flat(d)),
                      st, d, bm, bn, units);
 }
 
 template <int KIND>
 void launch_group(const Desc* descs, const int64_t* start, int32_t count, int32_t bm, int32_t bn,
-                  int64_t units, hipStream_t st) {
+                  int64_t units, unsigned lds, hipStream_t st) {
   hipLaunchKernelGGL(fp8bq::quantize_group<KIND>, dim3(grid_for(units)), dim3(fp8bq::kThreads),
-                     lds_for(KIND),
-                     st, descs, start, count, bm, bn, units);
+                     lds, st, descs, start, count, bm, bn, units);
 }
 
 // Effective tile of an [M, N] tensor: more than kBigTile elements takes the
@@ -366,8 +392,13 @@ void launch_args(const std::vector<Desc>& ds, const std::vector<int64_t>& st, in
     a.t[i].body = ds[i].body;
   }
   a.start[n] = static_cast<int32_t>(total);
+  if (KIND == fp8bq::kR128 && all_flat(ds)) {
+    hipLaunchKernelGGL((fp8bq::quantize_group_args_flat<CAP>), dim3(grid_for(total)),
+                       dim3(fp8bq::kThreads), kLds4PerCu, s, a, n, static_cast<int32_t>(total));
+    return;
+  }
   hipLaunchKernelGGL((fp8bq::quantize_group_args<KIND, CAP>), dim3(grid_for(total)),
-                     dim3(fp8bq::kThreads), lds_for(KIND), s, a, n, bm, bn,
+                     dim3(fp8bq::kThreads), lds_of(KIND, all_flat(ds)), s, a, n, bm, bn,
                      static_cast<int32_t>(total));
 }
 
@@ -581,7 +612,7 @@ int fp8bq_quantize(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, 
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
   }
-  switch (d.body != fp8bq::kBodyVec ? static_cast<int>(fp8bq::kGeneral) : kind) {
+  switch (d.body != fp8bq::kBodyVec && d.body != fp8bq::kBodyFlat ? static_cast<int>(fp8bq::kGeneral) : kind) {
     case fp8bq::kT128: launch_one<fp8bq::kT128>(d, bm, bn, units, s); break;
     case fp8bq::kT64: launch_one<fp8bq::kT64>(d, bm, bn, units, s); break;
     case fp8bq::kR128: launch_one<fp8bq::kR128>(d, bm, bn, units, s); break;
@@ -668,7 +699,7 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
     for (int32_t i = 0; i < n; ++i) {
       const Desc& d = g_descs[i];
       const int64_t units = (i + 1 < n ? g_starts[i + 1] : total) - g_starts[i];
-      switch (d.body != fp8bq::kBodyVec ? static_cast<int>(fp8bq::kGeneral) : kind) {
+      switch (d.body != fp8bq::kBodyVec && d.body != fp8bq::kBodyFlat ? static_cast<int>(fp8bq::kGeneral) : kind) {
         case fp8bq::kT128: launch_one<fp8bq::kT128>(d, bm, bn, units, s); break;
         case fp8bq::kT64: launch_one<fp8bq::kT64>(d, bm, bn, units, s); break;
         case fp8bq::kR128: launch_one<fp8bq::kR128>(d, bm, bn, units, s); break;
@@ -694,13 +725,14 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
     const size_t used = descs_bytes(count) + sizeof(int64_t) * (static_cast<size_t>(n) + 1);
     hipError_t e = hipMemcpyAsync(ws, g_stage.data(), used, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_failed(e);
+    const unsigned lds = lds_of(kind, all_flat(g_descs));
     const Desc* d_descs = reinterpret_cast<const Desc*>(ws);
     const int64_t* d_start = reinterpret_cast<const int64_t*>(ws + descs_bytes(count));
     switch (kind) {
-      case fp8bq::kT128: launch_group<fp8bq::kT128>(d_descs, d_start, n, bm, bn, total, s); break;
-      case fp8bq::kT64: launch_group<fp8bq::kT64>(d_descs, d_start, n, bm, bn, total, s); break;
-      case fp8bq::kR128: launch_group<fp8bq::kR128>(d_descs, d_start, n, bm, bn, total, s); break;
-      default: launch_group<fp8bq::kGeneral>(d_descs, d_start, n, bm, bn, total, s); break;
+      case fp8bq::kT128: launch_group<fp8bq::kT128>(d_descs, d_start, n, bm, bn, total, lds, s); break;
+      case fp8bq::kT64: launch_group<fp8bq::kT64>(d_descs, d_start, n, bm, bn, total, lds, s); break;
+      case fp8bq::kR128: launch_group<fp8bq::kR128>(d_descs, d_start, n, bm, bn, total, lds, s); break;
+      default: launch_group<fp8bq::kGeneral>(d_descs, d_start, n, bm, bn, total, lds, s); break;
     }
   }
   const hipError_t e = hipGetLastError();
