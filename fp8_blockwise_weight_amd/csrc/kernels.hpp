@@ -16,7 +16,9 @@
 //   * [1,128] blocks: unit = 64 rows x 128 = 64 row-tiles; each tile's
 //     maximum is reduced inside one 16-lane DPP row, with no LDS and no
 //     barrier, and each lane divides for one row-tile only (DPP quad
-//     broadcast of the reciprocals);
+//     broadcast of the reciprocals); when N % 128 == 0 the unit is instead
+//     64 consecutive row-tiles of the flat array (16 KB contiguous), in
+//     kernels of their own;
 //   * any other block size (one tile per unit): up to 16384 elements with
 //     8-aligned columns, the whole tile in registers; up to 65536, two
 //     16-byte passes over the tile; N % 8 != 0 or a misaligned pointer,
@@ -24,7 +26,11 @@
 //   * tiles of more than 65536 elements (e.g. one scale per tensor) and
 //     shards that start inside a tile: two passes over chunks of each tile
 //     (section "large tiles"): per-workgroup maxima in slots of q and a
-//     reduce kernel for whole tensors, atomic maxima for shards.
+//     reduce kernel for whole tensors, atomic maxima for shards;
+//   * shards whose tiles hold at most 16384 elements with 8-aligned tile
+//     columns: one workgroup per tile (64-row units for one-row tiles), the
+//     maxima pass and the quantize pass each one launch, singly or grouped
+//     (section "small tiles of shards").
 // Every body computes the same arithmetic, so results never depend on it.
 // The file also holds dequantization (decode(q) * s, section
 // "dequantization") and the final cast on its own.
