@@ -10,7 +10,9 @@
 //     wave's load touches 4 rows x 256 contiguous bytes and its 8-byte FP8
 //     store writes 4 rows x 128 contiguous bytes (whole cache lines);
 //   * [128,128] blocks: unit = one tile (8 loads per thread, all held in
-//     registers: the tile is read from HBM exactly once);
+//     registers: the tile is read from HBM exactly once), or, for launches
+//     of wide and many tiles, four side-by-side tiles (128 x 512, 32 loads
+//     per thread) so that every wave load reads one 1 KB row run;
 //   * [64,64] blocks: unit = 64 x 128 = two side-by-side tiles, so the FP8
 //     rows written are still full 128-byte lines;
 //   * [1,128] blocks: unit = 64 rows x 128 = 64 row-tiles; each tile's
@@ -58,7 +60,7 @@ constexpr float kE4m3Max = 448.0f;
 constexpr float kEps = 1e-10f;
 constexpr int kThreads = 256;
 
-enum Kind : int { kT128 = 0, kT64 = 1, kR128 = 2, kGeneral = 3 };
+enum Kind : int { kT128 = 0, kT64 = 1, kR128 = 2, kGeneral = 3, kT128W = 4 };
 
 // Pointers into device memory, marked as global so loads and stores are
 // emitted as global_* (not flat_*) instructions.
@@ -303,6 +305,70 @@ __device__ __forceinline__ void vec_unit(const Desc& d, int64_t ur, int64_t uc, 
   }
 }
 
+// [128,128] blocks, wide unit (kind kT128W): 128 rows x 512 columns, four
+// side-by-side tiles per workgroup.  Lane c of a wave holds columns
+// 8c..8c+7 of a 512-column row run (16-lane DPP row d = tile d of the
+// unit), and wave w holds rows w, w+4, ..., w+124, so every wave load reads
+// one contiguous 1 KB run and every store writes 512 contiguous bytes.  32
+// loads per thread (all held in registers, about 224 VGPRs: 2 workgroups
+// per CU).  A tile's maximum: fold over the thread's 32 loads, max over its
+// DPP row, then over the 4 waves through LDS.  Against the one-tile unit
+// this moved the 252-tensor dense set from 77.1% to 80.3% of the HBM peak
+// (data-movement probes: 128x128 units 76.6-78.3%, 128x512 80.7%), but
+// launches of few or half-empty units lose (one MoE layer: 76.3% -> 74.1%),
+// so the host picks it per launch.
+template <bool CHECK>
+__device__ __forceinline__ void vec_unit_wide(const Desc& d, int64_t ur, int64_t uc, uint32_t* red) {
+  constexpr int L = 32;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int sub = lane >> 4;
+  const int64_t N = d.N;
+  const int64_t row0 = ur * 128;
+  const int64_t col = uc * 512 + lane * 8;
+  int rows_valid = 128;
+  bool col_ok = true;
+  if (CHECK) {
+    const int64_t left = d.M - row0;
+    rows_valid = left < 128 ? (int)left : 128;
+    col_ok = col < N;  // N % 8 == 0: a chunk is wholly inside or outside
+  }
+  const size_t base = (size_t)(row0 + wave) * (size_t)N + (size_t)col;
+  const FP8BQ_GLOBAL u32x4* xp = (const FP8BQ_GLOBAL u32x4*)(d.x + base);
+  const size_t pitch16 = (size_t)N * 4 / 8;  // 4 rows, in 16-byte chunks
+  u32x4 v[L];
+#pragma unroll
+  for (int k = 0; k < L; ++k) {
+    if (!CHECK || (col_ok && k * 4 + wave < rows_valid)) {
+      v[k] = __builtin_nontemporal_load(&xp[k * pitch16]);
+    } else {
+      v[k] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < L; ++k) m = pk_max_u16(m, fold_abs(v[k]));
+  m = max16(halves_max(m));
+  if ((lane & 15) == 0) red[wave * 4 + sub] = m;
+  __syncthreads();
+  const uint32_t tm = max(max(red[sub], red[4 + sub]), max(red[8 + sub], red[12 + sub]));
+  float s, r;
+  tile_scale(tm, s, r);
+  FP8BQ_GLOBAL u32x2* qp = (FP8BQ_GLOBAL u32x2*)(d.q + base);
+  const size_t qpitch8 = (size_t)N * 4 / 8;  // 4 rows, in 8-byte chunks
+#pragma unroll
+  for (int k = 0; k < L; ++k) {
+    if (!CHECK || (col_ok && k * 4 + wave < rows_valid)) {
+      __builtin_nontemporal_store(quant8(v[k], r), &qp[k * qpitch8]);
+    }
+  }
+  const int64_t tj = uc * 4 + sub;
+  if (wave == 0 && (lane & 15) == 0 && (!CHECK || tj < d.TN)) {
+    ((FP8BQ_GLOBAL float*)d.s)[(size_t)ur * d.TN + tj] = s;
+  }
+}
+
 // A whole tile of at most kRegTile elements held in registers: rows x cols
 // with cols % 8 == 0, x 16-byte and q 8-byte aligned, N % 8 == 0.  Vector v
 // of the tile is row v / (cols/8), 8-column group v % (cols/8); thread t
@@ -489,6 +555,13 @@ __device__ __forceinline__ void run_unit(const Desc& d, int32_t bm, int32_t bn, 
     }
   } else if (d.body != kBodyVec) {
     general_tile<false>(d, bm, bn, ur, uc, red);
+  } else if constexpr (KIND == kT128W) {
+    const bool inside = (int64_t)(ur + 1) * 128 <= d.M && (int64_t)(uc + 1) * 512 <= d.N;
+    if (inside) {
+      vec_unit_wide<false>(d, ur, uc, red);
+    } else {
+      vec_unit_wide<true>(d, ur, uc, red);
+    }
   } else {
     constexpr int R = UnitShape<KIND>::kRows;
     const bool inside = (int64_t)(ur + 1) * R <= d.M && (int64_t)(uc + 1) * 128 <= d.N;
@@ -537,7 +610,7 @@ __device__ __forceinline__ void for_each_unit(int64_t total, F&& f) {
 template <int KIND>
 __global__ __launch_bounds__(kThreads) void quantize_one(Desc d, int32_t bm, int32_t bn,
                                                          int64_t total) {
-  __shared__ uint32_t red[8];
+  __shared__ uint32_t red[16];
   for_each_unit(total, [&](int64_t u) {
     run_unit<KIND>(d, bm, bn, u, red);
   });
@@ -574,7 +647,7 @@ __global__ __launch_bounds__(kThreads) void quantize_group(const Desc* __restric
                                                            const int64_t* __restrict__ start,
                                                            int32_t count, int32_t bm, int32_t bn,
                                                            int64_t total) {
-  __shared__ uint32_t red[8];
+  __shared__ uint32_t red[16];
   for_each_unit(total, [&](int64_t u) {
     const int lo = find_tensor(start, count, u);
     const Desc d = descs[lo];
@@ -1033,7 +1106,7 @@ __global__ __launch_bounds__(kThreads) void shard_rows(Big b, const float* amax,
 template <int PASS>
 __global__ __launch_bounds__(kThreads) void shard_small(Big b, const float* amax, float* out,
                                                         int64_t tiles) {
-  __shared__ uint32_t red[8];
+  __shared__ uint32_t red[16];
   for_each_unit(tiles, [&](int64_t tile) { shard_small_tile<PASS>(b, tile, amax, out, red); });
 }
 
@@ -1230,7 +1303,7 @@ template <int KIND, int CAP>
 __global__ __launch_bounds__(kThreads) void quantize_group_args(const GroupArgs<CAP> a,
                                                                 int32_t count, int32_t bm,
                                                                 int32_t bn, int32_t total) {
-  __shared__ uint32_t red[8];
+  __shared__ uint32_t red[16];
   for_each_unit(total, [&](int64_t u) {
     const int lo = find_tensor(a.start, count, u);
     const ArgTensor& at = a.t[lo];
@@ -1242,7 +1315,8 @@ __global__ __launch_bounds__(kThreads) void quantize_group_args(const GroupArgs<
     d.N = at.N;
     d.TN = (int32_t)(((int64_t)at.N + bn - 1) / bn);
     d.body = at.body;
-    d.UN = at.body != kBodyVec ? d.TN : (int32_t)(((int64_t)at.N + 127) / 128);
+    constexpr int64_t kUnitCols = KIND == kT128W ? 512 : 128;
+    d.UN = at.body != kBodyVec ? d.TN : (int32_t)(((int64_t)at.N + kUnitCols - 1) / kUnitCols);
     d.pad = 0;
     d.reserved = 0;
     run_unit<KIND>(d, bm, bn, u - a.start[lo], red);
@@ -1278,7 +1352,7 @@ struct ShardGroupArgs {
 template <int PASS, bool ROWS, int CAP>
 __global__ __launch_bounds__(kThreads) void shard_group(const ShardGroupArgs<CAP> a, int32_t count,
                                                         int32_t bm, int32_t bn, int32_t total) {
-  __shared__ uint32_t red[8];
+  __shared__ uint32_t red[16];
   for_each_unit(total, [&](int64_t u) {
     const int i = find_tensor(a.start, count, u);
     const ShardEntry& en = a.e[i];

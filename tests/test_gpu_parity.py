@@ -481,6 +481,36 @@ def test_c3_dense_stack_one_grouped_launch(gpu_lib):
     say("C3 checked")
 
 
+def test_wide_unit_launch(gpu_lib):
+    """A [128,128] launch that takes the four-tile (128x512) unit: widths that
+    are multiples of 512 and at least 8192 such units in all (a 1 GB matrix
+    whose last unit row holds 72 rows), grouped with a misaligned tensor (a
+    general body in the same launch), a ragged-height tensor and an empty
+    one.  Every scale is checked against the oracle's scale of the exact
+    tile maxima, sampled tiles byte for byte; the small tensors equal their
+    single calls (one-tile units)."""
+    g = torch.Generator(device=DEV).manual_seed(61)
+    big = (torch.randn((32768 - 56, 16384), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    flat = (torch.randn(1000 * 4096 + 1, generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    mis = flat[1:].view(1000, 4096)                   # 2 bytes past a 16-byte boundary
+    ragged = (torch.randn((777, 1024), generator=g, device=DEV) * 0.05).to(torch.bfloat16)
+    empty = torch.empty((0, 512), dtype=torch.bfloat16, device=DEV)
+    xs = [ragged, big, mis, empty]
+    say("wide-unit launch")
+    outs = fq.quantize_many(xs, (128, 128))
+    torch.cuda.synchronize()
+    assert_scales_match_oracle(big, outs[1][1], 128, 128, "wide big")
+    assert_properties_gpu(big, outs[1][0], outs[1][1], 128, 128, "wide big")
+    tiles = sample_tiles(*big.shape, 128, 128, 6, seed=61) + [(255, 127), (255, 0), (0, 127)]
+    assert_tiles_match_oracle(big, outs[1][0], outs[1][1], 128, 128, tiles, "wide big")
+    for x, (q, s), name in ((ragged, outs[0], "ragged"), (mis, outs[2], "misaligned")):
+        q1, s1 = fq.quantize(x, (128, 128))
+        assert torch.equal(q.view(torch.uint8), q1.view(torch.uint8)), name
+        assert torch.equal(s.view(torch.int32), s1.view(torch.int32)), name
+    assert_matches_oracle(ragged, outs[0][0], outs[0][1], 128, 128, "ragged in wide launch")
+    del big, outs
+
+
 @pytest.mark.parametrize("part", range(4))
 def test_c4_moe_per_layer_grouped(gpu_lib, part):
     """MoE weight set: 48 layers x 256 expert matrices, one grouped launch per
