@@ -316,7 +316,10 @@ __device__ __forceinline__ void vec_unit(const Desc& d, int64_t ur, int64_t uc, 
 // this moved the 252-tensor dense set from 77.1% to 80.3% of the HBM peak
 // (data-movement probes: 128x128 units 76.6-78.3%, 128x512 80.7%), but
 // launches of few or half-empty units lose (one MoE layer: 76.3% -> 74.1%),
-// so the host picks it per launch.
+// so the host picks it per launch.  Also measured and not kept: two-tile
+// 128x256 units (dense set 76.7%, below both), and MoE launches that give
+// the 2048-wide matrices wide units and the 768-wide ones one-tile units
+// (74.8% against 77.0% with one-tile units throughout).
 template <bool CHECK>
 __device__ __forceinline__ void vec_unit_wide(const Desc& d, int64_t ur, int64_t uc, uint32_t* red) {
   constexpr int L = 32;
@@ -556,7 +559,11 @@ __device__ __forceinline__ void run_unit(const Desc& d, int32_t bm, int32_t bn, 
   } else if (d.body != kBodyVec) {
     general_tile<false>(d, bm, bn, ur, uc, red);
   } else if constexpr (KIND == kT128W) {
-    const bool inside = (int64_t)(ur + 1) * 128 <= d.M && (int64_t)(uc + 1) * 512 <= d.N;
+    // The host picks this kind only for tensors whose width is a whole number
+    // of 512-column units, so only the last unit row can be ragged.  Testing
+    // the rows alone measured 1-2% faster than also testing the columns
+    // (dense 36-layer set 80.1% -> 81.2% of peak, 151937x4096 78.9% -> 81.0%).
+    const bool inside = (int64_t)(ur + 1) * 128 <= d.M;
     if (inside) {
       vec_unit_wide<false>(d, ur, uc, red);
     } else {
