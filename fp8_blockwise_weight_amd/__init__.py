@@ -41,6 +41,7 @@ EXPORTS = (
     "fp8bq_quantize_amax",
     "fp8bq_tile_amax_many",
     "fp8bq_quantize_amax_many",
+    "fp8bq_set_resident_wait_us",
     "fp8bq_status_string",
     "fp8bq_last_hip_error",
 )
@@ -114,6 +115,8 @@ def load_library() -> ctypes.CDLL:
         getattr(lib, name).restype = ctypes.c_int
     lib.fp8bq_encode_e4m3.argtypes = [c_vp, c_vp, c_i64, c_vp]
     lib.fp8bq_encode_e4m3.restype = ctypes.c_int
+    lib.fp8bq_set_resident_wait_us.argtypes = [c_i64]
+    lib.fp8bq_set_resident_wait_us.restype = ctypes.c_int
     lib.fp8bq_status_string.argtypes = [ctypes.c_int]
     lib.fp8bq_status_string.restype = ctypes.c_char_p
     lib.fp8bq_last_hip_error.argtypes = []
@@ -490,6 +493,13 @@ def quantize_with_amax_many(xs: Sequence, amaxs: Sequence, block_size=(128, 128)
     return list(zip(qs, scales))
 
 
+def set_resident_wait_us(microseconds: int) -> None:
+    """Longest wait of a workgroup of the one-scale-per-tensor kernel for the
+    tensor-wide maximum before it computes that maximum itself
+    (``fp8bq_set_resident_wait_us``; process-wide, default 2000 us)."""
+    _check("fp8bq_set_resident_wait_us", load_library().fp8bq_set_resident_wait_us(int(microseconds)))
+
+
 def encode_e4m3(y):
     """The final cast alone: float32 GPU tensor -> e4m3fn codes (uint8), clamped to +-448."""
     import torch
@@ -508,5 +518,6 @@ __all__ = [
     "EXPORTS", "Fp8bqError", "TensorEntry", "block_shape", "dequantize", "encode_e4m3",
     "load_library", "local_grid", "quantize_with_amax", "quantize_with_amax_many", "tile_amax",
     "tile_amax_many", "ShardEntry",
-    "make_entries", "quantize", "quantize_many", "scale_shape", "workspace_bytes",
+    "make_entries", "quantize", "quantize_many", "scale_shape", "set_resident_wait_us",
+    "workspace_bytes",
 ]

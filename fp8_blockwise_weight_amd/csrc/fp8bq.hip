@@ -10,6 +10,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <utility>
 #include <vector>
 
 #include "fp8bq.h"
@@ -354,6 +355,113 @@ void launch_big_tensor(const fp8bq::Big& b, float* scale_inv, hipStream_t st) {
                      b, static_cast<const float*>(scale_inv));
 }
 
+// ---- one scale per tensor, held in registers (resident_quant)
+//
+// A whole tensor of at least kResMinValues values with one tile, aligned for
+// 16-byte loads, that fits in the registers of the grid the device holds at
+// once.  Grid and chunks per thread (L) per tensor, from measurements on
+// MI355X: the fewest chunks per thread that need at most 128 workgroups
+// (1024x4096: 128 x 16 chunks 8.6 us, 256 x 8 9.4 us, 512 x 4 12.5 us),
+// else 32 or 48 chunks per thread (4096x4096: 256 x 32 14.5 us against
+// 512 x 16 17.1 us; 12288x4096: 512 x 48 29.4 us).  The two-pass path took
+// 10.6, 19.2 and 44.7 us.
+constexpr int64_t kResMinValues = int64_t{1} << 20;
+constexpr int kResPrepCap = 128;
+constexpr int64_t kResWaitUsDefault = 2000;
+
+struct ResPlan {
+  int L;
+  uint32_t grid;
+  uint32_t nchunks;
+};
+
+// Per device: workgroups of resident_quant<48> held at once (0 unknown, -1
+// failed) and s_memrealtime ticks per microsecond.
+std::atomic<int> g_res_grid[kMaxDevices];
+std::atomic<int> g_res_tick_mhz[kMaxDevices];
+std::atomic<int64_t> g_res_wait_us{kResWaitUsDefault};
+
+// Workgroups of the largest variant the current device holds at once, or 0.
+int resident_capacity(int* tick_mhz) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int cap = g_res_grid[dev].load(std::memory_order_acquire);
+  if (cap == 0) {
+    int per = 0, cus = 0, khz = 0;
+    const bool ok =
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fp8bq::resident_quant<fp8bq::kResMaxLoads>,
+                                                     fp8bq::kThreads, 0) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess &&
+        per > 0 && cus > 0 && khz >= 1000;
+    (void)hipGetLastError();
+    cap = ok ? per * cus : -1;
+    g_res_tick_mhz[dev].store(ok ? khz / 1000 : 0, std::memory_order_relaxed);
+    g_res_grid[dev].store(cap, std::memory_order_release);
+  }
+  *tick_mhz = g_res_tick_mhz[dev].load(std::memory_order_relaxed);
+  return cap > 0 ? cap : 0;
+}
+
+// The resident plan of a tensor (bm >= M and bn >= N: one tile), or false.
+bool resident_plan(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, const void* q,
+                   int cap, ResPlan* p) {
+  if (cap <= 0 || M > bm || N > bn || (N % 8) != 0) return false;
+  if ((reinterpret_cast<uintptr_t>(x) & 15) != 0 || (reinterpret_cast<uintptr_t>(q) & 7) != 0) {
+    return false;
+  }
+  const int64_t n = M * N;
+  if (n < kResMinValues) return false;
+  const int64_t chunks = n / 8;
+  if (chunks > (int64_t{1} << 26)) return false;  // byte offsets stay below 2^31
+  const int64_t per_wg = fp8bq::kThreads;
+  for (int L : {4, 8, 16}) {
+    const int64_t g = ceil_div(chunks, per_wg * L);
+    if (g <= 128 && g <= cap) {
+      *p = ResPlan{L, static_cast<uint32_t>(g), static_cast<uint32_t>(chunks)};
+      return true;
+    }
+  }
+  for (int L : {32, fp8bq::kResMaxLoads}) {
+    const int64_t g = ceil_div(chunks, per_wg * L);
+    if (g <= cap) {
+      *p = ResPlan{L, static_cast<uint32_t>(g), static_cast<uint32_t>(chunks)};
+      return true;
+    }
+  }
+  return false;
+}
+
+// Handshake words and scale sentinels of n resident tensors (before any of
+// their resident_quant launches).
+void launch_resident_prep(const fp8bq::ResTensor* ts, int n, hipStream_t st) {
+  for (int i0 = 0; i0 < n; i0 += kResPrepCap) {
+    const int c = n - i0 < kResPrepCap ? n - i0 : kResPrepCap;
+    fp8bq::ResPrepArgs<kResPrepCap> a;
+    std::memset(&a, 0, sizeof(a));
+    for (int i = 0; i < c; ++i) a.t[i] = ts[i0 + i];
+    hipLaunchKernelGGL(fp8bq::resident_prep<kResPrepCap>, dim3(1), dim3(kResPrepCap), 0, st, a, c);
+  }
+}
+
+void launch_resident(const ResPlan& p, const void* x, void* q, float* s, int tick_mhz,
+                     hipStream_t st) {
+  const uint64_t ticks = static_cast<uint64_t>(g_res_wait_us.load(std::memory_order_relaxed)) *
+                         static_cast<uint64_t>(tick_mhz);
+  const uint16_t* xs = static_cast<const uint16_t*>(x);
+  uint8_t* qs = static_cast<uint8_t*>(q);
+  const dim3 g(p.grid), b(fp8bq::kThreads);
+  switch (p.L) {
+    case 4: hipLaunchKernelGGL(fp8bq::resident_quant<4>, g, b, 0, st, xs, qs, s, p.nchunks, ticks); break;
+    case 8: hipLaunchKernelGGL(fp8bq::resident_quant<8>, g, b, 0, st, xs, qs, s, p.nchunks, ticks); break;
+    case 16: hipLaunchKernelGGL(fp8bq::resident_quant<16>, g, b, 0, st, xs, qs, s, p.nchunks, ticks); break;
+    case 32: hipLaunchKernelGGL(fp8bq::resident_quant<32>, g, b, 0, st, xs, qs, s, p.nchunks, ticks); break;
+    default:
+      hipLaunchKernelGGL(fp8bq::resident_quant<fp8bq::kResMaxLoads>, g, b, 0, st, xs, qs, s, p.nchunks, ticks);
+      break;
+  }
+}
+
 constexpr int kBigGroupCap = 128;  // tensors per grouped large-tile launch
 
 // Whole tensors with large tiles, up to kBigGroupCap per group: 3 launches per
@@ -635,7 +743,15 @@ int fp8bq_quantize(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (big_tiles(M, N, bm, bn)) {
-    launch_big_tensor(make_big(x, M, N, bm, bn, 0, 0, q), scale_inv, s);
+    int tick_mhz = 0;
+    ResPlan p;
+    if (resident_plan(x, M, N, bm, bn, q, resident_capacity(&tick_mhz), &p)) {
+      const fp8bq::ResTensor t{static_cast<uint8_t*>(q), scale_inv};
+      launch_resident_prep(&t, 1, s);
+      launch_resident(p, x, q, scale_inv, tick_mhz, s);
+    } else {
+      launch_big_tensor(make_big(x, M, N, bm, bn, 0, 0, q), scale_inv, s);
+    }
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
   }
@@ -702,7 +818,28 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (any_big) {
-    // Grouped two-pass launches, kBigGroupCap tensors at a time.
+    // Whole tensors that fit in registers: one resident launch each, after
+    // one preparation launch for all of them.
+    int tick_mhz = 0;
+    const int cap = resident_capacity(&tick_mhz);
+    std::vector<std::pair<const fp8bq_tensor*, ResPlan>> res;
+    std::vector<fp8bq::ResTensor> res_t;
+    for (int32_t i = 0; i < count; ++i) {
+      const fp8bq_tensor& t = list[i];
+      ResPlan p;
+      if (t.M == 0 || t.N == 0 || !big_tiles(t.M, t.N, bm, bn) ||
+          !resident_plan(t.x, t.M, t.N, bm, bn, t.q, cap, &p)) {
+        continue;
+      }
+      res.emplace_back(&t, p);
+      res_t.push_back(fp8bq::ResTensor{static_cast<uint8_t*>(t.q), t.scale_inv});
+    }
+    if (!res.empty()) {
+      launch_resident_prep(res_t.data(), static_cast<int>(res_t.size()), s);
+      for (const auto& r : res) launch_resident(r.second, r.first->x, r.first->q, r.first->scale_inv, tick_mhz, s);
+    }
+    // The other large-tile tensors: grouped two-pass launches, kBigGroupCap
+    // tensors at a time.
     std::vector<const fp8bq_tensor*> group;
     auto flush = [&]() {
       if (group.empty()) return;
@@ -715,7 +852,11 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
     };
     for (int32_t i = 0; i < count; ++i) {
       const fp8bq_tensor& t = list[i];
-      if (t.M == 0 || t.N == 0 || !big_tiles(t.M, t.N, bm, bn)) continue;
+      ResPlan p;
+      if (t.M == 0 || t.N == 0 || !big_tiles(t.M, t.N, bm, bn) ||
+          resident_plan(t.x, t.M, t.N, bm, bn, t.q, cap, &p)) {
+        continue;
+      }
       group.push_back(&t);
       if (static_cast<int>(group.size()) == kBigGroupCap) flush();
     }
@@ -911,6 +1052,12 @@ int fp8bq_dequantize(const void* q, const float* scale_inv, int64_t M, int64_t N
   }
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
+}
+
+int fp8bq_set_resident_wait_us(int64_t microseconds) {
+  if (microseconds < 0 || microseconds > (int64_t{1} << 40)) return FP8BQ_ERR_INVALID_ARGUMENT;
+  g_res_wait_us.store(microseconds, std::memory_order_relaxed);
+  return FP8BQ_OK;
 }
 
 const char* fp8bq_status_string(int status) {

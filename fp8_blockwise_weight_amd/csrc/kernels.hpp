@@ -981,6 +981,166 @@ __global__ __launch_bounds__(kThreads) void big_group_quant(const BigGroupArgs<C
 }
 
 // out[i] = 0 for i < n.
+// ---------------------------------------------------------------- one scale per tensor, held in registers
+//
+// A whole tensor with a single tile (one scale) that fits in the registers
+// of one grid is read from HBM once instead of twice: every thread loads its
+// share (up to kResMaxLoads 16-byte chunks, 8 values each) into registers,
+// the workgroups combine their maxima, and each then quantizes the values it
+// still holds.  3 bytes move per value instead of the two-pass path's 5.
+//
+// Cross-workgroup handshake, all through relaxed device-scope atomics (the
+// only data that crosses workgroups is the atomics' own values):
+//   * before the launch, resident_prep zeroes a count (q bytes 0..3) and a
+//     maximum (q bytes 128..131, its own cache line: a shared line measured
+//     15-20% slower) and writes kResNoScale into scale_inv (no scale is NaN);
+//   * a workgroup raises the maximum, and only once that atomic has returned
+//     increments the count (the count's operand depends on the returned
+//     value); the workgroup that brings the count to the grid size reads the
+//     maximum, computes the scale and stores it to scale_inv;
+//   * the others poll scale_inv.  One that has waited longer than
+//     `wait_ticks` (100 MHz s_memrealtime ticks; the workgroups of a launch
+//     need not all be resident at once, e.g. beside another launch) computes
+//     the tensor's maximum itself from x: the scale is the same either way
+//     and no wait is unbounded;
+//   * the two q words are overwritten last by atomic exchanges, in the same
+//     coherence order as the handshake atomics.
+// Acquire/release ordering would make every workgroup write back and
+// invalidate its L2 (measured: a fixed ~15 us per launch), and nothing but
+// the atomics' values needs ordering.
+//
+// Loads and stores go through raw buffer resources sized to the tensor, with
+// the whole byte offset in the per-lane (range-checked) offset: loads past
+// the end return 0 (no effect on a maximum of magnitudes) and stores past
+// the end are dropped, so the body has no bounds branches.
+
+constexpr int kResMaxLoads = 48;            // chunks per thread, largest variant
+constexpr uint32_t kResNoScale = 0xFFFFFFFFu;
+constexpr int kResCountWord = 0;            // 32-bit word of q
+constexpr int kResMaxWord = 32;             // 32-bit word of q (byte 128)
+constexpr int kRawBufferFlags = 0x00020000; // buffer resource word 3: 32-bit format
+constexpr int kNtPolicy = 2;                // nontemporal cache policy of buffer ops
+constexpr uint32_t kResDropOffset = 0x7FFFFFF8u;  // past any tensor here: the store is dropped
+
+struct ResTensor {
+  uint8_t* q;
+  float* s;
+};
+
+template <int CAP>
+struct ResPrepArgs {
+  ResTensor t[CAP];
+};
+
+template <int CAP>
+__global__ void resident_prep(const ResPrepArgs<CAP> a, int32_t count) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i >= count) return;
+  uint32_t* w = reinterpret_cast<uint32_t*>(a.t[i].q);
+  w[kResCountWord] = 0u;
+  w[kResMaxWord] = 0u;
+  *reinterpret_cast<uint32_t*>(a.t[i].s) = kResNoScale;
+}
+
+// Thread 0 of a workgroup: contributes `bmax` and returns the scale's bits,
+// or kResNoScale when the wait limit passed first.
+__device__ __forceinline__ uint32_t resident_arrive(uint32_t bmax, uint8_t* q, float* s,
+                                                    uint64_t wait_ticks) {
+  uint32_t* w = reinterpret_cast<uint32_t*>(q);
+  uint32_t* sb = reinterpret_cast<uint32_t*>(s);
+  const uint32_t prev =
+      __hip_atomic_fetch_max(&w[kResMaxWord], bmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // prev <= 0x7FFF, so the operand is 1; the dependency orders the two atomics.
+  const uint32_t old = __hip_atomic_fetch_add(&w[kResCountWord], 1u + (prev >> 31),
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (old == gridDim.x - 1) {
+    const uint32_t amax = __hip_atomic_load(&w[kResMaxWord], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float sf, rf;
+    tile_scale(amax, sf, rf);
+    const uint32_t sv = __float_as_uint(sf);
+    __hip_atomic_store(sb, sv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return sv;
+  }
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (;;) {
+    const uint32_t sv = __hip_atomic_load(sb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (sv != kResNoScale) return sv;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > wait_ticks) return kResNoScale;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// The scale's bits from all of x, by one workgroup (the wait-limit path).
+__device__ __forceinline__ uint32_t resident_scan(__amdgpu_buffer_rsrc_t xr, uint32_t nchunks,
+                                                  uint32_t* red) {
+  const uint32_t t = threadIdx.x;
+  uint32_t m = 0;
+  for (uint32_t c = t; c < nchunks; c += kThreads) {
+    const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(c * 16u), 0, 0));
+    m = pk_max_u16(m, fold_abs(w));
+  }
+  m = rows_max<0>(max16(halves_max(m)));
+  __syncthreads();  // red[] may still be read by other waves
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  float sf, rf;
+  tile_scale(max(max(red[0], red[1]), max(red[2], red[3])), sf, rf);
+  return __float_as_uint(sf);
+}
+
+// One tensor of nchunks 16-byte chunks (nchunks <= gridDim.x * kThreads * L,
+// (nchunks + gridDim.x * kThreads * L) * 16 < 2^31, nchunks > kResMaxWord / 2);
+// thread t of workgroup b
+// holds chunks c0 + k * gridDim.x * kThreads, c0 = b * kThreads + t, so each
+// wave load reads 1 KB contiguous.
+template <int L>
+__global__ __launch_bounds__(kThreads, 2) void resident_quant(const uint16_t* __restrict__ x,
+                                                              uint8_t* q, float* s,
+                                                              uint32_t nchunks,
+                                                              uint64_t wait_ticks) {
+  __shared__ uint32_t red[8];
+  const uint32_t t = threadIdx.x;
+  const uint32_t stride = gridDim.x * kThreads;
+  const uint32_t c0 = blockIdx.x * kThreads + t;
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x), (short)0, (int)(nchunks * 16u), kRawBufferFlags);
+  const __amdgpu_buffer_rsrc_t qr =
+      __builtin_amdgcn_make_buffer_rsrc(q, (short)0, (int)(nchunks * 8u), kRawBufferFlags);
+  u32x4 v[L];
+#pragma unroll
+  for (int k = 0; k < L; ++k) {
+    v[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         xr, (int)((c0 + (uint32_t)k * stride) * 16u), 0, kNtPolicy));
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < L; ++k) m = pk_max_u16(m, fold_abs(v[k]));
+  m = rows_max<0>(max16(halves_max(m)));
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  if (t == 0) {
+    red[4] = resident_arrive(max(max(red[0], red[1]), max(red[2], red[3])), q, s, wait_ticks);
+  }
+  __syncthreads();
+  uint32_t sv = red[4];
+  if (sv == kResNoScale) sv = resident_scan(xr, nchunks, red);
+  const float r = 1.0f / __uint_as_float(sv);
+  // Chunks 0 and 16 (workgroup 0) hold the handshake words: atomic exchange,
+  // and their buffer stores get an offset past the end, which drops them.
+  const bool word = blockIdx.x == 0 && (t == kResCountWord / 2 || t == kResMaxWord / 2);
+#pragma unroll
+  for (int k = 0; k < L; ++k) {
+    const u32x2 o = quant8(v[k], r);
+    if (k == 0 && word) {
+      __hip_atomic_exchange(reinterpret_cast<uint64_t*>(q + (size_t)c0 * 8u),
+                            (uint64_t)o.x | ((uint64_t)o.y << 32), __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const uint32_t off = (k == 0 && word) ? kResDropOffset : (c0 + (uint32_t)k * stride) * 8u;
+    __builtin_amdgcn_raw_buffer_store_b64(o, qr, (int)off, 0, kNtPolicy);
+  }
+}
+
 // ---------------------------------------------------------------- small tiles of shards
 //
 // Shards whose tiles hold at most kRegTile elements, with tile columns that

@@ -44,7 +44,13 @@
  *     than 65536 elements take two passes (maxima, then quantization), and
  *     between the passes q holds partial maxima until the codes replace
  *     them; all other cases take a general one-workgroup-per-tile kernel.
- *     Results are identical whichever kernel runs.
+ *     A whole tensor with one tile (bm >= M, bn >= N) of at least 2^20
+ *     values, aligned as above, that fits in the registers of the grid the
+ *     device holds at once (about 50 M values on an MI355X) is read once
+ *     and held in registers while the workgroups agree on its maximum
+ *     (fp8bq_set_resident_wait_us); during the call q's bytes 0..7 and
+ *     128..135 and scale_inv hold that handshake until the results replace
+ *     them.  Results are identical whichever kernel runs.
  *   - Thread safety: calls may be made from several host threads; each
  *     thread has its own fp8bq_last_hip_error().
  */
@@ -236,6 +242,20 @@ int fp8bq_dequantize(const void* q, const float* scale_inv, int64_t M, int64_t N
  *   y  device, fp32 [n];  q  device, uint8 [n];  n >= 0.
  */
 int fp8bq_encode_e4m3(const float* y, void* q, int64_t n, void* stream);
+
+/*
+ * Longest time a workgroup of the one-scale-per-tensor kernel held in
+ * registers waits for the tensor-wide maximum (the page "fp8_kernel.py — FP8
+ * 量化内核", section 2: the block maximum, here over one block that spans the
+ * tensor) before it reads all of x and computes that maximum itself.  The
+ * wait only runs long when the launch's workgroups are not all resident at
+ * once (e.g. beside another kernel); the results are the same either way.
+ *   microseconds  0 .. 2^40; default 2000.  0 makes every workgroup but the
+ *                 last to arrive compute the maximum itself (slow; for tests).
+ * Process-wide; applies to launches enqueued after the call.  Returns
+ * FP8BQ_OK or FP8BQ_ERR_INVALID_ARGUMENT; touches no device.
+ */
+int fp8bq_set_resident_wait_us(int64_t microseconds);
 
 /* Static English text for a status code (never NULL). */
 const char* fp8bq_status_string(int status);

@@ -55,6 +55,8 @@ int main(void) {
     expect(fp8bq_quantize_amax_many(sh, 0, 128, 128, NULL), FP8BQ_OK, "no shards");
   }
   expect(fp8bq_encode_e4m3(NULL, Q, 4, NULL), FP8BQ_ERR_INVALID_ARGUMENT, "null y");
+  expect(fp8bq_set_resident_wait_us(-1), FP8BQ_ERR_INVALID_ARGUMENT, "negative wait");
+  expect(fp8bq_set_resident_wait_us(2000), FP8BQ_OK, "default wait");
   expect(fp8bq_last_hip_error(), 0, "no HIP call made");
   if (failures == 0) printf("abi ok\n");
   return failures == 0 ? 0 : 1;

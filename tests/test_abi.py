@@ -190,6 +190,20 @@ def test_encode_rejects(lib):
     assert lib.fp8bq_encode_e4m3(None, None, 0, None) == fq.OK
 
 
+def test_resident_wait_limit(lib):
+    """The wait limit of the one-scale-per-tensor kernel: range checked, no
+    device touched, and the Python setter round-trips."""
+    assert lib.fp8bq_set_resident_wait_us(-1) == INVALID
+    assert lib.fp8bq_set_resident_wait_us(2 ** 40 + 1) == INVALID
+    assert lib.fp8bq_set_resident_wait_us(0) == fq.OK
+    assert lib.fp8bq_set_resident_wait_us(2 ** 40) == fq.OK
+    assert lib.fp8bq_set_resident_wait_us(2000) == fq.OK
+    with pytest.raises(fq.Fp8bqError):
+        fq.set_resident_wait_us(-5)
+    fq.set_resident_wait_us(2000)
+    assert lib.fp8bq_last_hip_error() == 0
+
+
 def test_dequantize_rejects(lib):
     f = lib.fp8bq_dequantize
     assert f(Q, S, -1, 128, 128, 128, X, 0, None) == INVALID        # negative M

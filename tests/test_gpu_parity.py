@@ -908,6 +908,76 @@ def test_per_tensor_vocab_matrix(gpu_lib):
     assert_properties_gpu(x, q, s, sp.M, sp.N, "vocab per-tensor")
 
 
+@pytest.mark.parametrize("M,N", [(1024, 1024),      # 2^20 values: 128 workgroups x 4 chunks
+                                 (1031, 1032),      # ragged: 65 x 8, loads past the end
+                                 (2048, 4096),      # 128 x 32
+                                 (4096, 4096),      # 256 x 32
+                                 (1, 2 ** 21 + 8),  # one row
+                                 (2 ** 17 + 3, 8)]) # eight columns
+def test_per_tensor_held_in_registers(gpu_lib, M, N):
+    """One scale per tensor through the kernel that holds the tensor in
+    registers: equal to the oracle byte for byte (including q bytes 0..7 and
+    128..135, which carry the cross-workgroup handshake during the call),
+    nothing written past q, the same through the grouped call, and the same
+    when every workgroup but the last computes the maximum itself."""
+    say("resident", M, N)
+    g = torch.Generator(device=DEV).manual_seed(M * 7 + N)
+    x = (torch.randn((M, N), generator=g, device=DEV) * 0.04).to(torch.bfloat16)
+    x.view(-1)[(M * N) // 2 + 5] = -1.75            # the maximum, held by one workgroup
+    buf = torch.full((M * N + 256,), 0x5A, dtype=torch.uint8, device=DEV)
+    q = buf[:M * N].view(M, N)
+    s = torch.empty((1, 1), dtype=torch.float32, device=DEV)
+    fq.quantize(x, (M, N), out=(q, s))
+    assert_matches_oracle(x, q, s, M, N, f"resident {M}x{N}")
+    assert bool((buf[M * N:] == 0x5A).all())
+    ((qg, sg),) = fq.quantize_many([x], (M, N))
+    assert torch.equal(qg.view(torch.uint8), q) and torch.equal(sg.view(torch.int32), s.view(torch.int32))
+    try:
+        fq.set_resident_wait_us(0)
+        q0, s0 = fq.quantize(x, (M, N))
+        torch.cuda.synchronize()
+    finally:
+        fq.set_resident_wait_us(2000)
+    assert torch.equal(q0.view(torch.uint8), q) and torch.equal(s0.view(torch.int32), s.view(torch.int32))
+
+
+def test_per_tensor_register_capacity(gpu_lib):
+    """12288x4096, the largest tensor the register-resident kernel holds on an
+    MI355X (512 workgroups x 256 threads x 48 chunks), and 12289x4096, one
+    row more, which takes the two-pass path: exact scales, sampled rows
+    against the oracle, invariants everywhere; a grouped call mixing both
+    with a misaligned and a small tensor equals the single calls."""
+    g = torch.Generator(device=DEV).manual_seed(83)
+    outs = []
+    xs = []
+    for M in (12288, 12289):
+        say("resident capacity", M)
+        x = (torch.randn((M, 4096), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+        x[M - 1, 4095] = 2.25
+        q, s = fq.quantize(x, (16384, 16384))
+        amax = float(x.abs().max().float())
+        assert amax == 2.25
+        assert float(s[0, 0]) == float(np.float32(np.float32(amax) / np.float32(448.0)))
+        for r0 in (0, 3001, M - 64):
+            band = x[r0:r0 + 64].contiguous()
+            q_ref, _ = oracle.quantize_with_amax(bits_np(band), 16384, 16384, np.array([[amax]]))
+            assert np.array_equal(codes_np(q[r0:r0 + 64].contiguous()), q_ref), (M, r0)
+        assert_properties_gpu(x, q, s, 16384, 16384, f"capacity {M}")
+        xs.append(x)
+        outs.append((q, s))
+    raw = (torch.randn(1500 * 1200 + 8, generator=g, device=DEV) * 0.1).to(torch.bfloat16)
+    mis = raw[1:1 + 1500 * 1200].view(1500, 1200)   # x not 16-byte aligned: two-pass path
+    small = (torch.randn((100, 200), generator=g, device=DEV)).to(torch.bfloat16)
+    group = [xs[0], mis, xs[1], small]
+    got = fq.quantize_many(group, (16384, 16384))
+    for i, x in enumerate(group):
+        q1, s1 = outs[i // 2] if i in (0, 2) else fq.quantize(x, (16384, 16384))
+        assert torch.equal(got[i][0].view(torch.uint8), q1.view(torch.uint8)), i
+        assert torch.equal(got[i][1].view(torch.int32), s1.view(torch.int32)), i
+    assert_matches_oracle(mis, got[1][0], got[1][1], 16384, 16384, "grouped misaligned")
+    del xs, outs, got
+
+
 # ------------------------------------------------------------------ maximum sizes
 
 def test_beyond_2_31_elements(gpu_lib):
