@@ -367,6 +367,7 @@ void launch_big_tensor(const fp8bq::Big& b, float* scale_inv, hipStream_t st) {
 // 10.6, 19.2 and 44.7 us.
 constexpr int64_t kResMinValues = int64_t{1} << 20;
 constexpr int kResPrepCap = 128;
+constexpr int kResGroupCap = 128;  // tensors per persistent resident launch
 constexpr int64_t kResWaitUsDefault = 2000;
 
 struct ResPlan {
@@ -381,21 +382,23 @@ std::atomic<int> g_res_grid[kMaxDevices];
 std::atomic<int> g_res_tick_mhz[kMaxDevices];
 std::atomic<int64_t> g_res_wait_us{kResWaitUsDefault};
 
-// Workgroups of the largest variant the current device holds at once, or 0.
+// Workgroups of the resident kernels the current device holds at once, or 0.
 int resident_capacity(int* tick_mhz) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
   int cap = g_res_grid[dev].load(std::memory_order_acquire);
   if (cap == 0) {
-    int per = 0, cus = 0, khz = 0;
+    int per = 0, per_group = 0, cus = 0, khz = 0;
     const bool ok =
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fp8bq::resident_quant<fp8bq::kResMaxLoads>,
                                                      fp8bq::kThreads, 0) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_group, fp8bq::resident_group<kResGroupCap>,
+                                                     fp8bq::kThreads, 0) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess &&
-        per > 0 && cus > 0 && khz >= 1000;
+        per > 0 && per_group > 0 && cus > 0 && khz >= 1000;
     (void)hipGetLastError();
-    cap = ok ? per * cus : -1;
+    cap = ok ? (per < per_group ? per : per_group) * cus : -1;
     g_res_tick_mhz[dev].store(ok ? khz / 1000 : 0, std::memory_order_relaxed);
     g_res_grid[dev].store(cap, std::memory_order_release);
   }
@@ -444,10 +447,14 @@ void launch_resident_prep(const fp8bq::ResTensor* ts, int n, hipStream_t st) {
   }
 }
 
+uint64_t resident_wait_ticks(int tick_mhz) {
+  return static_cast<uint64_t>(g_res_wait_us.load(std::memory_order_relaxed)) *
+         static_cast<uint64_t>(tick_mhz);
+}
+
 void launch_resident(const ResPlan& p, const void* x, void* q, float* s, int tick_mhz,
                      hipStream_t st) {
-  const uint64_t ticks = static_cast<uint64_t>(g_res_wait_us.load(std::memory_order_relaxed)) *
-                         static_cast<uint64_t>(tick_mhz);
+  const uint64_t ticks = resident_wait_ticks(tick_mhz);
   const uint16_t* xs = static_cast<const uint16_t*>(x);
   uint8_t* qs = static_cast<uint8_t*>(q);
   const dim3 g(p.grid), b(fp8bq::kThreads);
@@ -459,6 +466,39 @@ void launch_resident(const ResPlan& p, const void* x, void* q, float* s, int tic
     default:
       hipLaunchKernelGGL(fp8bq::resident_quant<fp8bq::kResMaxLoads>, g, b, 0, st, xs, qs, s, p.nchunks, ticks);
       break;
+  }
+}
+
+// Several resident tensors: persistent launches of up to kResGroupCap tensors
+// over at most `cap` workgroups; tensor i takes the next plan.grid
+// workgroups after tensor i-1's (wrapping around).
+
+void launch_resident_group(const std::vector<std::pair<const fp8bq_tensor*, ResPlan>>& res, int cap,
+                           int tick_mhz, hipStream_t st) {
+  const uint64_t ticks = resident_wait_ticks(tick_mhz);
+  for (size_t i0 = 0; i0 < res.size(); i0 += kResGroupCap) {
+    const size_t c = res.size() - i0 < static_cast<size_t>(kResGroupCap) ? res.size() - i0 : kResGroupCap;
+    int64_t want = 0;
+    for (size_t i = 0; i < c; ++i) want += res[i0 + i].second.grid;
+    const uint32_t g = static_cast<uint32_t>(want < cap ? want : cap);
+    fp8bq::ResGroupArgs<kResGroupCap> a;
+    std::memset(&a, 0, sizeof(a));
+    uint32_t cursor = 0;
+    for (size_t i = 0; i < c; ++i) {
+      const fp8bq_tensor& t = *res[i0 + i].first;
+      const ResPlan& p = res[i0 + i].second;
+      fp8bq::ResEntry& e = a.e[i];
+      e.x = static_cast<const uint16_t*>(t.x);
+      e.q = static_cast<uint8_t*>(t.q);
+      e.s = t.scale_inv;
+      e.nchunks = p.nchunks;
+      e.grid = p.grid;
+      e.first = cursor;
+      e.loads = p.L;
+      cursor = static_cast<uint32_t>((static_cast<uint64_t>(cursor) + p.grid) % g);
+    }
+    hipLaunchKernelGGL(fp8bq::resident_group<kResGroupCap>, dim3(g), dim3(fp8bq::kThreads), 0, st,
+                       a, static_cast<int32_t>(c), ticks);
   }
 }
 
@@ -818,8 +858,8 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (any_big) {
-    // Whole tensors that fit in registers: one resident launch each, after
-    // one preparation launch for all of them.
+    // Whole tensors that fit in registers: a preparation launch for all of
+    // them, then persistent resident launches.
     int tick_mhz = 0;
     const int cap = resident_capacity(&tick_mhz);
     std::vector<std::pair<const fp8bq_tensor*, ResPlan>> res;
@@ -836,7 +876,12 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
     }
     if (!res.empty()) {
       launch_resident_prep(res_t.data(), static_cast<int>(res_t.size()), s);
-      for (const auto& r : res) launch_resident(r.second, r.first->x, r.first->q, r.first->scale_inv, tick_mhz, s);
+      if (res.size() == 1) {
+        launch_resident(res[0].second, res[0].first->x, res[0].first->q, res[0].first->scale_inv,
+                        tick_mhz, s);
+      } else {
+        launch_resident_group(res, cap, tick_mhz, s);
+      }
     }
     // The other large-tile tensors: grouped two-pass launches, kBigGroupCap
     // tensors at a time.

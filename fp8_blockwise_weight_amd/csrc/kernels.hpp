@@ -999,12 +999,15 @@ __global__ __launch_bounds__(kThreads) void big_group_quant(const BigGroupArgs<C
 //     value); the workgroup that brings the count to the grid size reads the
 //     maximum, computes the scale and stores it to scale_inv;
 //   * the others poll scale_inv.  One that has waited longer than
-//     `wait_ticks` (100 MHz s_memrealtime ticks; the workgroups of a launch
-//     need not all be resident at once, e.g. beside another launch) computes
-//     the tensor's maximum itself from x: the scale is the same either way
-//     and no wait is unbounded;
-//   * the two q words are overwritten last by atomic exchanges, in the same
-//     coherence order as the handshake atomics.
+//     `wait_ticks` (s_memrealtime ticks; the workgroups of a launch need not
+//     all be resident at once, e.g. beside another launch) computes the
+//     tensor's maximum itself from x: the scale is the same either way and
+//     no wait is unbounded;
+//   * only the last workgroup to arrive, which comes after every handshake
+//     atomic, writes the codes of the two q chunks that hold the words
+//     (loading those 16 values of x itself), with atomic exchanges in the
+//     same coherence order; a workgroup past its wait limit may run ahead of
+//     late arrivals, so no other workgroup writes there.
 // Acquire/release ordering would make every workgroup write back and
 // invalidate its L2 (measured: a fixed ~15 us per launch), and nothing but
 // the atomics' values needs ordering.
@@ -1044,8 +1047,8 @@ __global__ void resident_prep(const ResPrepArgs<CAP> a, int32_t count) {
 
 // Thread 0 of a workgroup: contributes `bmax` and returns the scale's bits,
 // or kResNoScale when the wait limit passed first.
-__device__ __forceinline__ uint32_t resident_arrive(uint32_t bmax, uint8_t* q, float* s,
-                                                    uint64_t wait_ticks) {
+__device__ __forceinline__ uint32_t resident_arrive(const uint16_t* x, uint32_t bmax, uint8_t* q,
+                                                    float* s, uint32_t grid, uint64_t wait_ticks) {
   uint32_t* w = reinterpret_cast<uint32_t*>(q);
   uint32_t* sb = reinterpret_cast<uint32_t*>(s);
   const uint32_t prev =
@@ -1053,12 +1056,18 @@ __device__ __forceinline__ uint32_t resident_arrive(uint32_t bmax, uint8_t* q, f
   // prev <= 0x7FFF, so the operand is 1; the dependency orders the two atomics.
   const uint32_t old = __hip_atomic_fetch_add(&w[kResCountWord], 1u + (prev >> 31),
                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (old == gridDim.x - 1) {
+  if (old == grid - 1) {
     const uint32_t amax = __hip_atomic_load(&w[kResMaxWord], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     float sf, rf;
     tile_scale(amax, sf, rf);
     const uint32_t sv = __float_as_uint(sf);
     __hip_atomic_store(sb, sv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Every workgroup has arrived: the codes of the two handshake chunks.
+    for (int c : {kResCountWord / 2, kResMaxWord / 2}) {
+      const u32x2 o = quant8(*reinterpret_cast<const u32x4*>(x + c * 8), rf);
+      __hip_atomic_exchange(reinterpret_cast<uint64_t*>(q + c * 8), (uint64_t)o.x | ((uint64_t)o.y << 32),
+                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     return sv;
   }
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -1088,20 +1097,18 @@ __device__ __forceinline__ uint32_t resident_scan(__amdgpu_buffer_rsrc_t xr, uin
   return __float_as_uint(sf);
 }
 
-// One tensor of nchunks 16-byte chunks (nchunks <= gridDim.x * kThreads * L,
-// (nchunks + gridDim.x * kThreads * L) * 16 < 2^31, nchunks > kResMaxWord / 2);
-// thread t of workgroup b
-// holds chunks c0 + k * gridDim.x * kThreads, c0 = b * kThreads + t, so each
-// wave load reads 1 KB contiguous.
+// One tensor of nchunks 16-byte chunks on `grid` workgroups, this one being
+// number b (nchunks <= grid * kThreads * L, (nchunks + grid * kThreads * L)
+// * 16 < 2^31, nchunks > kResMaxWord / 2).  Thread t holds chunks
+// c0 + k * grid * kThreads, c0 = b * kThreads + t, so each wave load reads
+// 1 KB contiguous.
 template <int L>
-__global__ __launch_bounds__(kThreads, 2) void resident_quant(const uint16_t* __restrict__ x,
-                                                              uint8_t* q, float* s,
-                                                              uint32_t nchunks,
-                                                              uint64_t wait_ticks) {
-  __shared__ uint32_t red[8];
+__device__ __forceinline__ void resident_body(const uint16_t* __restrict__ x, uint8_t* q, float* s,
+                                              uint32_t nchunks, uint32_t grid, uint32_t b,
+                                              uint64_t wait_ticks, uint32_t* red) {
   const uint32_t t = threadIdx.x;
-  const uint32_t stride = gridDim.x * kThreads;
-  const uint32_t c0 = blockIdx.x * kThreads + t;
+  const uint32_t stride = grid * kThreads;
+  const uint32_t c0 = b * kThreads + t;
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(x), (short)0, (int)(nchunks * 16u), kRawBufferFlags);
   const __amdgpu_buffer_rsrc_t qr =
@@ -1119,25 +1126,73 @@ __global__ __launch_bounds__(kThreads, 2) void resident_quant(const uint16_t* __
   if ((t & 63) == 0) red[t >> 6] = m;
   __syncthreads();
   if (t == 0) {
-    red[4] = resident_arrive(max(max(red[0], red[1]), max(red[2], red[3])), q, s, wait_ticks);
+    red[4] = resident_arrive(x, max(max(red[0], red[1]), max(red[2], red[3])), q, s, grid, wait_ticks);
   }
   __syncthreads();
   uint32_t sv = red[4];
   if (sv == kResNoScale) sv = resident_scan(xr, nchunks, red);
   const float r = 1.0f / __uint_as_float(sv);
-  // Chunks 0 and 16 (workgroup 0) hold the handshake words: atomic exchange,
-  // and their buffer stores get an offset past the end, which drops them.
-  const bool word = blockIdx.x == 0 && (t == kResCountWord / 2 || t == kResMaxWord / 2);
+  // Chunks 0 and 16 hold the handshake words, which the last workgroup to
+  // arrive writes: workgroup 0's stores there get an offset past the end,
+  // which drops them.
+  const bool word = b == 0 && (t == kResCountWord / 2 || t == kResMaxWord / 2);
 #pragma unroll
   for (int k = 0; k < L; ++k) {
     const u32x2 o = quant8(v[k], r);
-    if (k == 0 && word) {
-      __hip_atomic_exchange(reinterpret_cast<uint64_t*>(q + (size_t)c0 * 8u),
-                            (uint64_t)o.x | ((uint64_t)o.y << 32), __ATOMIC_RELAXED,
-                            __HIP_MEMORY_SCOPE_AGENT);
-    }
     const uint32_t off = (k == 0 && word) ? kResDropOffset : (c0 + (uint32_t)k * stride) * 8u;
     __builtin_amdgcn_raw_buffer_store_b64(o, qr, (int)off, 0, kNtPolicy);
+  }
+}
+
+template <int L>
+__global__ __launch_bounds__(kThreads, 2) void resident_quant(const uint16_t* __restrict__ x,
+                                                              uint8_t* q, float* s,
+                                                              uint32_t nchunks,
+                                                              uint64_t wait_ticks) {
+  __shared__ uint32_t red[8];
+  resident_body<L>(x, q, s, nchunks, gridDim.x, blockIdx.x, wait_ticks, red);
+}
+
+// A list of such tensors in one persistent launch: tensor i runs on the
+// `grid` workgroups first, first + 1, ... (mod gridDim.x), and every
+// workgroup takes its tensors in list order, so tensors on disjoint
+// workgroups run side by side and no workgroup waits at a kernel boundary.
+// A workgroup only ever waits for workgroups of the same tensor, which are
+// at that tensor or at an earlier one, so the waits always end when the
+// launch's workgroups are resident together (and the wait limit covers the
+// case where they are not).
+struct ResEntry {
+  const uint16_t* x;
+  uint8_t* q;
+  float* s;
+  uint32_t nchunks;
+  uint32_t grid;
+  uint32_t first;
+  int32_t loads;  // L: 4, 8, 16, 32 or kResMaxLoads
+};
+
+template <int CAP>
+struct ResGroupArgs {
+  ResEntry e[CAP];
+};
+
+template <int CAP>
+__global__ __launch_bounds__(kThreads, 2) void resident_group(const ResGroupArgs<CAP> a,
+                                                              int32_t count,
+                                                              uint64_t wait_ticks) {
+  __shared__ uint32_t red[8];
+  for (int32_t i = 0; i < count; ++i) {
+    const ResEntry& e = a.e[i];
+    const uint32_t b = blockIdx.x >= e.first ? blockIdx.x - e.first : blockIdx.x + gridDim.x - e.first;
+    if (b >= e.grid) continue;
+    __syncthreads();  // red[] of the previous tensor is no longer read
+    switch (e.loads) {
+      case 4: resident_body<4>(e.x, e.q, e.s, e.nchunks, e.grid, b, wait_ticks, red); break;
+      case 8: resident_body<8>(e.x, e.q, e.s, e.nchunks, e.grid, b, wait_ticks, red); break;
+      case 16: resident_body<16>(e.x, e.q, e.s, e.nchunks, e.grid, b, wait_ticks, red); break;
+      case 32: resident_body<32>(e.x, e.q, e.s, e.nchunks, e.grid, b, wait_ticks, red); break;
+      default: resident_body<kResMaxLoads>(e.x, e.q, e.s, e.nchunks, e.grid, b, wait_ticks, red); break;
+    }
   }
 }
 

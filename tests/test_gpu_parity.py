@@ -978,6 +978,41 @@ def test_per_tensor_register_capacity(gpu_lib):
     del xs, outs, got
 
 
+def test_per_tensor_resident_groups(gpu_lib):
+    """Grouped one-scale-per-tensor calls through the persistent resident
+    launch: 300 tensors of mixed sizes (three launches of up to 128 tensors,
+    tensors on disjoint and wrapping workgroup ranges) equal the single calls,
+    also when every workgroup but the last of each tensor computes the
+    maximum itself; a few against the oracle."""
+    g = torch.Generator(device=DEV).manual_seed(89)
+    rng = np.random.default_rng(89)
+    shapes = [(1024, 1024), (1031, 1032), (2048, 1024), (512, 4096), (4096, 1024), (1100, 3000)]
+    xs = []
+    for i in range(300):
+        M, N = shapes[int(rng.integers(len(shapes)))]
+        x = (torch.randn((M, N), generator=g, device=DEV) * float(rng.uniform(0.01, 0.1))).to(torch.bfloat16)
+        x.view(-1)[int(rng.integers(M * N))] = float(rng.uniform(-3, 3))
+        xs.append(x)
+    xs[7] = torch.zeros_like(xs[7])
+    block = (8192, 8192)
+    outs = fq.quantize_many(xs, block)
+    singles = [fq.quantize(x, block) for x in xs]
+    for i, ((q, s), (q1, s1)) in enumerate(zip(outs, singles)):
+        assert torch.equal(q.view(torch.uint8), q1.view(torch.uint8)), i
+        assert torch.equal(s.view(torch.int32), s1.view(torch.int32)), i
+    for i in (0, 7, 150, 299):
+        assert_matches_oracle(xs[i], outs[i][0], outs[i][1], *block, f"resident group [{i}]")
+    try:
+        fq.set_resident_wait_us(0)
+        outs0 = fq.quantize_many(xs[:40], block)
+        torch.cuda.synchronize()
+    finally:
+        fq.set_resident_wait_us(2000)
+    for i, (q, s) in enumerate(outs0):
+        assert torch.equal(q.view(torch.uint8), outs[i][0].view(torch.uint8)), i
+        assert torch.equal(s.view(torch.int32), outs[i][1].view(torch.int32)), i
+
+
 # ------------------------------------------------------------------ maximum sizes
 
 def test_beyond_2_31_elements(gpu_lib):
