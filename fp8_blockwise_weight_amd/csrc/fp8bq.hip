@@ -367,7 +367,7 @@ void launch_big_tensor(const fp8bq::Big& b, float* scale_inv, hipStream_t st) {
 // 10.6, 19.2 and 44.7 us.
 constexpr int64_t kResMinValues = int64_t{1} << 20;
 constexpr int kResPrepCap = 128;
-constexpr int kResGroupCap = 128;  // tensors per persistent resident launch
+constexpr int kResGroupCap = 256;  // tensors per persistent resident launch
 constexpr int64_t kResWaitUsDefault = 2000;
 
 struct ResPlan {
@@ -471,7 +471,8 @@ void launch_resident(const ResPlan& p, const void* x, void* q, float* s, int tic
 
 // Several resident tensors: persistent launches of up to kResGroupCap tensors
 // over at most `cap` workgroups; tensor i takes the next plan.grid
-// workgroups after tensor i-1's (wrapping around).
+// workgroups after tensor i-1's (wrapping around).  256 tensors per launch
+// against 128: 8 MoE layers (384 tensors each) 66.7% -> 68.2% of peak.
 
 void launch_resident_group(const std::vector<std::pair<const fp8bq_tensor*, ResPlan>>& res, int cap,
                            int tick_mhz, hipStream_t st) {
@@ -875,6 +876,17 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
       res_t.push_back(fp8bq::ResTensor{static_cast<uint8_t*>(t.q), t.scale_inv});
     }
     if (!res.empty()) {
+      if (res.size() > 1) {
+        // Side by side in a persistent launch, the fewest workgroups per
+        // tensor (48 chunks per thread) measured best: dense set 66.7% ->
+        // 68.6% of peak, one layer 64.5% -> 69.4%, 8 MoE layers 52.6% ->
+        // 66.4% (32 chunks: 67.3 / 67.8 / 64.8%; 16: 62.7 / 59.3 / 54.5%).
+        for (auto& r : res) {
+          const int64_t g = ceil_div(r.second.nchunks, int64_t{fp8bq::kThreads} * fp8bq::kResMaxLoads);
+          r.second.L = fp8bq::kResMaxLoads;
+          r.second.grid = static_cast<uint32_t>(g);
+        }
+      }
       launch_resident_prep(res_t.data(), static_cast<int>(res_t.size()), s);
       if (res.size() == 1) {
         launch_resident(res[0].second, res[0].first->x, res[0].first->q, res[0].first->scale_inv,
