@@ -213,6 +213,72 @@ def test_concurrent_host_threads(gpu_lib):
             assert torch.equal(q.view(torch.uint8), qr), i
 
 
+def test_per_tensor_held_in_registers_beside_other_streams(gpu_lib):
+    """One-scale-per-tensor lists (persistent launches that hold tensors in
+    registers and wait for each other's maxima) on two streams at once, next
+    to a [128,128] launch on a third: the launches compete for the CUs, so
+    workgroups may not be resident together and some may pass the wait limit
+    and compute maxima themselves.  Every byte equals the sequential results,
+    with the default limit and with a 20 us limit.  A captured single call
+    replays to the same bytes."""
+    g = torch.Generator(device=DEV).manual_seed(97)
+    lists = [[(torch.randn((2048, 2048), generator=g, device=DEV) * (0.01 * (i + 1))).to(torch.bfloat16)
+              for i in range(40)] for _ in range(2)]
+    dense = [wl.materialize(sp, DEV) for sp in wl.c2()]
+    block = (4096, 4096)
+    ref = [[(q.view(torch.uint8).clone(), s.clone()) for q, s in fq.quantize_many(xs, block)] for xs in lists]
+    ref_dense = [(q.view(torch.uint8).clone(), s.clone()) for q, s in fq.quantize_many(dense, (128, 128))]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    try:
+        for wait_us in (2000, 20):
+            _say("concurrent resident lists, wait limit", wait_us)
+            fq.set_resident_wait_us(wait_us)
+            for rep in range(2):
+                got = [None, None]
+                for st in streams:
+                    st.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(streams[2]):
+                    got_dense = fq.quantize_many(dense, (128, 128))
+                for i in range(2):
+                    with torch.cuda.stream(streams[i]):
+                        got[i] = fq.quantize_many(lists[i], block)
+                torch.cuda.synchronize()
+                for i in range(2):
+                    for j, ((q, s), (qr, sr)) in enumerate(zip(got[i], ref[i])):
+                        assert torch.equal(q.view(torch.uint8), qr), (wait_us, rep, i, j)
+                        assert torch.equal(s.view(torch.int32), sr.view(torch.int32)), (wait_us, rep, i, j)
+                for (q, s), (qr, sr) in zip(got_dense, ref_dense):
+                    assert torch.equal(q.view(torch.uint8), qr) and torch.equal(s, sr)
+    finally:
+        fq.set_resident_wait_us(2000)
+    # a captured single call (prep + resident kernel), replayed with eager work between
+    x = wl.materialize(wl.c2()[0], DEV)                    # 4096x4096: one resident launch
+    q = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=DEV)
+    s = torch.empty((1, 1), dtype=torch.float32, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fq.quantize(x, (4096, 4096), out=(q, s))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fq.quantize(x, (4096, 4096), out=(q, s))
+    torch.cuda.synchronize()
+    for rep in range(3):
+        _say("resident graph replay", rep)
+        x.mul_(-1.5 if rep % 2 else 0.75)
+        q.view(torch.uint8).fill_(0xA5)
+        s.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        q1, s1 = fq.quantize(x, (4096, 4096))
+        assert torch.equal(q1.view(torch.uint8), q.view(torch.uint8)), rep
+        assert torch.equal(s1.view(torch.int32), s.view(torch.int32)), rep
+
+
 def test_error_reporting_on_device(gpu_lib):
     """Argument errors raise with the library's status text; nothing is
     launched (outputs keep their fill)."""
