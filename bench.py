@@ -112,6 +112,31 @@ def group_kernel_name(kind, count, flat=False):
     return f"fp8bq::quantize_group<{kind}>"
 
 
+RESIDENT_MIN_VALUES = 1 << 20          # smallest tensor held in registers
+RESIDENT_CAPACITY = 512 * 256 * 48 * 8  # values the MI355X holds in registers (2 workgroups per CU)
+
+
+def call_kernels(specs, bm, bn, kind, flat):
+    """(label, kernel launches) of one fp8bq_quantize_many call over `specs`,
+    mirroring the library's choice (the label only; timing does not use it).
+    Lists of whole one-tile tensors that fit in registers take a preparation
+    launch and a persistent resident launch per 256 tensors; other tiles
+    above 65536 elements take the grouped two-pass kernels, 3 launches per
+    128 tensors."""
+    n = len(specs)
+    one_tile = all(sp.M <= bm and sp.N <= bn for sp in specs)
+    big = all(min(sp.M, bm) * min(sp.N, bn) > 65536 for sp in specs)
+    if one_tile and all(sp.N % 8 == 0 and RESIDENT_MIN_VALUES <= sp.M * sp.N <= RESIDENT_CAPACITY
+                        for sp in specs):
+        calls = -(-n // 256)
+        if n == 1:
+            return "fp8bq::resident_prep<256> + fp8bq::resident_quant<L>", 2
+        return "fp8bq::resident_prep<256> + fp8bq::resident_group<256>", 2 * calls
+    if big:
+        return "fp8bq::big_group_max/reduce/quant<128>", 3 * -(-n // 128)
+    return group_kernel_name(kind, n, flat), 1
+
+
 def build_workload(name, dev, block=None):
     import torch  # noqa: F401
     from fp8_blockwise_weight_amd import workloads as wl
@@ -282,6 +307,7 @@ def main():
             all(sp.N % 512 == 0 for sp in specs)
             and sum(-(-sp.M // 128) * (sp.N // 512) for sp in specs) >= 8192 for specs in groups):
         kind = "kT128W"
+    label, kernels = call_kernels(max(groups, key=len), bm, bn, kind, flat)
     roofline = {
         "bound": "hbm",
         "achieved": round(achieved, 1),
@@ -289,8 +315,8 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": traffic,
-        "kernel": f"{group_kernel_name(kind, max(c for _, c, _ in calls), flat)} "
-                  f"({'one launch' if launches == 1 else f'{launches} launches'} per step)",
+        "kernel": f"{label} ({'one call' if launches == 1 else f'{launches} calls'} per step, "
+                  f"{'one kernel launch' if kernels == 1 else f'{kernels} kernel launches'} per call)",
         "bytes_per_launch": bytes_per_launch,
         "mean_launch_ms": round(mean_launch_ms, 4),
         "median_launch_ms": round(sorted(ev_ms)[len(ev_ms) // 2] / launches, 4),

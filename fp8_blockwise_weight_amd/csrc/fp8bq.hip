@@ -366,8 +366,8 @@ void launch_big_tensor(const fp8bq::Big& b, float* scale_inv, hipStream_t st) {
 // 512 x 16 17.1 us; 12288x4096: 512 x 48 29.4 us).  The two-pass path took
 // 10.6, 19.2 and 44.7 us.
 constexpr int64_t kResMinValues = int64_t{1} << 20;
-constexpr int kResPrepCap = 128;
 constexpr int kResGroupCap = 256;  // tensors per persistent resident launch
+constexpr int kResPrepCap = kResGroupCap;
 constexpr int64_t kResWaitUsDefault = 2000;
 
 struct ResPlan {

@@ -85,3 +85,22 @@ def test_kernel_fingerprint_ignores_comments_only():
     assert bench._code_only(base) != bench._code_only(other)
     assert bench._code_only('const char* s = "//x";') == 'const char* s = "//x";'
     assert len(bench.kernel_sha()) == 16
+
+
+def test_call_kernels_label_mirrors_library_choice():
+    """The bench's label of what one grouped call launches follows the
+    library's rules: the four-tile [128,128] kernel for the dense set, the
+    register-resident pair for one-tile lists within capacity, the two-pass
+    kernels beyond it."""
+    import bench
+    from fp8_blockwise_weight_amd import workloads as wl
+
+    assert bench.call_kernels(wl.c3(), 128, 128, "kT128W", False) == (
+        "fp8bq::quantize_group_args<kT128W,512>", 1)
+    label, k = bench.call_kernels(wl.c3(), 12288, 12288, "kGeneral", False)
+    assert "resident_group<256>" in label and k == 2
+    label, k = bench.call_kernels(wl.c2()[:1], 4096, 4096, "kGeneral", False)
+    assert "resident_quant" in label and k == 2
+    vocab = [s for s in wl.c5() if s.M == 151937]
+    assert bench.call_kernels(vocab, 151937, 4096, "kGeneral", False)[1] == 3
+    assert bench.RESIDENT_CAPACITY == 12288 * 4096
