@@ -1211,35 +1211,13 @@ __global__ __launch_bounds__(kThreads, 2) void resident_group(const ResGroupArgs
 // magnitude).  PASS 1: quantize with a = amax[tile], out[tile] = s.  `amax`
 // may be `out` itself: every thread takes a from LDS after a barrier, so the
 // tile's entry is read before thread 0 overwrites it.
-template <int PASS>
-__device__ __forceinline__ void shard_small_tile(const Big& b, int64_t tile, const float* amax,
-                                                 float* out, uint32_t* red) {
+// The tile's values v[0..7] are loaded; off(k) is vector k's element offset
+// from the tile's origin and valid(k) says whether it lies in the tile.
+template <int PASS, typename Off, typename Valid>
+__device__ __forceinline__ void shard_tile_finish(const Big& b, int64_t tile, size_t base,
+                                                  const u32x4 (&v)[8], Off off, Valid valid,
+                                                  float* out, uint32_t* red) {
   const int t = threadIdx.x;
-  const int64_t ti = tile / b.TNl;
-  const int64_t tj = tile - ti * b.TNl;
-  int64_t r0, r1, c0, c1;
-  big_rect(b, ti, tj, r0, r1, c0, c1);
-  const uint32_t vpr = (uint32_t)(c1 - c0) / 8;
-  const uint32_t nvec = (uint32_t)(r1 - r0) * vpr;  // <= kRegTile / 8 = 8 per thread
-  const size_t base = (size_t)r0 * b.N + c0;
-  const FP8BQ_GLOBAL uint16_t* x = (const FP8BQ_GLOBAL uint16_t*)(b.x + base);
-  float sc = 0.0f, r = 0.0f;
-  if (PASS == 1) {
-    if (t == 0) red[4] = __float_as_uint(((const FP8BQ_GLOBAL float*)amax)[tile]);
-  }
-  u32x4 v[8];
-  size_t off[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint32_t vi = (uint32_t)t + (uint32_t)k * kThreads;
-    if (vi < nvec) {
-      const uint32_t rr = vi / vpr;
-      off[k] = (size_t)rr * b.N + (size_t)(vi - rr * vpr) * 8;
-      v[k] = __builtin_nontemporal_load((const FP8BQ_GLOBAL u32x4*)(x + off[k]));
-    } else {
-      v[k] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
   if (PASS == 0) {
     uint32_t m = 0;
 #pragma unroll
@@ -1252,15 +1230,69 @@ __device__ __forceinline__ void shard_small_tile(const Big& b, int64_t tile, con
     if (t == 0) ((FP8BQ_GLOBAL float*)out)[tile] = __uint_as_float(tm << 16);
   } else {
     __syncthreads();
+    float sc, r;
     tile_scale_f(__uint_as_float(red[4]), sc, r);
     FP8BQ_GLOBAL uint8_t* q = (FP8BQ_GLOBAL uint8_t*)(b.q + base);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const uint32_t vi = (uint32_t)t + (uint32_t)k * kThreads;
-      if (vi < nvec) __builtin_nontemporal_store(quant8(v[k], r), (FP8BQ_GLOBAL u32x2*)(q + off[k]));
+      if (valid(k)) __builtin_nontemporal_store(quant8(v[k], r), (FP8BQ_GLOBAL u32x2*)(q + off(k)));
     }
     if (t == 0) ((FP8BQ_GLOBAL float*)out)[tile] = sc;
   }
+}
+
+// PASS 0: out[tile] = max |x| over the tile's part (fp32 of the BF16
+// magnitude).  PASS 1: quantize with a = amax[tile], out[tile] = s.  `amax`
+// may be `out` itself: every thread takes a from LDS after a barrier, so the
+// tile's entry is read before thread 0 overwrites it.  A whole tile of
+// exactly kRegTile elements whose 8-column groups per row divide the
+// workgroup (every interior [128,128] tile) takes a branch-free body: thread
+// t holds row t / groups + k * (256 / groups), one strided address per load
+// (151937x4096 shard at phase (64, 0): maxima pass 86.3% -> 89.3% of peak,
+// quantize pass 72.3% -> 77.4%).
+template <int PASS>
+__device__ __forceinline__ void shard_small_tile(const Big& b, int64_t tile, const float* amax,
+                                                 float* out, uint32_t* red) {
+  const int t = threadIdx.x;
+  const int64_t ti = tile / b.TNl;
+  const int64_t tj = tile - ti * b.TNl;
+  int64_t r0, r1, c0, c1;
+  big_rect(b, ti, tj, r0, r1, c0, c1);
+  const uint32_t vpr = (uint32_t)(c1 - c0) / 8;
+  const uint32_t nvec = (uint32_t)(r1 - r0) * vpr;  // <= kRegTile / 8 = 8 per thread
+  const size_t base = (size_t)r0 * b.N + c0;
+  const FP8BQ_GLOBAL uint16_t* x = (const FP8BQ_GLOBAL uint16_t*)(b.x + base);
+  if (PASS == 1) {
+    if (t == 0) red[4] = __float_as_uint(((const FP8BQ_GLOBAL float*)amax)[tile]);
+  }
+  u32x4 v[8];
+  if (nvec == (uint32_t)(kRegTile / 8) && (kThreads % vpr) == 0u) {
+    const uint32_t sh = (uint32_t)__builtin_ctz(vpr);
+    const size_t lane = (size_t)((uint32_t)t >> sh) * b.N + (size_t)((uint32_t)t & (vpr - 1u)) * 8;
+    const size_t step = (size_t)(kThreads >> sh) * b.N;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      v[k] = __builtin_nontemporal_load((const FP8BQ_GLOBAL u32x4*)(x + lane + (size_t)k * step));
+    }
+    shard_tile_finish<PASS>(b, tile, base, v, [&](int k) { return lane + (size_t)k * step; },
+                            [](int) { return true; }, out, red);
+    return;
+  }
+  size_t off[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t vi = (uint32_t)t + (uint32_t)k * kThreads;
+    if (vi < nvec) {
+      const uint32_t rr = vi / vpr;
+      off[k] = (size_t)rr * b.N + (size_t)(vi - rr * vpr) * 8;
+      v[k] = __builtin_nontemporal_load((const FP8BQ_GLOBAL u32x4*)(x + off[k]));
+    } else {
+      off[k] = 0;
+      v[k] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  shard_tile_finish<PASS>(b, tile, base, v, [&](int k) { return off[k]; },
+                          [&](int k) { return (uint32_t)t + (uint32_t)k * kThreads < nvec; }, out, red);
 }
 
 // Shards with one-row tiles of at most 128 columns ([1, bn], bn <= 128 and a
