@@ -388,17 +388,32 @@ __device__ __forceinline__ void reg_tile(const Desc& d, int32_t bm, int32_t bn, 
   const size_t base = (size_t)r0 * d.N + c0;
   const FP8BQ_GLOBAL uint16_t* x = (const FP8BQ_GLOBAL uint16_t*)(d.x + base);
   FP8BQ_GLOBAL uint8_t* q = (FP8BQ_GLOBAL uint8_t*)(d.q + base);
+  // A whole tile of exactly kRegTile elements whose 8-column groups per row
+  // divide the workgroup: thread t holds row t / groups + k * (256 / groups),
+  // one strided address per load and no per-load branch.
+  const bool whole = nvec == (uint32_t)(kRegTile / 8) && (kThreads % vpr) == 0u;
+  const uint32_t sh = whole ? (uint32_t)__builtin_ctz(vpr) : 0u;
+  const size_t lane = (size_t)((uint32_t)t >> sh) * d.N + (size_t)((uint32_t)t & (vpr - 1u)) * 8;
+  const size_t step = (size_t)(kThreads >> sh) * d.N;
   u32x4 v[8];
   size_t off[8];
+  if (whole) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint32_t vi = (uint32_t)t + (uint32_t)k * kThreads;
-    if (vi < nvec) {
-      const uint32_t rr = vi / vpr;
-      off[k] = (size_t)rr * d.N + (size_t)(vi - rr * vpr) * 8;
-      v[k] = __builtin_nontemporal_load((const FP8BQ_GLOBAL u32x4*)(x + off[k]));
-    } else {
-      v[k] = u32x4{0u, 0u, 0u, 0u};
+    for (int k = 0; k < 8; ++k) {
+      v[k] = __builtin_nontemporal_load((const FP8BQ_GLOBAL u32x4*)(x + lane + (size_t)k * step));
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t vi = (uint32_t)t + (uint32_t)k * kThreads;
+      if (vi < nvec) {
+        const uint32_t rr = vi / vpr;
+        off[k] = (size_t)rr * d.N + (size_t)(vi - rr * vpr) * 8;
+        v[k] = __builtin_nontemporal_load((const FP8BQ_GLOBAL u32x4*)(x + off[k]));
+      } else {
+        off[k] = 0;
+        v[k] = u32x4{0u, 0u, 0u, 0u};
+      }
     }
   }
   uint32_t m = 0;
@@ -411,10 +426,17 @@ __device__ __forceinline__ void reg_tile(const Desc& d, int32_t bm, int32_t bn, 
   const uint32_t tm = max(max(red[0], red[1]), max(red[2], red[3]));
   float s, r;
   tile_scale(tm, s, r);
+  if (whole) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint32_t vi = (uint32_t)t + (uint32_t)k * kThreads;
-    if (vi < nvec) __builtin_nontemporal_store(quant8(v[k], r), (FP8BQ_GLOBAL u32x2*)(q + off[k]));
+    for (int k = 0; k < 8; ++k) {
+      __builtin_nontemporal_store(quant8(v[k], r), (FP8BQ_GLOBAL u32x2*)(q + lane + (size_t)k * step));
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t vi = (uint32_t)t + (uint32_t)k * kThreads;
+      if (vi < nvec) __builtin_nontemporal_store(quant8(v[k], r), (FP8BQ_GLOBAL u32x2*)(q + off[k]));
+    }
   }
   if (t == 0) ((FP8BQ_GLOBAL float*)d.s)[(size_t)ti * d.TN + tj] = s;
 }
