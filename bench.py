@@ -301,12 +301,12 @@ def main():
     traffic = committed_traffic() if args.workload == "dense" else None
     kind = {(128, 128): "kT128", (64, 64): "kT64", (1, 128): "kR128"}.get((bm, bn), "kGeneral")
     flat = kind == "kR128" and all(sp.N % 128 == 0 for specs in groups for sp in specs)
-    # the library's choice of the wide [128,128] unit, per launch: every width a
-    # multiple of 512 and at least 8192 wide units (the label only)
-    if kind == "kT128" and all(
+    # the library's choice of the wide [128,128] / [64,64] unit, per launch:
+    # every width a multiple of 512 and at least 8192 wide units (the label only)
+    if kind in ("kT128", "kT64") and all(
             all(sp.N % 512 == 0 for sp in specs)
-            and sum(-(-sp.M // 128) * (sp.N // 512) for sp in specs) >= 8192 for specs in groups):
-        kind = "kT128W"
+            and sum(-(-sp.M // bm) * (sp.N // 512) for sp in specs) >= 8192 for specs in groups):
+        kind += "W"
     label, kernels = call_kernels(max(groups, key=len), bm, bn, kind, flat)
     roofline = {
         "bound": "hbm",

@@ -42,17 +42,25 @@ constexpr int64_t kMaxGrid = static_cast<int64_t>(UINT32_MAX) / fp8bq::kThreads;
 //     [64,64] 75% at 4 per CU -> 79.6%, [1,128] 74% -> 77.5%).
 constexpr unsigned kLds4PerCu = 36 * 1024;  // 160 KB / 36 KB -> 4 workgroups
 constexpr unsigned kLds6PerCu = 26 * 1024;  // 160 KB / 26 KB -> 6 workgroups
+constexpr unsigned kLds3PerCu = 44 * 1024;  // 160 KB / 44 KB -> 3 workgroups
+constexpr unsigned kLds2PerCu = 64 * 1024;  // 160 KB / 64 KB -> 2 workgroups
 
 // The wide [128,128] unit needs no reserve: its ~224 VGPRs already hold a
-// CU to 2 workgroups (64 KB of tile data each in flight).
-constexpr unsigned lds_for(int kind) {
-  return kind == fp8bq::kGeneral || kind == fp8bq::kT128W
+// CU to 2 workgroups (64 KB of tile data each in flight).  The wide [64,64]
+// unit (64 KB per workgroup, ~95 VGPRs) runs best at 2 per CU in launches of
+// up to 8 tensors (151937x4096: 82.4%, against 80.9% at 3 and 79.6% at 4)
+// and at 3 per CU with larger tables (dense 36-layer set: 81.0%, 75.8% at
+// 2), whose per-unit table search needs the extra waves.
+constexpr unsigned lds_for(int kind, int32_t count = 1) {
+  return kind == fp8bq::kT64W ? (count <= 8 ? kLds2PerCu : kLds3PerCu)
+         : kind == fp8bq::kGeneral || kind == fp8bq::kT128W
              ? 0u
              : (kind == fp8bq::kT128 ? kLds4PerCu : kLds6PerCu);
 }
 
-// [128,128] launches take the wide unit (kT128W, four tiles per workgroup)
-// when every vector-body tensor is a whole number of 512-column units wide
+// [128,128] launches take the wide unit (kT128W, four tiles per workgroup),
+// and [64,64] launches theirs (kT64W, eight tiles), when every vector-body
+// tensor is a whole number of 512-column units wide
 // (no half-empty units) and the launch has at least kWideMinUnits of them
 // (16 rounds of the 512 workgroups the chip holds), so that the 4x larger
 // units still spread evenly.  Measured: the dense 36-layer set 77.1% ->
@@ -96,16 +104,24 @@ int kind_of(int32_t bm, int32_t bn) {
   return fp8bq::kGeneral;
 }
 
-// Wide [128,128] units of one tensor: 0 when it takes a general body (it
-// does not constrain the choice), -1 when its width is not a whole number of
-// 512-column units.
-int64_t wide_units(const void* x, int64_t M, int64_t N, const void* q) {
+// Wide units (128 or 64 rows x 512 columns) of one tensor: 0 when it takes a
+// general body (it does not constrain the choice), -1 when its width is not
+// a whole number of 512-column units.
+int64_t wide_units(const void* x, int64_t M, int64_t N, const void* q, int64_t rows = 128) {
   if (M <= 0 || N <= 0) return 0;
   const bool aligned = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
                        (reinterpret_cast<uintptr_t>(q) & 7) == 0;
   if (!aligned) return 0;
   if (N % 512 != 0) return -1;
-  return ceil_div(M, 128) * (N / 512);
+  return ceil_div(M, rows) * (N / 512);
+}
+
+// The wide kind of a [128,128] or [64,64] launch whose tensors' wide-unit
+// counts (wide_units) sum to `wide` (negative: some width is not a whole
+// number of 512-column units), or `kind` itself.
+int wide_kind(int kind, int64_t wide) {
+  if (wide < kWideMinUnits) return kind;
+  return kind == fp8bq::kT128 ? fp8bq::kT128W : (kind == fp8bq::kT64 ? fp8bq::kT64W : kind);
 }
 
 // Checks one tensor and fills its descriptor.  Returns FP8BQ_OK with
@@ -149,7 +165,7 @@ int make_desc(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, void*
     u = ceil_div(M * (N / 128), 64);
   } else if (vec) {
     const int64_t rows = kind == fp8bq::kT128 || kind == fp8bq::kT128W ? 128 : 64;
-    d->UN = static_cast<int32_t>(ceil_div(N, kind == fp8bq::kT128W ? 512 : 128));
+    d->UN = static_cast<int32_t>(ceil_div(N, kind == fp8bq::kT128W || kind == fp8bq::kT64W ? 512 : 128));
     d->body = fp8bq::kBodyVec;
     u = ceil_div(M, rows) * d->UN;
   } else {
@@ -174,8 +190,8 @@ unsigned grid_for(int64_t units) {
 bool is_flat(const Desc& d) { return d.body == fp8bq::kBodyFlat; }
 
 // LDS reserve of a launch whose tensors all have flat bodies (all_flat) or not.
-unsigned lds_of(int kind, bool all_flat) {
-  return kind == fp8bq::kR128 && all_flat ? kLds4PerCu : lds_for(kind);
+unsigned lds_of(int kind, bool all_flat, int32_t count = 1) {
+  return kind == fp8bq::kR128 && all_flat ? kLds4PerCu : lds_for(kind, count);
 }
 
 bool all_flat(const std::vector<Desc>& ds) {
@@ -573,7 +589,7 @@ void launch_args(const std::vector<Desc>& ds, const std::vector<int64_t>& st, in
     return;
   }
   hipLaunchKernelGGL((fp8bq::quantize_group_args<KIND, CAP>), dim3(grid_for(total)),
-                     dim3(fp8bq::kThreads), lds_of(KIND, all_flat(ds)), s, a, n, bm, bn,
+                     dim3(fp8bq::kThreads), lds_of(KIND, all_flat(ds), n), s, a, n, bm, bn,
                      static_cast<int32_t>(total));
 }
 
@@ -774,7 +790,9 @@ int fp8bq_quantize(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, 
                    float* scale_inv, void* stream) {
   if (bm < 1 || bn < 1) return FP8BQ_ERR_INVALID_ARGUMENT;
   int kind = kind_of(bm, bn);
-  if (kind == fp8bq::kT128 && wide_units(x, M, N, q) >= kWideMinUnits) kind = fp8bq::kT128W;
+  if (kind == fp8bq::kT128 || kind == fp8bq::kT64) {
+    kind = wide_kind(kind, wide_units(x, M, N, q, kind == fp8bq::kT128 ? 128 : 64));
+  }
   Desc d;
   int64_t units = 0;
   int st = make_desc(x, M, N, bm, bn, q, scale_inv, kind, &d, &units);
@@ -799,6 +817,7 @@ int fp8bq_quantize(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, 
   switch (d.body != fp8bq::kBodyVec && d.body != fp8bq::kBodyFlat ? static_cast<int>(fp8bq::kGeneral) : kind) {
     case fp8bq::kT128: launch_one<fp8bq::kT128>(d, bm, bn, units, s); break;
     case fp8bq::kT128W: launch_one<fp8bq::kT128W>(d, bm, bn, units, s); break;
+    case fp8bq::kT64W: launch_one<fp8bq::kT64W>(d, bm, bn, units, s); break;
     case fp8bq::kT64: launch_one<fp8bq::kT64>(d, bm, bn, units, s); break;
     case fp8bq::kR128: launch_one<fp8bq::kR128>(d, bm, bn, units, s); break;
     default: launch_one<fp8bq::kGeneral>(d, bm, bn, units, s); break;
@@ -823,13 +842,14 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
     return FP8BQ_ERR_WORKSPACE;
   }
   int kind = kind_of(bm, bn);
-  if (kind == fp8bq::kT128) {
+  if (kind == fp8bq::kT128 || kind == fp8bq::kT64) {
+    const int64_t rows = kind == fp8bq::kT128 ? 128 : 64;
     int64_t wide = 0;
     for (int32_t i = 0; i < count && wide >= 0; ++i) {
-      const int64_t w = wide_units(list[i].x, list[i].M, list[i].N, list[i].q);
+      const int64_t w = wide_units(list[i].x, list[i].M, list[i].N, list[i].q, rows);
       wide = w < 0 ? -1 : wide + w;
     }
-    if (wide >= kWideMinUnits) kind = fp8bq::kT128W;
+    kind = wide_kind(kind, wide);
   }
   g_descs.clear();
   g_starts.clear();
@@ -924,6 +944,7 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
     switch (kind) {
       case fp8bq::kT128: launch_args_kind<fp8bq::kT128>(g_descs, g_starts, bm, bn, total, s); break;
       case fp8bq::kT128W: launch_args_kind<fp8bq::kT128W>(g_descs, g_starts, bm, bn, total, s); break;
+      case fp8bq::kT64W: launch_args_kind<fp8bq::kT64W>(g_descs, g_starts, bm, bn, total, s); break;
       case fp8bq::kT64: launch_args_kind<fp8bq::kT64>(g_descs, g_starts, bm, bn, total, s); break;
       case fp8bq::kR128: launch_args_kind<fp8bq::kR128>(g_descs, g_starts, bm, bn, total, s); break;
       default: launch_args_kind<fp8bq::kGeneral>(g_descs, g_starts, bm, bn, total, s); break;
@@ -937,6 +958,7 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
       switch (d.body != fp8bq::kBodyVec && d.body != fp8bq::kBodyFlat ? static_cast<int>(fp8bq::kGeneral) : kind) {
         case fp8bq::kT128: launch_one<fp8bq::kT128>(d, bm, bn, units, s); break;
         case fp8bq::kT128W: launch_one<fp8bq::kT128W>(d, bm, bn, units, s); break;
+        case fp8bq::kT64W: launch_one<fp8bq::kT64W>(d, bm, bn, units, s); break;
         case fp8bq::kT64: launch_one<fp8bq::kT64>(d, bm, bn, units, s); break;
         case fp8bq::kR128: launch_one<fp8bq::kR128>(d, bm, bn, units, s); break;
         default: launch_one<fp8bq::kGeneral>(d, bm, bn, units, s); break;
@@ -947,6 +969,7 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
     switch (kind) {
       case fp8bq::kT128: launch_args_chunks<fp8bq::kT128>(g_descs, g_starts, bm, bn, total, s); break;
       case fp8bq::kT128W: launch_args_chunks<fp8bq::kT128W>(g_descs, g_starts, bm, bn, total, s); break;
+      case fp8bq::kT64W: launch_args_chunks<fp8bq::kT64W>(g_descs, g_starts, bm, bn, total, s); break;
       case fp8bq::kT64: launch_args_chunks<fp8bq::kT64>(g_descs, g_starts, bm, bn, total, s); break;
       case fp8bq::kR128: launch_args_chunks<fp8bq::kR128>(g_descs, g_starts, bm, bn, total, s); break;
       default: launch_args_chunks<fp8bq::kGeneral>(g_descs, g_starts, bm, bn, total, s); break;
@@ -962,12 +985,13 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
     const size_t used = descs_bytes(count) + sizeof(int64_t) * (static_cast<size_t>(n) + 1);
     hipError_t e = hipMemcpyAsync(ws, g_stage.data(), used, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_failed(e);
-    const unsigned lds = lds_of(kind, all_flat(g_descs));
+    const unsigned lds = lds_of(kind, all_flat(g_descs), n);
     const Desc* d_descs = reinterpret_cast<const Desc*>(ws);
     const int64_t* d_start = reinterpret_cast<const int64_t*>(ws + descs_bytes(count));
     switch (kind) {
       case fp8bq::kT128: launch_group<fp8bq::kT128>(d_descs, d_start, n, bm, bn, total, lds, s); break;
       case fp8bq::kT128W: launch_group<fp8bq::kT128W>(d_descs, d_start, n, bm, bn, total, lds, s); break;
+      case fp8bq::kT64W: launch_group<fp8bq::kT64W>(d_descs, d_start, n, bm, bn, total, lds, s); break;
       case fp8bq::kT64: launch_group<fp8bq::kT64>(d_descs, d_start, n, bm, bn, total, lds, s); break;
       case fp8bq::kR128: launch_group<fp8bq::kR128>(d_descs, d_start, n, bm, bn, total, lds, s); break;
       default: launch_group<fp8bq::kGeneral>(d_descs, d_start, n, bm, bn, total, lds, s); break;

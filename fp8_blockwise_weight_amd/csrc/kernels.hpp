@@ -60,7 +60,7 @@ constexpr float kE4m3Max = 448.0f;
 constexpr float kEps = 1e-10f;
 constexpr int kThreads = 256;
 
-enum Kind : int { kT128 = 0, kT64 = 1, kR128 = 2, kGeneral = 3, kT128W = 4 };
+enum Kind : int { kT128 = 0, kT64 = 1, kR128 = 2, kGeneral = 3, kT128W = 4, kT64W = 5 };
 
 // Pointers into device memory, marked as global so loads and stores are
 // emitted as global_* (not flat_*) instructions.
@@ -374,6 +374,64 @@ __device__ __forceinline__ void vec_unit_wide(const Desc& d, int64_t ur, int64_t
   }
 }
 
+// [64,64] blocks, wide unit (kind kT64W): 64 rows x 512 columns, eight
+// side-by-side tiles per workgroup, the [64,64] counterpart of the unit
+// above.  Lane c holds columns 8c..8c+7 of a 512-column row run (8 lanes per
+// tile: tile c / 8), wave w holds rows w, w+4, ..., w+60, so every wave load
+// reads one contiguous 1 KB run.  16 loads per thread.  A tile's maximum:
+// fold over the thread's loads, max over its 8 lanes, then over the 4 waves
+// through LDS.  151937x4096: 79.0% -> 80.9% at 3 workgroups per CU, 82.4%
+// at 2; the 252-tensor dense set at [64,64]: 79.4% -> 81.0% at 3 per CU
+// (75.8% at 2).
+template <bool CHECK>
+__device__ __forceinline__ void vec_unit_wide64(const Desc& d, int64_t ur, int64_t uc, uint32_t* red) {
+  constexpr int L = 16;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int sub = lane >> 3;
+  const int64_t N = d.N;
+  const int64_t row0 = ur * 64;
+  const int64_t col = uc * 512 + lane * 8;
+  int rows_valid = 64;
+  if (CHECK) {
+    const int64_t left = d.M - row0;
+    rows_valid = left < 64 ? (int)left : 64;
+  }
+  const size_t base = (size_t)(row0 + wave) * (size_t)N + (size_t)col;
+  const FP8BQ_GLOBAL u32x4* xp = (const FP8BQ_GLOBAL u32x4*)(d.x + base);
+  const size_t pitch16 = (size_t)N * 4 / 8;
+  u32x4 v[L];
+#pragma unroll
+  for (int k = 0; k < L; ++k) {
+    if (!CHECK || 4 * k + wave < rows_valid) {
+      v[k] = __builtin_nontemporal_load(&xp[k * pitch16]);
+    } else {
+      v[k] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < L; ++k) m = pk_max_u16(m, fold_abs(v[k]));
+  m = max8(halves_max(m));
+  if ((lane & 7) == 0) red[wave * 8 + sub] = m;
+  __syncthreads();
+  const uint32_t tm = max(max(red[sub], red[8 + sub]), max(red[16 + sub], red[24 + sub]));
+  float s, r;
+  tile_scale(tm, s, r);
+  FP8BQ_GLOBAL u32x2* qp = (FP8BQ_GLOBAL u32x2*)(d.q + base);
+  const size_t qpitch8 = (size_t)N * 4 / 8;
+#pragma unroll
+  for (int k = 0; k < L; ++k) {
+    if (!CHECK || 4 * k + wave < rows_valid) {
+      __builtin_nontemporal_store(quant8(v[k], r), &qp[k * qpitch8]);
+    }
+  }
+  if (wave == 0 && (lane & 7) == 0) {
+    ((FP8BQ_GLOBAL float*)d.s)[(size_t)ur * d.TN + (size_t)uc * 8 + sub] = s;
+  }
+}
+
 // A whole tile of at most kRegTile elements held in registers: rows x cols
 // with cols % 8 == 0, x 16-byte and q 8-byte aligned, N % 8 == 0.  Vector v
 // of the tile is row v / (cols/8), 8-column group v % (cols/8); thread t
@@ -582,6 +640,13 @@ __device__ __forceinline__ void run_unit(const Desc& d, int32_t bm, int32_t bn, 
     }
   } else if (d.body != kBodyVec) {
     general_tile<false>(d, bm, bn, ur, uc, red);
+  } else if constexpr (KIND == kT64W) {
+    // Whole 512-column units only (as for kT128W): the rows alone are tested.
+    if ((int64_t)(ur + 1) * 64 <= d.M) {
+      vec_unit_wide64<false>(d, ur, uc, red);
+    } else {
+      vec_unit_wide64<true>(d, ur, uc, red);
+    }
   } else if constexpr (KIND == kT128W) {
     // The host picks this kind only for tensors whose width is a whole number
     // of 512-column units, so only the last unit row can be ragged.  Testing
@@ -641,7 +706,7 @@ __device__ __forceinline__ void for_each_unit(int64_t total, F&& f) {
 template <int KIND>
 __global__ __launch_bounds__(kThreads) void quantize_one(Desc d, int32_t bm, int32_t bn,
                                                          int64_t total) {
-  __shared__ uint32_t red[16];
+  __shared__ uint32_t red[32];
   for_each_unit(total, [&](int64_t u) {
     run_unit<KIND>(d, bm, bn, u, red);
   });
@@ -678,7 +743,7 @@ __global__ __launch_bounds__(kThreads) void quantize_group(const Desc* __restric
                                                            const int64_t* __restrict__ start,
                                                            int32_t count, int32_t bm, int32_t bn,
                                                            int64_t total) {
-  __shared__ uint32_t red[16];
+  __shared__ uint32_t red[32];
   for_each_unit(total, [&](int64_t u) {
     const int lo = find_tensor(start, count, u);
     const Desc d = descs[lo];
@@ -1384,7 +1449,7 @@ __global__ __launch_bounds__(kThreads) void shard_rows(Big b, const float* amax,
 template <int PASS>
 __global__ __launch_bounds__(kThreads) void shard_small(Big b, const float* amax, float* out,
                                                         int64_t tiles) {
-  __shared__ uint32_t red[16];
+  __shared__ uint32_t red[32];
   for_each_unit(tiles, [&](int64_t tile) { shard_small_tile<PASS>(b, tile, amax, out, red); });
 }
 
@@ -1581,7 +1646,7 @@ template <int KIND, int CAP>
 __global__ __launch_bounds__(kThreads) void quantize_group_args(const GroupArgs<CAP> a,
                                                                 int32_t count, int32_t bm,
                                                                 int32_t bn, int32_t total) {
-  __shared__ uint32_t red[16];
+  __shared__ uint32_t red[32];
   for_each_unit(total, [&](int64_t u) {
     const int lo = find_tensor(a.start, count, u);
     const ArgTensor& at = a.t[lo];
@@ -1593,7 +1658,7 @@ __global__ __launch_bounds__(kThreads) void quantize_group_args(const GroupArgs<
     d.N = at.N;
     d.TN = (int32_t)(((int64_t)at.N + bn - 1) / bn);
     d.body = at.body;
-    constexpr int64_t kUnitCols = KIND == kT128W ? 512 : 128;
+    constexpr int64_t kUnitCols = KIND == kT128W || KIND == kT64W ? 512 : 128;
     d.UN = at.body != kBodyVec ? d.TN : (int32_t)(((int64_t)at.N + kUnitCols - 1) / kUnitCols);
     d.pad = 0;
     d.reserved = 0;
@@ -1630,7 +1695,7 @@ struct ShardGroupArgs {
 template <int PASS, bool ROWS, int CAP>
 __global__ __launch_bounds__(kThreads) void shard_group(const ShardGroupArgs<CAP> a, int32_t count,
                                                         int32_t bm, int32_t bn, int32_t total) {
-  __shared__ uint32_t red[16];
+  __shared__ uint32_t red[32];
   for_each_unit(total, [&](int64_t u) {
     const int i = find_tensor(a.start, count, u);
     const ShardEntry& en = a.e[i];

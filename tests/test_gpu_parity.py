@@ -481,14 +481,16 @@ def test_c3_dense_stack_one_grouped_launch(gpu_lib):
     say("C3 checked")
 
 
-def test_wide_unit_launch(gpu_lib):
-    """A [128,128] launch that takes the four-tile (128x512) unit: widths that
-    are multiples of 512 and at least 8192 such units in all (a 1 GB matrix
-    whose last unit row holds 72 rows), grouped with a misaligned tensor (a
-    general body in the same launch), a ragged-height tensor and an empty
-    one.  Every scale is checked against the oracle's scale of the exact
-    tile maxima, sampled tiles byte for byte; the small tensors equal their
-    single calls (one-tile units)."""
+@pytest.mark.parametrize("block", [(128, 128), (64, 64)])
+def test_wide_unit_launch(gpu_lib, block):
+    """A [128,128] or [64,64] launch that takes the wide unit (128x512: four
+    tiles; 64x512: eight): widths that are multiples of 512 and at least 8192
+    such units in all (a 1 GB matrix whose last unit row is partial), grouped
+    with a misaligned tensor (a general body in the same launch), a
+    ragged-height tensor and an empty one.  Every scale is checked against
+    the oracle's scale of the exact tile maxima, sampled tiles byte for byte;
+    the small tensors equal their single calls (narrow units)."""
+    bm, bn = block
     g = torch.Generator(device=DEV).manual_seed(61)
     big = (torch.randn((32768 - 56, 16384), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
     flat = (torch.randn(1000 * 4096 + 1, generator=g, device=DEV) * 0.02).to(torch.bfloat16)
@@ -496,18 +498,19 @@ def test_wide_unit_launch(gpu_lib):
     ragged = (torch.randn((777, 1024), generator=g, device=DEV) * 0.05).to(torch.bfloat16)
     empty = torch.empty((0, 512), dtype=torch.bfloat16, device=DEV)
     xs = [ragged, big, mis, empty]
-    say("wide-unit launch")
-    outs = fq.quantize_many(xs, (128, 128))
+    say("wide-unit launch", block)
+    outs = fq.quantize_many(xs, block)
     torch.cuda.synchronize()
-    assert_scales_match_oracle(big, outs[1][1], 128, 128, "wide big")
-    assert_properties_gpu(big, outs[1][0], outs[1][1], 128, 128, "wide big")
-    tiles = sample_tiles(*big.shape, 128, 128, 6, seed=61) + [(255, 127), (255, 0), (0, 127)]
-    assert_tiles_match_oracle(big, outs[1][0], outs[1][1], 128, 128, tiles, "wide big")
+    assert_scales_match_oracle(big, outs[1][1], bm, bn, "wide big")
+    assert_properties_gpu(big, outs[1][0], outs[1][1], bm, bn, "wide big")
+    TM, TN = fq.scale_shape(*big.shape, bm, bn)
+    tiles = sample_tiles(*big.shape, bm, bn, 6, seed=61) + [(TM - 1, TN - 1), (TM - 1, 0), (0, TN - 1)]
+    assert_tiles_match_oracle(big, outs[1][0], outs[1][1], bm, bn, tiles, "wide big")
     for x, (q, s), name in ((ragged, outs[0], "ragged"), (mis, outs[2], "misaligned")):
-        q1, s1 = fq.quantize(x, (128, 128))
+        q1, s1 = fq.quantize(x, block)
         assert torch.equal(q.view(torch.uint8), q1.view(torch.uint8)), name
         assert torch.equal(s.view(torch.int32), s1.view(torch.int32)), name
-    assert_matches_oracle(ragged, outs[0][0], outs[0][1], 128, 128, "ragged in wide launch")
+    assert_matches_oracle(ragged, outs[0][0], outs[0][1], bm, bn, "ragged in wide launch")
     del big, outs
 
 
