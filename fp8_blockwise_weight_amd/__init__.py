@@ -37,6 +37,7 @@ EXPORTS = (
     "fp8bq_quantize_many",
     "fp8bq_encode_e4m3",
     "fp8bq_dequantize",
+    "fp8bq_dequantize_many",
     "fp8bq_tile_amax",
     "fp8bq_quantize_amax",
     "fp8bq_tile_amax_many",
@@ -45,6 +46,12 @@ EXPORTS = (
     "fp8bq_status_string",
     "fp8bq_last_hip_error",
 )
+
+
+class DqEntry(ctypes.Structure):
+    """``fp8bq_dq_tensor`` of include/fp8bq.h (40 bytes, no padding)."""
+    _fields_ = [("q", ctypes.c_void_p), ("scale_inv", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64)]
 
 
 class TensorEntry(ctypes.Structure):
@@ -105,6 +112,8 @@ def load_library() -> ctypes.CDLL:
     lib.fp8bq_quantize_many.restype = ctypes.c_int
     lib.fp8bq_dequantize.argtypes = [c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_vp, c_i32, c_vp]
     lib.fp8bq_dequantize.restype = ctypes.c_int
+    lib.fp8bq_dequantize_many.argtypes = [ctypes.POINTER(DqEntry), c_i32, c_i32, c_i32, c_i32, c_vp]
+    lib.fp8bq_dequantize_many.restype = ctypes.c_int
     lib.fp8bq_tile_amax.argtypes = [c_vp, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]
     lib.fp8bq_tile_amax.restype = ctypes.c_int
     lib.fp8bq_quantize_amax.argtypes = [c_vp, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_vp,
@@ -364,6 +373,49 @@ def dequantize(q, scale_inv, block_size=(128, 128), out_dtype=None, out=None):
     return out
 
 
+def dequantize_many(qs: Sequence, scales: Sequence, block_size=(128, 128), out_dtype=None,
+                    outs: Optional[Sequence] = None) -> List:
+    """``dequantize`` over a list of (q, scale_inv) pairs with one block size
+    and one output type, in grouped launches (``fp8bq_dequantize_many``)."""
+    import torch
+
+    bm, bn = block_shape(block_size)
+    out_dtype = out_dtype or torch.float32
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    if len(qs) != len(scales) or (outs is not None and len(outs) != len(qs)):
+        raise ValueError("qs, scales (and outs) must have the same length")
+    if not qs:
+        return []
+    device = qs[0].device
+    esize = 4 if out_dtype == torch.float32 else 2
+    table = (DqEntry * len(qs))()
+    result = []
+    for i, (q, s) in enumerate(zip(qs, scales)):
+        if q.dim() != 2 or q.element_size() != 1 or not q.is_cuda or not q.is_contiguous():
+            raise TypeError(f"qs[{i}] must be a contiguous 2-D one-byte GPU tensor")
+        if q.device != device:
+            raise ValueError("every tensor must be on one device")
+        M, N = q.shape
+        if tuple(s.shape) != scale_shape(M, N, bm, bn) or s.dtype != torch.float32 \
+                or not s.is_contiguous() or s.device != device:
+            raise TypeError(f"scales[{i}] must be contiguous float32 [ceil(M/bm), ceil(N/bn)] on q's device")
+        if outs is None:
+            o = torch.empty((M, N), dtype=out_dtype, device=device)
+        else:
+            o = outs[i]
+            _check_buffer(o, (M, N), esize, device, f"outs[{i}]")
+            if o.dtype != out_dtype:
+                raise TypeError(f"outs[{i}] must be {out_dtype}")
+        table[i] = DqEntry(q.data_ptr(), s.data_ptr(), o.data_ptr(), M, N)
+        result.append(o)
+    code = 0 if out_dtype == torch.float32 else 1
+    with torch.cuda.device(device):
+        _check("fp8bq_dequantize_many",
+               load_library().fp8bq_dequantize_many(table, len(qs), bm, bn, code, _stream(device)))
+    return result
+
+
 def local_grid(M: int, N: int, bm: int, bn: int, phase=(0, 0)) -> Tuple[int, int]:
     """Tile grid of a shard whose element (0,0) sits at ``phase`` inside a tile."""
     rp, cp = phase
@@ -515,7 +567,8 @@ def encode_e4m3(y):
 
 
 __all__ = [
-    "EXPORTS", "Fp8bqError", "TensorEntry", "block_shape", "dequantize", "encode_e4m3",
+    "DqEntry", "EXPORTS", "Fp8bqError", "TensorEntry", "block_shape", "dequantize",
+    "dequantize_many", "encode_e4m3",
     "load_library", "local_grid", "quantize_with_amax", "quantize_with_amax_many", "tile_amax",
     "tile_amax_many", "ShardEntry",
     "make_entries", "quantize", "quantize_many", "scale_shape", "set_resident_wait_us",

@@ -782,6 +782,75 @@ int shard_many(const fp8bq_shard* list, int32_t count, int32_t bm, int32_t bn, v
   return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
 }
 
+// Checks a dequantization call; *vec says whether it takes the vector body.
+int check_dequant(const void* q, const float* scale_inv, int64_t M, int64_t N, int32_t bm,
+                  int32_t bn, void* out, int32_t out_dtype, bool* vec) {
+  *vec = false;
+  if (M < 0 || N < 0 || M > INT32_MAX || N > INT32_MAX || bm < 1 || bn < 1) {
+    return FP8BQ_ERR_INVALID_ARGUMENT;
+  }
+  if (out_dtype != FP8BQ_OUT_F32 && out_dtype != FP8BQ_OUT_BF16) return FP8BQ_ERR_INVALID_ARGUMENT;
+  if (M == 0 || N == 0) return FP8BQ_OK;
+  if (q == nullptr || scale_inv == nullptr || out == nullptr) return FP8BQ_ERR_INVALID_ARGUMENT;
+  const uintptr_t qa = reinterpret_cast<uintptr_t>(q);
+  const uintptr_t sa = reinterpret_cast<uintptr_t>(scale_inv);
+  const uintptr_t oa = reinterpret_cast<uintptr_t>(out);
+  const uint64_t esize = out_dtype == FP8BQ_OUT_F32 ? 4 : 2;
+  if ((sa & 3) != 0 || (oa & (esize - 1)) != 0) return FP8BQ_ERR_INVALID_ARGUMENT;
+  const int64_t TM = ceil_div(M, bm);
+  const int64_t TN = ceil_div(N, bn);
+  const uint64_t n = static_cast<uint64_t>(M) * static_cast<uint64_t>(N);
+  const uint64_t ns = static_cast<uint64_t>(TM) * static_cast<uint64_t>(TN);
+  if (overlap(out, esize * n, q, n) || overlap(out, esize * n, scale_inv, 4 * ns)) {
+    return FP8BQ_ERR_INVALID_ARGUMENT;
+  }
+  const int64_t G = out_dtype == FP8BQ_OUT_F32 ? 4 : 8;
+  *vec = (N % G) == 0 && (bn % G) == 0 && (qa % G) == 0 && (oa & 15) == 0;
+  return FP8BQ_OK;
+}
+
+void launch_dequant_vec(const void* q, const float* scale_inv, int64_t M, int64_t N, int32_t bm,
+                        int32_t bn, void* out, int32_t out_dtype, hipStream_t s) {
+  const uint8_t* qb = static_cast<const uint8_t*>(q);
+  const int32_t tn = static_cast<int32_t>(ceil_div(N, bn));
+  const int64_t G = out_dtype == FP8BQ_OUT_F32 ? 4 : 8;
+  const int64_t groups = M * N / G;
+  const int64_t per_block = static_cast<int64_t>(fp8bq::kThreads) * fp8bq::kDqUnroll;
+  const unsigned grid = grid_for((groups + per_block - 1) / per_block);
+  const int64_t gpr = N / G;  // groups per row, < 2^29
+  const int64_t stride = static_cast<int64_t>(grid) * per_block;
+  const fp8bq::Div31 by_gpr = fp8bq::make_div31(static_cast<uint32_t>(gpr));
+  const fp8bq::Div31 by_bm = fp8bq::make_div31(static_cast<uint32_t>(bm));
+  const fp8bq::Div31 by_bn = fp8bq::make_div31(static_cast<uint32_t>(bn));
+  const int64_t step_rows = stride / gpr;
+  const int32_t step_cols = static_cast<int32_t>(stride % gpr);
+  if (out_dtype == FP8BQ_OUT_F32) {
+    hipLaunchKernelGGL(fp8bq::dequant_vec<fp8bq::kOutF32>, dim3(grid), dim3(fp8bq::kThreads), 0, s,
+                       qb, scale_inv, static_cast<int32_t>(gpr), tn, by_gpr, by_bm, by_bn, out,
+                       groups, static_cast<int32_t>(M - 1), step_rows, step_cols);
+  } else {
+    hipLaunchKernelGGL(fp8bq::dequant_vec<fp8bq::kOutBF16>, dim3(grid), dim3(fp8bq::kThreads), 0, s,
+                       qb, scale_inv, static_cast<int32_t>(gpr), tn, by_gpr, by_bm, by_bn, out,
+                       groups, static_cast<int32_t>(M - 1), step_rows, step_cols);
+  }
+}
+
+void launch_dequant_elem(const void* q, const float* scale_inv, int64_t M, int64_t N, int32_t bm,
+                         int32_t bn, void* out, int32_t out_dtype, hipStream_t s) {
+  const uint8_t* qb = static_cast<const uint8_t*>(q);
+  const int32_t tn = static_cast<int32_t>(ceil_div(N, bn));
+  const int64_t n = M * N;
+  const int64_t blocks = (n + fp8bq::kThreads - 1) / fp8bq::kThreads;
+  const dim3 grid(static_cast<unsigned>(blocks < 65536 * 16 ? blocks : 65536 * 16));
+  if (out_dtype == FP8BQ_OUT_F32) {
+    hipLaunchKernelGGL(fp8bq::dequant_elem<fp8bq::kOutF32>, grid, dim3(fp8bq::kThreads), 0, s, qb,
+                       scale_inv, N, bm, bn, tn, out, n);
+  } else {
+    hipLaunchKernelGGL(fp8bq::dequant_elem<fp8bq::kOutBF16>, grid, dim3(fp8bq::kThreads), 0, s, qb,
+                       scale_inv, N, bm, bn, tn, out, n);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -1074,63 +1143,103 @@ int fp8bq_encode_e4m3(const float* y, void* q, int64_t n, void* stream) {
 
 int fp8bq_dequantize(const void* q, const float* scale_inv, int64_t M, int64_t N, int32_t bm,
                      int32_t bn, void* out, int32_t out_dtype, void* stream) {
-  if (M < 0 || N < 0 || M > INT32_MAX || N > INT32_MAX || bm < 1 || bn < 1) {
-    return FP8BQ_ERR_INVALID_ARGUMENT;
-  }
-  if (out_dtype != FP8BQ_OUT_F32 && out_dtype != FP8BQ_OUT_BF16) return FP8BQ_ERR_INVALID_ARGUMENT;
-  if (M == 0 || N == 0) return FP8BQ_OK;
-  if (q == nullptr || scale_inv == nullptr || out == nullptr) return FP8BQ_ERR_INVALID_ARGUMENT;
-  const uintptr_t qa = reinterpret_cast<uintptr_t>(q);
-  const uintptr_t sa = reinterpret_cast<uintptr_t>(scale_inv);
-  const uintptr_t oa = reinterpret_cast<uintptr_t>(out);
-  const uint64_t esize = out_dtype == FP8BQ_OUT_F32 ? 4 : 2;
-  if ((sa & 3) != 0 || (oa & (esize - 1)) != 0) return FP8BQ_ERR_INVALID_ARGUMENT;
-  const int64_t TM = ceil_div(M, bm);
-  const int64_t TN = ceil_div(N, bn);
-  const uint64_t n = static_cast<uint64_t>(M) * static_cast<uint64_t>(N);
-  const uint64_t ns = static_cast<uint64_t>(TM) * static_cast<uint64_t>(TN);
-  if (overlap(out, esize * n, q, n) || overlap(out, esize * n, scale_inv, 4 * ns)) {
-    return FP8BQ_ERR_INVALID_ARGUMENT;
-  }
+  bool vec = false;
+  const int st0 = check_dequant(q, scale_inv, M, N, bm, bn, out, out_dtype, &vec);
+  if (st0 != FP8BQ_OK || M == 0 || N == 0) return st0;
   const int st = device_check();
   if (st != FP8BQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  const uint8_t* qb = static_cast<const uint8_t*>(q);
-  const int32_t tn = static_cast<int32_t>(TN);
-  const int64_t G = out_dtype == FP8BQ_OUT_F32 ? 4 : 8;
-  const bool vec = (N % G) == 0 && (bn % G) == 0 && (qa % G) == 0 && (oa & 15) == 0;
   if (vec) {
-    const int64_t groups = static_cast<int64_t>(n) / G;
-    const int64_t per_block = static_cast<int64_t>(fp8bq::kThreads) * fp8bq::kDqUnroll;
-    const unsigned grid = grid_for((groups + per_block - 1) / per_block);
-    const int64_t gpr = N / G;  // groups per row, < 2^29
-    const int64_t stride = static_cast<int64_t>(grid) * per_block;
-    const fp8bq::Div31 by_gpr = fp8bq::make_div31(static_cast<uint32_t>(gpr));
-    const fp8bq::Div31 by_bm = fp8bq::make_div31(static_cast<uint32_t>(bm));
-    const fp8bq::Div31 by_bn = fp8bq::make_div31(static_cast<uint32_t>(bn));
-    const int64_t step_rows = stride / gpr;
-    const int32_t step_cols = static_cast<int32_t>(stride % gpr);
-    if (out_dtype == FP8BQ_OUT_F32) {
-      hipLaunchKernelGGL(fp8bq::dequant_vec<fp8bq::kOutF32>, dim3(grid), dim3(fp8bq::kThreads), 0,
-                         s, qb, scale_inv, static_cast<int32_t>(gpr), tn, by_gpr, by_bm, by_bn, out,
-                         groups, static_cast<int32_t>(M - 1), step_rows, step_cols);
-    } else {
-      hipLaunchKernelGGL(fp8bq::dequant_vec<fp8bq::kOutBF16>, dim3(grid), dim3(fp8bq::kThreads), 0,
-                         s, qb, scale_inv, static_cast<int32_t>(gpr), tn, by_gpr, by_bm, by_bn, out,
-                         groups, static_cast<int32_t>(M - 1), step_rows, step_cols);
-    }
+    launch_dequant_vec(q, scale_inv, M, N, bm, bn, out, out_dtype, s);
   } else {
-    const int64_t blocks = (static_cast<int64_t>(n) + fp8bq::kThreads - 1) / fp8bq::kThreads;
-    const dim3 grid(static_cast<unsigned>(blocks < 65536 * 16 ? blocks : 65536 * 16));
-    if (out_dtype == FP8BQ_OUT_F32) {
-      hipLaunchKernelGGL(fp8bq::dequant_elem<fp8bq::kOutF32>, grid, dim3(fp8bq::kThreads), 0, s, qb,
-                         scale_inv, N, bm, bn, tn, out, static_cast<int64_t>(n));
-    } else {
-      hipLaunchKernelGGL(fp8bq::dequant_elem<fp8bq::kOutBF16>, grid, dim3(fp8bq::kThreads), 0, s, qb,
-                         scale_inv, N, bm, bn, tn, out, static_cast<int64_t>(n));
-    }
+    launch_dequant_elem(q, scale_inv, M, N, bm, bn, out, out_dtype, s);
   }
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
+}
+
+int fp8bq_dequantize_many(const fp8bq_dq_tensor* list, int32_t count, int32_t bm, int32_t bn,
+                          int32_t out_dtype, void* stream) {
+  if (count < 0 || bm < 1 || bn < 1) return FP8BQ_ERR_INVALID_ARGUMENT;
+  if (out_dtype != FP8BQ_OUT_F32 && out_dtype != FP8BQ_OUT_BF16) return FP8BQ_ERR_INVALID_ARGUMENT;
+  if (count == 0) return FP8BQ_OK;
+  if (list == nullptr) return FP8BQ_ERR_INVALID_ARGUMENT;
+  std::vector<char> vec(static_cast<size_t>(count), 0);
+  bool any = false;
+  for (int32_t i = 0; i < count; ++i) {
+    const fp8bq_dq_tensor& t = list[i];
+    bool v = false;
+    const int st = check_dequant(t.q, t.scale_inv, t.M, t.N, bm, bn, t.out, out_dtype, &v);
+    if (st != FP8BQ_OK) return st;
+    vec[static_cast<size_t>(i)] = v ? 1 : 0;
+    any = any || (t.M > 0 && t.N > 0);
+  }
+  if (!any) return FP8BQ_OK;
+  const int st = device_check();
+  if (st != FP8BQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const int64_t G = out_dtype == FP8BQ_OUT_F32 ? 4 : 8;
+  const int64_t per_block = static_cast<int64_t>(fp8bq::kThreads) * fp8bq::kDqUnroll;
+  // fp32 output over more than 8 entries: runs of 2 blocks and the counting
+  // table search; otherwise one block per unit and the binary search.
+  const bool f32 = out_dtype == FP8BQ_OUT_F32;
+  int32_t vec_count = 0;
+  for (int32_t i = 0; i < count; ++i) vec_count += vec[static_cast<size_t>(i)] && list[i].M > 0 && list[i].N > 0;
+  const int64_t run = f32 && vec_count > 8 ? 2 : 1;
+  fp8bq::DqGroupArgs<fp8bq::kDqArgsMax> a;
+  int32_t n = 0;
+  int64_t total = 0;
+  auto flush = [&]() {
+    if (n == 0) return;
+    a.start[n] = static_cast<int32_t>(total);
+    const dim3 grid(grid_for(total)), blk(fp8bq::kThreads);
+    const int32_t tot = static_cast<int32_t>(total);
+    constexpr int C = fp8bq::kDqArgsMax;
+    if (f32 && run == 2) {
+      hipLaunchKernelGGL((fp8bq::dequant_group<fp8bq::kOutF32, C, 2, true>), grid, blk, 0, s, a, n, tot);
+    } else if (f32) {
+      hipLaunchKernelGGL((fp8bq::dequant_group<fp8bq::kOutF32, C, 1, false>), grid, blk, 0, s, a, n, tot);
+    } else {
+      hipLaunchKernelGGL((fp8bq::dequant_group<fp8bq::kOutBF16, C, 1, false>), grid, blk, 0, s, a, n, tot);
+    }
+    n = 0;
+    total = 0;
+  };
+  for (int32_t i = 0; i < count; ++i) {
+    const fp8bq_dq_tensor& t = list[i];
+    if (t.M == 0 || t.N == 0) continue;
+    if (!vec[static_cast<size_t>(i)]) {
+      launch_dequant_elem(t.q, t.scale_inv, t.M, t.N, bm, bn, t.out, out_dtype, s);
+      continue;
+    }
+    const int64_t groups = t.M * t.N / G;
+    const int64_t runs = ceil_div(groups, per_block * run);
+    if (groups >= (int64_t{1} << 31) - per_block * run) {  // beyond 32-bit group numbers: its own launch
+      launch_dequant_vec(t.q, t.scale_inv, t.M, t.N, bm, bn, t.out, out_dtype, s);
+      continue;
+    }
+    if (n == fp8bq::kDqArgsMax || total + runs > INT32_MAX) flush();
+    if (n == 0) std::memset(&a, 0, sizeof(a));
+    fp8bq::DqEntry& e = a.e[n];
+    e.q = static_cast<const uint8_t*>(t.q);
+    e.s = t.scale_inv;
+    e.out = t.out;
+    e.groups = groups;
+    e.gpr = static_cast<int32_t>(t.N / G);
+    e.TN = static_cast<int32_t>(ceil_div(t.N, bn));
+    e.last_row = static_cast<int32_t>(t.M - 1);
+    e.step_rows = static_cast<int32_t>(per_block / (t.N / G));
+    e.step_cols = static_cast<int32_t>(per_block % (t.N / G));
+    e.by_gpr = fp8bq::make_div31(static_cast<uint32_t>(t.N / G));
+    e.by_bm = fp8bq::make_div31(static_cast<uint32_t>(bm));
+    e.by_bn = fp8bq::make_div31(static_cast<uint32_t>(bn));
+    a.start[n] = static_cast<int32_t>(total);
+    total += runs;
+    ++n;
+  }
+  flush();
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
 }

@@ -1595,6 +1595,79 @@ __global__ __launch_bounds__(kThreads) void dequant_vec(const uint8_t* __restric
   }
 }
 
+// A list of tensors that take the vector body, in one launch: the table
+// rides in the kernel arguments.  A unit is a run of RUN consecutive blocks
+// of one tensor; unit u belongs to the entry whose first unit start[e] is
+// the largest <= u, found by a binary search over the table (eight
+// dependent scalar loads for 256 entries) or, with COUNT, by counting the
+// entries that start at or before u, one per thread, in one barrier.  The
+// run's first group is divided into (row, column) once (32-bit: the host
+// keeps every entry below 2^31 groups), then the position steps by whole
+// blocks.  Measured on MI355X (dense 36-layer set / 8 MoE layers / the
+// 151937x4096 matrix alone): fp32 output with RUN 1 and the search 70.4 /
+// 68.8 / 80.8% of peak, with RUN 2 and COUNT 73.8 / 75.4 / 72.0%; BF16 with
+// RUN 1 and the search 79.7 / 76.0 / 78.4%, with RUN 2 and COUNT 72.0 /
+// 75.3 / 74.8%; RUN 8 67 / 68 / 69%.
+struct DqEntry {
+  const uint8_t* q;
+  const float* s;
+  void* out;
+  int64_t groups;     // M * N / G, < 2^31
+  int32_t gpr;        // groups per row, N / G
+  int32_t TN;
+  int32_t last_row;   // M - 1
+  int32_t step_rows;  // one block of groups = step_rows rows + step_cols groups
+  int32_t step_cols;
+  Div31 by_gpr;
+  Div31 by_bm;
+  Div31 by_bn;
+};
+
+constexpr int kDqArgsMax = 256;
+
+template <int CAP>
+struct DqGroupArgs {
+  int32_t start[CAP + 1];
+  DqEntry e[CAP];
+};
+
+template <int OUT, int CAP, int RUN, bool COUNT>
+__global__ __launch_bounds__(kThreads) void dequant_group(const DqGroupArgs<CAP> a, int32_t count,
+                                                          int32_t total) {
+  static_assert(!COUNT || CAP <= kThreads, "one table entry per thread");
+  const int64_t per_block = (int64_t)kThreads * kDqUnroll;
+  for (int64_t u = blockIdx.x; u < total; u += gridDim.x) {
+    int i;
+    if constexpr (COUNT) {
+      i = __syncthreads_count((int)threadIdx.x < count && a.start[threadIdx.x] <= u) - 1;
+    } else {
+      i = find_tensor(a.start, count, u);
+    }
+    const DqEntry& e = a.e[i];
+    int64_t b0 = (u - a.start[i]) * (per_block * RUN);
+    int64_t row0 = div31((uint32_t)b0, e.by_gpr);
+    int32_t col0 = (int32_t)(b0 - row0 * e.gpr);
+#pragma unroll
+    for (int r = 0; r < RUN; ++r) {
+      if (b0 >= e.groups) break;
+      if (b0 + per_block <= e.groups) {
+        dequant_block<OUT, false>(e.q, e.s, e.gpr, e.TN, e.by_gpr, e.by_bm, e.by_bn, e.out,
+                                  e.groups, e.last_row, b0, row0, col0);
+      } else {
+        dequant_block<OUT, true>(e.q, e.s, e.gpr, e.TN, e.by_gpr, e.by_bm, e.by_bn, e.out,
+                                 e.groups, e.last_row, b0, row0, col0);
+      }
+      b0 += per_block;
+      row0 += e.step_rows;
+      col0 += e.step_cols;
+      if (col0 >= e.gpr) {
+        col0 -= e.gpr;
+        ++row0;
+      }
+    }
+  }
+}
+
 // One thread per element: any shape, block size and alignment.
 template <int OUT>
 __global__ __launch_bounds__(kThreads) void dequant_elem(const uint8_t* __restrict__ q,

@@ -236,6 +236,34 @@ enum fp8bq_out_dtype {
 int fp8bq_dequantize(const void* q, const float* scale_inv, int64_t M, int64_t N, int32_t bm,
                      int32_t bn, void* out, int32_t out_dtype, void* stream);
 
+/* One tensor of a grouped dequantization (40 bytes, no padding). */
+typedef struct {
+  const void* q;          /* device, e4m3fn bytes [M, N] row-major */
+  const float* scale_inv; /* device, fp32 [ceil(M/bm), ceil(N/bn)] row-major */
+  void* out;              /* device, [M, N] row-major of the call's out_dtype */
+  int64_t M;
+  int64_t N;
+} fp8bq_dq_tensor;
+
+/*
+ * fp8bq_dequantize over a list of tensors that share one block size and one
+ * output type: the same results as one call per entry, in fewer launches
+ * (the consumer side of a grouped fp8bq_quantize_many, e.g. the round trip
+ * of a whole layer list).
+ *   list       HOST array of `count` entries, read before the call returns
+ *   count      number of entries (>= 0); entries with M == 0 or N == 0 are skipped
+ *   bm, bn     block size shared by every entry
+ *   out_dtype  FP8BQ_OUT_F32 or FP8BQ_OUT_BF16, for every entry
+ * Every entry is checked as the single call checks it before anything is
+ * enqueued.  Entries that take the vector kernel share launches of up to 256
+ * entries with the table in the kernel arguments (no workspace,
+ * graph-capturable); the others take their own element-wise launches.
+ * Outputs of different entries must not overlap each other or any entry's
+ * inputs (not checked across entries).  Returns an fp8bq_status.
+ */
+int fp8bq_dequantize_many(const fp8bq_dq_tensor* list, int32_t count, int32_t bm, int32_t bn,
+                          int32_t out_dtype, void* stream);
+
 /*
  * The final cast alone (clamp to +-448, round to e4m3fn), for checking the
  * hardware convert over every float32 input.

@@ -55,6 +55,13 @@ int main(void) {
     expect(fp8bq_quantize_amax_many(sh, 0, 128, 128, NULL), FP8BQ_OK, "no shards");
   }
   expect(fp8bq_encode_e4m3(NULL, Q, 4, NULL), FP8BQ_ERR_INVALID_ARGUMENT, "null y");
+  {
+    fp8bq_dq_tensor dq[2] = {{Q, S, (void*)(uintptr_t)0x1000000000ull, 128, 128},
+                             {Q, S, (void*)(uintptr_t)0x1000000002ull, 128, 128}};
+    expect(fp8bq_dequantize_many(dq, 2, 128, 128, FP8BQ_OUT_F32, NULL), FP8BQ_ERR_INVALID_ARGUMENT,
+           "grouped dequant, misaligned out");
+    expect(fp8bq_dequantize_many(dq, 0, 128, 128, FP8BQ_OUT_F32, NULL), FP8BQ_OK, "no dequant entries");
+  }
   expect(fp8bq_set_resident_wait_us(-1), FP8BQ_ERR_INVALID_ARGUMENT, "negative wait");
   expect(fp8bq_set_resident_wait_us(2000), FP8BQ_OK, "default wait");
   expect(fp8bq_last_hip_error(), 0, "no HIP call made");

@@ -220,6 +220,36 @@ def test_dequantize_rejects(lib):
     assert f(None, None, 0, 128, 128, 128, None, 0, None) == fq.OK
 
 
+def test_dq_entry_layout_matches_header():
+    # fp8bq_dq_tensor: three pointers, two int64 -> 40 bytes on LP64
+    assert ctypes.sizeof(fq.DqEntry) == 40
+
+
+def test_dequantize_many_rejects(lib):
+    """Grouped dequantization: every entry is checked as the single call
+    checks it, before anything is enqueued (no device is touched here)."""
+    f = lib.fp8bq_dequantize_many
+
+    def table(*entries):
+        arr = (fq.DqEntry * len(entries))()
+        for i, e in enumerate(entries):
+            arr[i] = fq.DqEntry(*e)
+        return arr
+
+    good = (Q, S, X, 128, 128)
+    assert f(table(good), -1, 128, 128, 0, None) == INVALID          # negative count
+    assert f(None, 2, 128, 128, 0, None) == INVALID                  # null list
+    assert f(table(good), 1, 0, 128, 0, None) == INVALID             # bm < 1
+    assert f(table(good), 1, 128, 128, 3, None) == INVALID           # unknown out dtype
+    assert f(table(good, (Q, S, X + 2, 128, 128)), 2, 128, 128, 0, None) == INVALID  # out misaligned
+    assert f(table(good, (Q, S, Q + 64, 128, 128)), 2, 128, 128, 0, None) == INVALID  # out overlaps q
+    assert f(table(good, (None, S, X, 128, 128)), 2, 128, 128, 1, None) == INVALID  # null q
+    assert f(table(good, (Q, S, X, -1, 128)), 2, 128, 128, 0, None) == INVALID  # negative M
+    assert f(None, 0, 128, 128, 0, None) == fq.OK                    # nothing to do
+    assert f(table((None, None, None, 0, 128), (None, None, None, 7, 0)), 2, 128, 128, 1, None) == fq.OK
+    assert lib.fp8bq_last_hip_error() == 0
+
+
 def test_shard_calls_reject(lib):
     ta, qa = lib.fp8bq_tile_amax, lib.fp8bq_quantize_amax
     A = 0x50_0000_0000

@@ -605,6 +605,56 @@ def test_dequant_seeded_fuzz(gpu_lib):
         assert bad[0].size == 0, (i, M, N, bm, bn, out_dtype, bad[0].size)
 
 
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_dequantize_many_matches_single_calls(gpu_lib, out_dtype):
+    """Grouped dequantization of 300 entries (two launches of up to 256),
+    mixing vector-kernel entries with ragged shapes, entries that take the
+    element-wise kernel (N % 8 != 0, an output 4 bytes past a 16-byte
+    boundary) and empty ones: every output equals its single call bit for
+    bit, and seeded entries equal the oracle."""
+    rng = np.random.default_rng(909)
+    bm, bn = 64, 128
+    qs, ss, outs, codes_l, scales_l = [], [], [], [], []
+    esize = 4 if out_dtype == torch.float32 else 2
+    for i in range(300):
+        kind = i % 10
+        M = 0 if kind == 9 else int(rng.integers(1, 300))
+        N = int(rng.integers(1, 300)) if kind == 7 else int(rng.integers(1, 40)) * 8
+        TM, TN = -(-max(M, 1) // bm), -(-N // bn)
+        codes = rng.integers(0, 256, (M, N), dtype=np.int64).astype(np.uint8)
+        codes[(codes & 0x7F) == 0x7F] ^= 0x01
+        scales = np.exp2(rng.uniform(-20, 20, (-(-M // bm), TN))).astype(np.float32)
+        qs.append(torch.from_numpy(codes).to(DEV))
+        ss.append(torch.from_numpy(scales).to(DEV))
+        if kind == 8 and M > 0:                      # output 4 bytes past a 16-byte boundary
+            buf = torch.empty(M * N * esize + 16, dtype=torch.uint8, device=DEV)
+            outs.append(buf[4:4 + M * N * esize].view(out_dtype).view(M, N))
+        else:
+            outs.append(torch.empty((M, N), dtype=out_dtype, device=DEV))
+        codes_l.append(codes)
+        scales_l.append(scales)
+    say("dequantize_many", out_dtype)
+    got = fq.dequantize_many(qs, ss, (bm, bn), out_dtype=out_dtype, outs=outs)
+    torch.cuda.synchronize()
+    for i, (q, s, o) in enumerate(zip(qs, ss, got)):
+        if q.numel() == 0:
+            continue
+        one = fq.dequantize(q, s, (bm, bn), out_dtype=out_dtype)
+        assert torch.equal(o.view(torch.int16 if esize == 2 else torch.int32),
+                           one.view(torch.int16 if esize == 2 else torch.int32)), i
+    # a short list (one block per unit for either output type)
+    few = fq.dequantize_many(qs[:6], ss[:6], (bm, bn), out_dtype=out_dtype)
+    for i, o in enumerate(few):
+        if qs[i].numel():
+            assert torch.equal(o.view(torch.uint8), got[i].contiguous().view(torch.uint8)), i
+    name = "f32" if out_dtype == torch.float32 else "bf16"
+    for i in (0, 7, 8, 123, 299):
+        if codes_l[i].size == 0:
+            continue
+        want = oracle.dequantize(codes_l[i], scales_l[i], bm, bn, name)
+        assert np.array_equal(got[i].float().cpu().numpy().astype(np.float64), want), i
+
+
 def test_dequant_roundtrip_bound_layer(gpu_lib):
     """I4 over a whole Qwen3-8B-shaped layer on the GPU: |x - dequant(q)| is
     within half an e4m3 ulp of the scaled value times s (+ fp32 rounding)."""
