@@ -279,6 +279,41 @@ def test_per_tensor_held_in_registers_beside_other_streams(gpu_lib):
         assert torch.equal(s1.view(torch.int32), s.view(torch.int32)), rep
 
 
+def test_graph_capture_of_grouped_dequantization(gpu_lib):
+    """fp8bq_dequantize_many captured in a HIP graph (table in the kernel
+    arguments): every replay, with the codes changed eagerly in between,
+    equals single eager calls, for both output types."""
+    g = torch.Generator(device=DEV).manual_seed(71)
+    xs = [(torch.randn((int(m), int(n)), generator=g, device=DEV) * 0.05).to(torch.bfloat16)
+          for m, n in ((300, 512), (1024, 1024), (77, 128), (513, 2048))] * 5
+    qs, ss = zip(*fq.quantize_many(xs, (128, 128)))
+    qs = [q.view(torch.uint8) for q in qs]
+    for dt in (torch.float32, torch.bfloat16):
+        outs = [torch.empty(q.shape, dtype=dt, device=DEV) for q in qs]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fq.dequantize_many(qs, ss, (128, 128), out_dtype=dt, outs=outs)   # warm-up
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fq.dequantize_many(qs, ss, (128, 128), out_dtype=dt, outs=outs)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            _say("grouped dequant replay", dt, rep)
+            for q in qs:
+                q.copy_(torch.where(q == 0x7F, q, q ^ 0x80))     # flip signs, keep NaN codes away
+            for o in outs:
+                o.fill_(-7.0)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for i, (q, s, o) in enumerate(zip(qs, ss, outs)):
+                one = fq.dequantize(q, s, (128, 128), out_dtype=dt)
+                assert torch.equal(o.view(torch.int16), one.view(torch.int16)), (dt, rep, i)
+
+
 def test_error_reporting_on_device(gpu_lib):
     """Argument errors raise with the library's status text; nothing is
     launched (outputs keep their fill)."""
