@@ -14,7 +14,9 @@
 //     of wide and many tiles, four side-by-side tiles (128 x 512, 32 loads
 //     per thread) so that every wave load reads one 1 KB row run;
 //   * [64,64] blocks: unit = 64 x 128 = two side-by-side tiles, so the FP8
-//     rows written are still full 128-byte lines;
+//     rows written are still full 128-byte lines, or, for launches of wide
+//     and many tiles, eight side-by-side tiles (64 x 512, 16 loads per
+//     thread, 1 KB row runs per wave load);
 //   * [1,128] blocks: unit = 64 rows x 128 = 64 row-tiles; each tile's
 //     maximum is reduced inside one 16-lane DPP row, with no LDS and no
 //     barrier, and each lane divides for one row-tile only (DPP quad
@@ -25,17 +27,24 @@
 //     8-aligned columns, the whole tile in registers; up to 65536, two
 //     16-byte passes over the tile; N % 8 != 0 or a misaligned pointer,
 //     element by element;
-//   * tiles of more than 65536 elements (e.g. one scale per tensor) and
-//     shards that start inside a tile: two passes over chunks of each tile
-//     (section "large tiles"): per-workgroup maxima in slots of q and a
-//     reduce kernel for whole tensors, atomic maxima for shards;
+//   * one scale per tensor (a single tile of 2^20 or more values that fits
+//     in the registers of the grid the chip holds at once, about 50 M
+//     values): the tensor is read once and held in registers while the
+//     workgroups agree on its maximum through device-scope atomics
+//     (section "one scale per tensor, held in registers"), one launch per
+//     tensor or one persistent launch per list;
+//   * other tiles of more than 65536 elements and shards that start inside
+//     a tile: two passes over chunks of each tile (section "large tiles"):
+//     per-workgroup maxima in slots of q and a reduce kernel for whole
+//     tensors, atomic maxima for shards;
 //   * shards whose tiles hold at most 16384 elements with 8-aligned tile
 //     columns: one workgroup per tile (64-row units for one-row tiles), the
 //     maxima pass and the quantize pass each one launch, singly or grouped
 //     (section "small tiles of shards").
 // Every body computes the same arithmetic, so results never depend on it.
 // The file also holds dequantization (decode(q) * s, section
-// "dequantization") and the final cast on its own.
+// "dequantization", singly or over a list in one launch) and the final cast
+// on its own.
 //
 // The tile maximum is an integer max over (bits & 0x7FFF): for finite BF16
 // values magnitude order equals bit-pattern order, so this is exact.
