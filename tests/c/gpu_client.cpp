@@ -4,8 +4,10 @@
 //   2. captures fp8bq_quantize_many (one entry, other outputs) in a HIP
 //      graph and replays it twice, refilling those outputs with a pattern
 //      before each replay (eagerly, outside the graph);
-//   3. dequantizes the result of step 1 to fp32 with fp8bq_dequantize.
-// It checks that both quantizations agree byte for byte and writes
+//   3. dequantizes the result of step 1 to fp32 with fp8bq_dequantize, and
+//      both results again with one fp8bq_dequantize_many call.
+// It checks that both quantizations, and all three dequantizations, agree
+// byte for byte and writes
 // <prefix>.q (uint8 [M, N]), <prefix>.s (fp32 [TM, TN]) and <prefix>.deq
 // (fp32 [M, N]) for the caller to compare with the CPU oracle.
 //
@@ -74,6 +76,8 @@ int main(int argc, char** argv) {
   HIP_OK(hipMalloc(reinterpret_cast<void**>(&ds), 4 * ns));
   HIP_OK(hipMalloc(reinterpret_cast<void**>(&ds2), 4 * ns));
   HIP_OK(hipMalloc(reinterpret_cast<void**>(&ddeq), 4 * n));
+  float* ddeq2 = nullptr;
+  HIP_OK(hipMalloc(reinterpret_cast<void**>(&ddeq2), 8 * n));
   HIP_OK(hipMemcpy(dx, x.data(), 2 * n, hipMemcpyHostToDevice));
   hipStream_t st;
   HIP_OK(hipStreamCreate(&st));
@@ -95,6 +99,8 @@ int main(int argc, char** argv) {
   }
 
   FP8BQ_OK_(fp8bq_dequantize(dq, ds, M, N, bm, bn, ddeq, FP8BQ_OUT_F32, st));
+  const fp8bq_dq_tensor dql[2] = {{dq, ds, ddeq2, M, N}, {dq2, ds2, ddeq2 + n, M, N}};
+  FP8BQ_OK_(fp8bq_dequantize_many(dql, 2, bm, bn, FP8BQ_OUT_F32, st));
   HIP_OK(hipStreamSynchronize(st));
 
   std::vector<uint8_t> q(n), q2(n);
@@ -104,6 +110,13 @@ int main(int argc, char** argv) {
   HIP_OK(hipMemcpy(s.data(), ds, 4 * ns, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(s2.data(), ds2, 4 * ns, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(deq.data(), ddeq, 4 * n, hipMemcpyDeviceToHost));
+  std::vector<float> deq2(2 * n);
+  HIP_OK(hipMemcpy(deq2.data(), ddeq2, 8 * n, hipMemcpyDeviceToHost));
+  if (std::memcmp(deq.data(), deq2.data(), 4 * n) != 0 ||
+      std::memcmp(deq.data(), deq2.data() + n, 4 * n) != 0) {
+    std::fprintf(stderr, "grouped dequantization differs from the single call\n");
+    return 5;
+  }
   if (std::memcmp(q.data(), q2.data(), n) != 0 || std::memcmp(s.data(), s2.data(), 4 * ns) != 0) {
     std::fprintf(stderr, "graph replay differs from the direct call\n");
     return 4;
@@ -125,6 +138,7 @@ int main(int argc, char** argv) {
   HIP_OK(hipFree(ds));
   HIP_OK(hipFree(ds2));
   HIP_OK(hipFree(ddeq));
+  HIP_OK(hipFree(ddeq2));
   std::printf("gpu client ok: %lldx%lld at [%d,%d], graph replays equal\n",
               static_cast<long long>(M), static_cast<long long>(N), bm, bn);
   return 0;
