@@ -330,7 +330,9 @@ __device__ __forceinline__ void vec_unit(const Desc& d, int64_t ur, int64_t uc, 
 // the 2048-wide matrices wide units and the 768-wide ones one-tile units
 // (74.8% against 77.0% with one-tile units throughout), and eight-tile
 // 128x1024 units on 512-thread workgroups (single calls on 151937x4096 and
-// 32768x16384: 72-76% against 77-78%).
+// 32768x16384: 72-76% against 77-78%), and three-tile 128x384 units (48 of
+// 64 lanes active) for the MoE layers' 768-wide matrices beside four-tile
+// units for their 2048-wide ones (75.8% against 76.9%).
 template <bool CHECK>
 __device__ __forceinline__ void vec_unit_wide(const Desc& d, int64_t ur, int64_t uc, uint32_t* red) {
   constexpr int L = 32;
