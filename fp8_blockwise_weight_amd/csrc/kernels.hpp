@@ -332,7 +332,10 @@ __device__ __forceinline__ void vec_unit(const Desc& d, int64_t ur, int64_t uc, 
 // 128x1024 units on 512-thread workgroups (single calls on 151937x4096 and
 // 32768x16384: 72-76% against 77-78%), and three-tile 128x384 units (48 of
 // 64 lanes active) for the MoE layers' 768-wide matrices beside four-tile
-// units for their 2048-wide ones (75.8% against 76.9%).
+// units for their 2048-wide ones (75.8% against 76.9%), and raw buffer loads
+// and stores for interior units, the row step in the scalar offset and no
+// per-load address arithmetic (dense set 75.6-76.5% against 81.1%: the
+// compiler's split of these global loads, 22 then 10, runs faster).
 template <bool CHECK>
 __device__ __forceinline__ void vec_unit_wide(const Desc& d, int64_t ur, int64_t uc, uint32_t* red) {
   constexpr int L = 32;
