@@ -734,10 +734,15 @@ int shard_many(const fp8bq_shard* list, int32_t count, int32_t bm, int32_t bn, v
   fp8bq::ShardGroupArgs<fp8bq::kShardArgsMax> a;
   int32_t n = 0;
   int64_t total = 0;
+  // [128,128] quantize passes take four-tile units (shard_group_wide)
+  const bool wide = pass == 1 && bm == 128 && bn == 128;
   auto flush = [&]() {
     if (n == 0) return;
     a.start[n] = static_cast<int32_t>(total);
-    if (pass == 0) {
+    if (wide) {
+      hipLaunchKernelGGL((fp8bq::shard_group_wide<fp8bq::kShardArgsMax>), dim3(grid_for(total)),
+                         dim3(fp8bq::kThreads), kLds2PerCu, s, a, n, static_cast<int32_t>(total));
+    } else if (pass == 0) {
       if (rows) launch_shard_group<0, true>(a, n, bm, bn, total, lds, s);
       else launch_shard_group<0, false>(a, n, bm, bn, total, lds, s);
     } else {
@@ -758,7 +763,8 @@ int shard_many(const fp8bq_shard* list, int32_t count, int32_t bm, int32_t bn, v
       }
       continue;
     }
-    const int64_t units = rows ? ceil_div(b.M, 64) * b.TNl : b.TMl * b.TNl;
+    const int64_t units =
+        rows ? ceil_div(b.M, 64) * b.TNl : (wide ? b.TMl * ceil_div(b.TNl, 4) : b.TMl * b.TNl);
     if (n == fp8bq::kShardArgsMax || total + units > INT32_MAX) flush();
     if (units > INT32_MAX) {  // a single entry beyond 32-bit units: its own launch
       launch_shard_small(pass, b, t.amax, pass == 0 ? t.amax : t.scale_inv, s);

@@ -759,6 +759,43 @@ def test_shard_small_tile_kernels(gpu_lib):
             assert torch.equal(a2.view(torch.int32), s.view(torch.int32))
 
 
+def test_shard_many_four_tile_units(gpu_lib):
+    """The grouped [128,128] quantize pass takes four-tile units where four
+    whole tiles lie inside a shard and single tiles elsewhere: wide shards at
+    row and column phases (whole and partial units, widths not a multiple of
+    512) equal the single calls, also with the maxima converted in place,
+    and two equal the oracle."""
+    g = torch.Generator(device=DEV).manual_seed(67)
+    xs, phases = [], []
+    for i, (M, N, ph) in enumerate([(1000, 2048, (64, 0)), (1000, 2048, (0, 64)), (777, 1536, (0, 0)),
+                                    (300, 4096, (127, 8)), (129, 640, (1, 0)), (2048, 1000, (0, 0))] * 4):
+        xs.append((torch.randn((M, N), generator=g, device=DEV) * (0.01 + 0.01 * i)).to(torch.bfloat16))
+        phases.append(ph)
+    amaxs = fq.tile_amax_many(xs, (128, 128), phases)
+    outs = fq.quantize_with_amax_many(xs, amaxs, (128, 128), phases)
+    # maxima converted to scales in place: the table's scale_inv is amax itself
+    inplace = [a.clone() for a in amaxs]
+    q2s = [torch.empty_like(q) for q, _ in outs]
+    table = fq._shard_table(xs, phases, q2s, inplace, inplace)
+    lib = fq.load_library()
+    assert lib.fp8bq_quantize_amax_many(table, len(xs), 128, 128,
+                                        torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    outs2 = list(zip(q2s, inplace))
+    for i, (x, ph, a, (q, s), (q2, s2)) in enumerate(zip(xs, phases, amaxs, outs, outs2)):
+        q1, s1 = fq.quantize_with_amax(x, a, (128, 128), ph)
+        assert torch.equal(q.view(torch.uint8), q1.view(torch.uint8)), i
+        assert torch.equal(s.view(torch.int32), s1.view(torch.int32)), i
+        assert torch.equal(q2.view(torch.uint8), q1.view(torch.uint8)), i
+        assert torch.equal(s2.view(torch.int32), s1.view(torch.int32)), i
+    for i in (0, 1):
+        xb = bits_np(xs[i])
+        a_ref = oracle.tile_amax(xb, 128, 128, *phases[i])
+        q_ref, s_ref = oracle.quantize_with_amax(xb, 128, 128, a_ref, *phases[i])
+        assert np.array_equal(codes_np(outs[i][0]), q_ref), i
+        assert np.array_equal(scales_bits(outs[i][1]), scales_bits(s_ref)), i
+
+
 @pytest.mark.parametrize("block", [(128, 128), (64, 64), (1, 128), (32, 96)])
 def test_shard_many_matches_single_calls(gpu_lib, block):
     """Grouped shard calls over 300 shards (more than one 256-entry launch)
