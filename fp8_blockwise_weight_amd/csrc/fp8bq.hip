@@ -392,8 +392,8 @@ struct ResPlan {
   uint32_t nchunks;
 };
 
-// Per device: workgroups of resident_quant<48> held at once (0 unknown, -1
-// failed) and s_memrealtime ticks per microsecond.
+// Per device: workgroups of the resident kernels held at once (0 unknown,
+// -1 failed) and s_memrealtime ticks per microsecond.
 std::atomic<int> g_res_grid[kMaxDevices];
 std::atomic<int> g_res_tick_mhz[kMaxDevices];
 std::atomic<int64_t> g_res_wait_us{kResWaitUsDefault};
