@@ -58,7 +58,7 @@ def test_scale_kernels_divide_correctly_rounded_and_encode_e4m3(asm):
     assert len(bodies) >= 20
     divides = [n for n in bodies if re.search(r"quantize_one|quantize_group|quantize_flat|big_reduce|"
                                               r"big_group_reduce|big_quant|big_group_quant|"
-                                              r"finalize_scales|resident_quant", n)]
+                                              r"finalize_scales|resident_quant|shard_group_wide", n)]
     assert len(divides) >= 15
     for n in divides:
         b = bodies[n]
@@ -66,7 +66,7 @@ def test_scale_kernels_divide_correctly_rounded_and_encode_e4m3(asm):
             assert op in b, (n, op)
     for n in bodies:
         if re.search(r"quantize_one|quantize_group|quantize_flat|big_quant|big_group_quant|"
-                     r"shard_(small|rows|group)ILi1|encode_e4m3|resident_quant", n):
+                     r"shard_(small|rows|group)ILi1|shard_group_wide|encode_e4m3|resident_quant", n):
             assert "v_cvt_pk_fp8_f32" in bodies[n], n
         if "dequant" in n:
             assert "v_cvt_pk_f32_fp8" in bodies[n], n
