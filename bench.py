@@ -33,12 +33,15 @@ import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from fp8_blockwise_weight_amd import build as _build  # noqa: E402  (stdlib only, no torch)
+
 HBM_PEAK_GBS = 8000.0
 CPU_SAMPLE_VALUES = 770_000_000
 METRIC = "blockwise FP8 quantize GB/s (bf16 in + fp8/scale out), % of HBM peak, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_t128_dense36_traffic.md")
-KERNEL_SOURCES = ("fp8_blockwise_weight_amd/csrc/kernels.hpp", "fp8_blockwise_weight_amd/csrc/fp8bq.hip",
-                  "fp8_blockwise_weight_amd/csrc/div31.hpp")
 
 
 def log(*a):
@@ -50,39 +53,8 @@ def algorithmic_bytes(M, N, bm, bn):
     return 3 * M * N + 4 * TM * TN
 
 
-def _code_only(text):
-    """C++ source without comments, whitespace runs collapsed: comment and
-    layout edits leave the kernels, and so the fingerprint, unchanged."""
-    out, i, n = [], 0, len(text)
-    while i < n:
-        c = text[i]
-        if c == '"' or c == "'":                     # string or character literal
-            j = i + 1
-            while j < n and text[j] != c:
-                j += 2 if text[j] == "\\" else 1
-            out.append(text[i:j + 1])
-            i = j + 1
-        elif text.startswith("//", i):
-            j = text.find("\n", i)
-            i = n if j < 0 else j
-        elif text.startswith("/*", i):
-            j = text.find("*/", i + 2)
-            i = n if j < 0 else j + 2
-            out.append(" ")
-        else:
-            out.append(c)
-            i += 1
-    return " ".join("".join(out).split())
-
-
-def kernel_sha():
-    """Fingerprint of the kernel sources' code (comments excluded)."""
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
-            h.update(_code_only(f.read()).encode())
-        h.update(b"\0")
-    return h.hexdigest()[:16]
+_code_only = _build.code_only
+kernel_sha = _build.kernel_sha
 
 
 def committed_traffic():
@@ -203,9 +175,10 @@ def main():
     import torch
 
     import fp8_blockwise_weight_amd as fq
-    from fp8_blockwise_weight_amd import build as _build
 
-    _build.ensure_built()  # load what is built; build only when nothing is
+    _build.ensure_built()  # load the build of these sources; rebuild if it is of others
+    lib_sha = _build.built_sha()
+    log(f"libfp8bq.so built from sources {lib_sha}")
     lib = fq.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -17,10 +17,12 @@ def pytest_configure(config):
 
 
 def pytest_sessionstart(session):
-    # Load what is built; build only when nothing is (a fresh checkout).
+    # Load the build of these sources; rebuild when the library is missing
+    # or was built from other sources.
     from fp8_blockwise_weight_amd import build
 
     build.ensure_built()
+    print(f"libfp8bq.so built from sources {build.built_sha()}", flush=True)
 
 
 @pytest.fixture(scope="session")
