@@ -36,3 +36,15 @@ def gpu_lib():
 
     fq.load_library()
     return fq
+
+
+@pytest.fixture(scope="session")
+def oracle_pool():
+    """Oracle workers on the host's cores (at most 16) with two 4 GiB shared
+    blocks, for comparing full-size GPU outputs byte for byte."""
+    from oracle.pool import OraclePool
+
+    pool = OraclePool(4 << 30, arenas=2)
+    print(f"oracle pool: {pool.workers} worker processes", flush=True)
+    yield pool
+    pool.close()

@@ -113,3 +113,79 @@ def assert_properties_gpu(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, bm:
     xs = x.view(torch.int16) < 0
     qs = (codes & 0x80) != 0
     assert bool((xs == qs).all()), (what, "sign")
+
+
+class FullOracleCheck:
+    """Every byte and every scale of GPU results against the oracle, run on
+    the host's cores (``oracle.pool``).
+
+    ``add(name, x, q, s)`` copies the tensor's BF16 bits, codes and scales
+    into the current shared block; when a block is full its comparison starts
+    in the pool's workers while the next block is filled (the pool holds two
+    blocks).  ``finish()`` waits for every comparison and raises on the
+    first tensor that differs, naming its first differing byte or scale.
+    """
+
+    def __init__(self, pool, bm: int, bn: int, what: str = ""):
+        self.pool, self.bm, self.bn, self.what = pool, bm, bn, what
+        self.cur = 0
+        self.items = []
+        self.pending = [None] * len(pool.arenas)
+        self.failures = []
+        self.values = 0
+        self.tensors = 0
+        pool.arenas[0].reset()
+
+    def _stage(self, name, x, q, s):
+        """Copy one tensor's data into the current block; False if it is full."""
+        arena = self.pool.arenas[self.cur]
+        xa = arena.array(tuple(x.shape), np.uint16)
+        qa = arena.array(tuple(q.shape), np.uint8)
+        sa = arena.array(tuple(s.shape), np.float32)
+        if xa is None or qa is None or sa is None:
+            return False
+        for a, t, view_np, view_torch in ((xa, x, np.int16, torch.int16), (qa, q, np.uint8, torch.uint8),
+                                          (sa, s, np.float32, torch.float32)):
+            if a.size:
+                torch.from_numpy(a.view(view_np)).copy_(t.detach().view(view_torch))
+        self.items.append((name, xa, qa, sa))
+        return True
+
+    def _submit(self):
+        if self.items:
+            self.pending[self.cur] = self.pool.compare_async(self.items, self.bm, self.bn,
+                                                             self.pool.arenas[self.cur])
+            self.items = []
+        self.cur = (self.cur + 1) % len(self.pool.arenas)
+        self._collect(self.cur)
+        self.pool.arenas[self.cur].reset()
+
+    def _collect(self, k):
+        if self.pending[k] is not None:
+            for name, rec in self.pending[k].get().items():
+                if rec[0] or rec[2]:
+                    self.failures.append((name, rec))
+            self.pending[k] = None
+
+    def add(self, name, x, q, s):
+        assert tuple(q.shape) == tuple(x.shape)
+        need = 3 * x.numel() + 4 * s.numel() + 1024
+        if need > self.pool.arenas[0].nbytes:
+            raise ValueError(f"{name}: {need} bytes do not fit one shared block")
+        if not self._stage(name, x, q, s):
+            self._submit()
+            assert self._stage(name, x, q, s)
+        self.values += x.numel()
+        self.tensors += 1
+
+    def finish(self):
+        self._submit()
+        for k in range(len(self.pool.arenas)):
+            self._collect(k)
+        if self.failures:
+            name, (nb, first, ns, first_s) = self.failures[0]
+            msg = (f"{self.what}: {len(self.failures)} tensor(s) differ from the oracle; first {name}: "
+                   f"{nb} byte mismatches (first (row, col, got, want) = {first}), "
+                   f"{ns} scale mismatches (first tile {first_s})")
+            raise AssertionError(msg)
+        return self.tensors, self.values

@@ -1,6 +1,7 @@
 """The streaming quant_weights loop: ordering, grouping and pass-through on the
-CPU with a stand-in for the grouped launch; equality with single calls on
-the GPU."""
+CPU with a stand-in for the grouped launch; on the GPU every yielded code
+and descale against the oracle, with the order, the pass-through pairs, the
+casts and the squeezed descale checked too."""
 
 import pytest
 import torch
@@ -107,20 +108,72 @@ def test_squeeze_scale(monkeypatch):
     assert got["a.weight_scale_inv"].shape == (5,)
 
 
-@pytest.mark.gpu
-def test_stream_matches_single_calls(gpu_lib):
+def _stream_inputs(dev):
+    """A dense decoder layer and a slice of an MoE layer in model order, with
+    norms (1-D, passed through), a bias and an fp16 weight (cast to BF16)."""
     from fp8_blockwise_weight_amd import workloads as wl
 
-    specs = wl.c4_layer(0)[:40] + wl.c2()[:2]
     ws = []
-    for sp in specs:
-        ws.append((sp.name + ".weight", wl.materialize(sp, "cuda:0")))
-        ws.append((sp.name + ".bias", torch.zeros(sp.M, device="cuda:0")))
-    out = dict(stream.quant_weights(ws, (128, 128), group_max=16))
-    for name, x in ws:
-        if name.endswith("bias"):
-            assert out[name] is x
+    for sp in wl.c2():
+        if sp.name.endswith("q_proj"):
+            ws.append(("layers.0.input_layernorm.weight", torch.ones(4096, dtype=torch.bfloat16, device=dev)))
+        if sp.name.endswith("gate_proj"):
+            ws.append(("layers.0.post_attention_layernorm.weight",
+                       torch.ones(4096, dtype=torch.bfloat16, device=dev)))
+        ws.append((sp.name + ".weight", wl.materialize(sp, dev)))
+    ws.append(("layers.0.o_proj.bias", torch.zeros(4096, device=dev)))
+    for sp in wl.c4_layer(1)[:96]:
+        ws.append((sp.name + ".weight", wl.materialize(sp, dev)))
+    half = (torch.randn((640, 384), generator=torch.Generator(device=dev).manual_seed(7), device=dev)
+            * 0.05).to(torch.float16)
+    ws.append(("lm_head.weight", half))
+    return ws
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("limits", [dict(group_max=16, group_bytes=300 << 20),
+                                    dict(group_max=512, group_bytes=1 << 30),
+                                    dict(group_bytes=0)])
+def test_stream_matches_oracle(gpu_lib, oracle_pool, limits):
+    """Every yielded (name, q) and (name + "_scale_inv", s) pair against the
+    oracle, byte for byte and bit for bit, with groups cut inside the dense
+    layer and inside the MoE slice (or one tensor per launch); pass-through
+    pairs come out as the same objects, and the order is the input order."""
+    from gpu_helpers import FullOracleCheck
+
+    dev = "cuda:0"
+    ws = _stream_inputs(dev)
+    out = list(stream.quant_weights(ws, (128, 128), **limits))
+    want = []
+    for n, t in ws:
+        want += [n, n + "_scale_inv"] if (n.endswith("weight") and t.dim() == 2) else [n]
+    assert [n for n, _ in out] == want
+    got = dict(out)
+    chk = FullOracleCheck(oracle_pool, 128, 128, f"stream {limits}")
+    for name, t in ws:
+        if not (name.endswith("weight") and t.dim() == 2):
+            assert got[name] is t, name
             continue
-        q, s = fq.quantize(x, (128, 128))
-        assert torch.equal(out[name].view(torch.uint8), q.view(torch.uint8)), name
-        assert torch.equal(out[name + "_scale_inv"], s), name
+        q, s = got[name], got[name + "_scale_inv"]
+        assert q.dtype == torch.float8_e4m3fn and s.dtype == torch.float32, name
+        assert tuple(q.shape) == tuple(t.shape) and tuple(s.shape) == fq.scale_shape(*t.shape, 128, 128)
+        chk.add(name, t.to(torch.bfloat16), q, s)
+    n, values = chk.finish()
+    assert n == 7 + 96 + 1
+    del out, got
+
+
+@pytest.mark.gpu
+def test_stream_squeezed_scale_matches_oracle(gpu_lib):
+    """[1,128] blocks on 128-wide weights give an [M, 1] descale; with
+    ``squeeze_scale`` it comes out as [M] and still equals the oracle's."""
+    from gpu_helpers import assert_matches_oracle
+
+    g = torch.Generator(device="cuda:0").manual_seed(11)
+    ws = [(f"e{i}.weight", (torch.randn((m, 128), generator=g, device="cuda:0") * 0.03).to(torch.bfloat16))
+          for i, m in enumerate((1, 77, 300))]
+    got = dict(stream.quant_weights(ws, (1, 128), squeeze_scale=True))
+    for name, x in ws:
+        s = got[name + "_scale_inv"]
+        assert tuple(s.shape) == (x.shape[0],), name
+        assert_matches_oracle(x, got[name], s.unsqueeze(-1), 1, 128, name)
