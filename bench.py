@@ -12,15 +12,24 @@ Reported value: algorithmic GB/s = (2 B read + 1 B written per element +
                 `traffic` is the HBM byte count (FETCH_SIZE + WRITE_SIZE,
                 scaled by a copy-kernel calibration) from the committed
                 counter profile, or null if that profile is for other code;
-  cpu_baseline  the CPU oracle timed on a bounded sample of the same
-                workload (its first ~770M values: 4 of the 36 dense layers),
-                single process, on this host.
+  cpu_baseline  the CPU oracle timed on this host's cores (a pool of one
+                worker process per available core, at most 16) over the
+                whole benchmarked workload (or the first --cpu-values
+                values), from BF16 bits in host memory to codes and scales;
+  configs       (default run) the other weight sets in their own launch
+                configurations, measured in the same run: the 256x256
+                matrix, one dense layer (rotated copies, so the 256 MB
+                Infinity Cache cannot serve it), the MoE set (one launch per
+                layer) and the ragged set at each block size; wall and
+                kernel time per step, GB/s and percent of the HBM peak;
+  lib_sha       the fingerprint of the sources the loaded library was built from.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3]
                        [--workload dense|dense-layer|moe|ragged|vocab] [--block bm,bn]
-                       [--per-tensor] [--no-cpu-baseline] [--calibrate-copy] [--input-sha]
+                       [--copies N] [--per-tensor] [--no-cpu-baseline] [--cpu-values N]
+                       [--no-configs] [--calibrate-copy] [--input-sha]
 
-The CPU sample's inputs are hashed (SHA-256 per tensor on stderr, and a
+The first CPU-sample inputs are hashed (SHA-256 per tensor on stderr, and a
 digest of those in cpu_baseline.sample_sha256); --input-sha hashes every
 input of the workload.
 """
@@ -39,7 +48,6 @@ if ROOT not in sys.path:
 from fp8_blockwise_weight_amd import build as _build  # noqa: E402  (stdlib only, no torch)
 
 HBM_PEAK_GBS = 8000.0
-CPU_SAMPLE_VALUES = 770_000_000
 METRIC = "blockwise FP8 quantize GB/s (bf16 in + fp8/scale out), % of HBM peak, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_t128_dense36_traffic.md")
 
@@ -139,6 +147,127 @@ def build_workload(name, dev, block=None):
     return groups, block, desc
 
 
+class Prepared:
+    """A workload resident in HBM: its inputs (materialized once, cloned into
+    ``copies`` sets whose steps rotate, so that a set smaller than the 256 MB
+    Infinity Cache is not served from it), outputs and the host descriptor
+    table of every grouped call."""
+
+    def __init__(self, lib, groups, bm, bn, dev, sptr, copies=1):
+        import torch
+
+        import fp8_blockwise_weight_amd as fq
+        from fp8_blockwise_weight_amd import workloads as wl
+
+        t0 = time.perf_counter()
+        self.lib, self.bm, self.bn, self.sptr = lib, bm, bn, sptr
+        self.copies = max(1, int(copies))
+        self.calls = []          # per copy: [(entries, count, workspace)] per grouped call
+        self.keep = []           # copy 0: (xs, outs) per group
+        hold = []
+        base = [[wl.materialize(sp, dev) for sp in specs] for specs in groups]
+        for c in range(self.copies):
+            calls = []
+            for xs0 in base:
+                xs = xs0 if c == 0 else [x.clone() for x in xs0]
+                outs = [(torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=dev),
+                         torch.empty(fq.scale_shape(*x.shape, bm, bn), dtype=torch.float32, device=dev))
+                        for x in xs]
+                ws = torch.empty(max(fq.workspace_bytes(len(xs)), 1), dtype=torch.uint8, device=dev)
+                calls.append((fq.make_entries(xs, outs), len(xs), ws))
+                (self.keep if c == 0 else hold).append((xs, outs))
+            self.calls.append(calls)
+        self._hold = hold
+        specs = [sp for g in groups for sp in g]
+        self.bytes_per_step = sum(algorithmic_bytes(sp.M, sp.N, bm, bn) for sp in specs)
+        self.elements = sum(sp.M * sp.N for sp in specs)
+        self.tensors = len(specs)
+        self.launches = len(groups)
+        torch.cuda.synchronize()
+        log(f"generated {self.tensors} tensors, {self.elements / 1e9:.3f} G values"
+            f"{f' ({self.copies} copies)' if self.copies > 1 else ''} in {time.perf_counter() - t0:.1f}s")
+
+    def step(self, i):
+        lib, bm, bn, sptr = self.lib, self.bm, self.bn, self.sptr
+        for arr, count, ws in self.calls[i % self.copies]:
+            st = lib.fp8bq_quantize_many(arr, count, bm, bn, ws.data_ptr(), ws.numel(), sptr)
+            if st != 0:
+                raise RuntimeError(f"fp8bq_quantize_many failed: status {st}, "
+                                   f"hip error {lib.fp8bq_last_hip_error()}")
+
+    def time(self, steps, warmup, stream):
+        """W untimed steps, then K steps timed by the wall clock between two
+        device synchronizations, with HIP events on the launch stream around
+        each step.  Returns (wall ms per step, [event ms per step])."""
+        import torch
+
+        for i in range(warmup):
+            self.step(i)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            self.step(warmup + i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        return wall * 1e3 / steps, [a.elapsed_time(b) for a, b in evs]
+
+
+def config_records(lib, dev, sptr, stream, steps, warmup):
+    """Throughput of the other weight sets, each measured here in its own
+    launch configuration: the 256x256 matrix (launch-bound), one dense layer
+    (three rotated copies: 1.7 GB between reuses of a buffer, well above the
+    256 MB Infinity Cache), the MoE set (one grouped launch per layer) and the
+    ragged set at each block size (one launch per matrix).  Wall time per step
+    and kernel time per step (HIP events around the step) with their GB/s
+    and percent of the HBM peak."""
+    import torch
+    from fp8_blockwise_weight_amd import workloads as wl
+
+    plan = [
+        ("c1_256x256", "C1 256x256 with planted outliers and a zero tile, [128,128] (launch-bound)",
+         [wl.c1()], (128, 128), 1),
+        ("c2_dense_layer", "C2 one qwen3-8b-shaped layer (7 tensors), [128,128], 3 rotated copies",
+         [wl.c2()], (128, 128), 3),
+        ("c4_moe", "C4 moe 48 layers x 128 experts (w13 1536x2048, down 2048x768), [128,128], "
+                   "one grouped launch per layer", [wl.c4_layer(i) for i in range(wl.MOE_LAYERS)],
+         (128, 128), 1),
+    ]
+    for blk in wl.RAGGED_BLOCKS:
+        plan.append((f"c5_ragged_{blk[0]}x{blk[1]}",
+                     f"C5 ragged 1000x3000, 4097x11008, 151937x4096, 77x128 at [{blk[0]},{blk[1]}], "
+                     "one launch per matrix", [[sp] for sp in wl.c5()], blk, 1))
+    out = {}
+    for key, desc, groups, (bm, bn), copies in plan:
+        prep = Prepared(lib, groups, bm, bn, dev, sptr, copies=copies)
+        wall_ms, ev_ms = prep.time(steps, warmup, stream)
+        gpu_ms = sum(ev_ms) / len(ev_ms)
+        nbytes = prep.bytes_per_step
+        rec = {
+            "workload": desc,
+            "block": [bm, bn],
+            "tensors": prep.tensors,
+            "launches_per_step": prep.launches,
+            "rotated_copies": copies,
+            "algorithmic_bytes_per_step": nbytes,
+            "ms_per_step": round(wall_ms, 4),
+            "GBps": round(nbytes / (wall_ms * 1e-3) / 1e9, 1),
+            "pct_of_hbm_peak": round(100 * nbytes / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "gpu_ms_per_step": round(gpu_ms, 4),
+            "gpu_GBps": round(nbytes / (gpu_ms * 1e-3) / 1e9, 1),
+            "gpu_pct_of_hbm_peak": round(100 * nbytes / (gpu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        }
+        log(f"{key}: wall {wall_ms:.4f} ms/step ({rec['pct_of_hbm_peak']}% of peak), "
+            f"events {gpu_ms:.4f} ms/step ({rec['gpu_pct_of_hbm_peak']}%)")
+        out[key] = rec
+        del prep
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -159,11 +288,21 @@ def main():
     ap.add_argument("--per-tensor", action="store_true",
                     help="also time one fp8bq_quantize call per tensor (HIP events per call)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-values", type=int, default=0,
+                    help="bound the CPU oracle's sample to the first tensors holding about this "
+                         "many values (default 0: the whole workload)")
+    ap.add_argument("--copies", type=int, default=None,
+                    help="rotate this many copies of the inputs and outputs between steps "
+                         "(default: 3 for one dense layer, else 1)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration records of the default run")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of known size (for counter calibration)")
     ap.add_argument("--input-sha", action="store_true",
                     help="log the SHA-256 of every input tensor (copies the whole workload to the host)")
     args = ap.parse_args()
+    if args.copies is None:
+        args.copies = 3 if args.workload == "dense-layer" else 1
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU only; --gpus {args.gpus} is not supported "
               "(tiles are independent, so a multi-GPU run would shard rows on tile boundaries "
@@ -186,60 +325,17 @@ def main():
     groups, (bm, bn), desc = build_workload(args.workload, dev, block)
     from fp8_blockwise_weight_amd import workloads as wl
 
-    t0 = time.perf_counter()
-    calls = []       # (entries, count, workspace) per launch
-    keep = []        # tensors kept alive
-    total_bytes = 0
-    n_elems = 0
-    n_tensors = 0
-    for specs in groups:
-        xs = [wl.materialize(sp, dev) for sp in specs]
-        outs = [(torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=dev),
-                 torch.empty(fq.scale_shape(*x.shape, bm, bn), dtype=torch.float32, device=dev))
-                for x in xs]
-        ws = torch.empty(max(fq.workspace_bytes(len(xs)), 1), dtype=torch.uint8, device=dev)
-        arr = fq.make_entries(xs, outs)
-        calls.append((arr, len(xs), ws))
-        keep.append((xs, outs))
-        for sp in specs:
-            total_bytes += algorithmic_bytes(sp.M, sp.N, bm, bn)
-            n_elems += sp.M * sp.N
-        n_tensors += len(specs)
-    torch.cuda.synchronize()
-    log(f"generated {n_tensors} tensors, {n_elems / 1e9:.3f} G values in {time.perf_counter() - t0:.1f}s")
+    stream = torch.cuda.current_stream(dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    prep = Prepared(lib, groups, bm, bn, dev, sptr, copies=args.copies)
+    keep, total_bytes, n_elems, n_tensors = prep.keep, prep.bytes_per_step, prep.elements, prep.tensors
     if args.input_sha:
         for (xs, _), specs in zip(keep, groups):
             for x, sp in zip(xs, specs):
                 log(f"input sha256 {sp.name} {sp.M}x{sp.N} {tensor_sha256(x)}")
 
-    stream = torch.cuda.current_stream(dev)
-    sptr = ctypes.c_void_p(stream.cuda_stream)
-
-    def step():
-        for arr, count, ws in calls:
-            st = lib.fp8bq_quantize_many(arr, count, bm, bn, ws.data_ptr(), ws.numel(), sptr)
-            if st != 0:
-                raise RuntimeError(f"fp8bq_quantize_many failed: status {st}, "
-                                   f"hip error {lib.fp8bq_last_hip_error()}")
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # Per-step HIP events on the launch stream, and the wall clock around all steps.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    for a, b in evs:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ev_ms = [a.elapsed_time(b) for a, b in evs]
-    ms_per_step = wall * 1e3 / args.steps
-    launches = len(calls)
+    ms_per_step, ev_ms = prep.time(args.steps, args.warmup, stream)
+    launches = prep.launches
     mean_launch_ms = sum(ev_ms) / len(ev_ms) / launches
     bytes_per_launch = total_bytes / launches
     achieved = bytes_per_launch / (mean_launch_ms * 1e-3) / 1e9
@@ -297,16 +393,23 @@ def main():
     }
 
     cpu = None
+    xs_all = None
     if not args.no_cpu_baseline:
-        # A bounded sample of the same workload: the first tensors up to about
-        # 770M values (4 of the 36 dense layers; 10-30 s of single-core numpy).
         xs_all = [x for xs, _ in keep for x in xs]
         sp_all = [sp for specs in groups for sp in specs]
-        take, n = 0, 0
-        while take < len(sp_all) and n < CPU_SAMPLE_VALUES:
-            n += sp_all[take].M * sp_all[take].N
-            take += 1
-        cpu = cpu_baseline(xs_all[:take], sp_all[:take], bm, bn)
+        take, n = len(sp_all), 0
+        if args.cpu_values:
+            take = 0
+            while take < len(sp_all) and n < args.cpu_values:
+                n += sp_all[take].M * sp_all[take].N
+                take += 1
+        cpu = cpu_baseline(xs_all[:take], sp_all[:take], bm, bn, whole=take == len(sp_all))
+
+    configs = None
+    if args.workload == "dense" and args.block is None and not args.no_configs:
+        del keep, xs_all, prep
+        torch.cuda.empty_cache()
+        configs = config_records(lib, dev, sptr, stream, args.steps, args.warmup)
 
     out = {
         "metric": METRIC,
@@ -332,7 +435,10 @@ def main():
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "lib_sha": lib_sha,
     }
+    if configs is not None:
+        out["configs"] = configs
     if per_tensor is not None:
         out["per_tensor"] = per_tensor
     print(json.dumps(out), flush=True)
@@ -538,34 +644,50 @@ def tensor_sha256(x):
     return hashlib.sha256(x.view(torch.int16).cpu().numpy().view(np.uint8).tobytes()).hexdigest()
 
 
-def cpu_baseline(xs, specs, bm, bn):
-    """The CPU oracle (as it is, single process) on a bounded sample of the workload."""
+def cpu_baseline(xs, specs, bm, bn, whole=True):
+    """The CPU oracle as it is, on the host's cores: a pool of worker
+    processes (one per core this process may use, at most 16) quantizes the
+    sample one slab of whole tile rows at a time, from the BF16 bits in
+    shared host memory to the codes and scales.  The copy of the inputs to
+    the host is not timed."""
     import numpy as np
     import torch
 
-    import oracle
+    from oracle.pool import OraclePool
 
-    host = [x.view(torch.int16).cpu().numpy().view(np.uint16) for x in xs]
-    digest = hashlib.sha256()
-    for h, sp in zip(host, specs):
-        one = hashlib.sha256(h.tobytes()).hexdigest()
-        digest.update(bytes.fromhex(one))
-        log(f"input sha256 {sp.name} {sp.M}x{sp.N} {one}")
     nbytes = sum(algorithmic_bytes(sp.M, sp.N, bm, bn) for sp in specs)
     nel = sum(sp.M * sp.N for sp in specs)
-    t0 = time.perf_counter()
-    for h in host:
-        oracle.quantize(h, bm, bn)
-    dt = time.perf_counter() - t0
-    log(f"cpu oracle: {len(host)} tensors, {nel / 1e6:.1f} M values in {dt:.1f}s")
+    arena = sum(3 * sp.M * sp.N + 4 * -(-sp.M // bm) * -(-sp.N // bn) + 1024 for sp in specs)
+    digest = hashlib.sha256()
+    with OraclePool(arena) as pool:
+        items = []
+        t0 = time.perf_counter()
+        for i, (x, sp) in enumerate(zip(xs, specs)):
+            xa = pool.arena.array((sp.M, sp.N), np.uint16)
+            torch.from_numpy(xa.view(np.int16)).copy_(x.view(torch.int16))
+            qa = pool.arena.array((sp.M, sp.N), np.uint8)
+            sa = pool.arena.array((-(-sp.M // bm), -(-sp.N // bn)), np.float32)
+            items.append((i, xa, qa, sa))
+        log(f"cpu oracle: {len(items)} inputs copied to shared host memory in {time.perf_counter() - t0:.1f}s")
+        dt = pool.quantize(items, bm, bn)
+        workers = pool.workers
+        for (_, xa, _, _), sp in zip(items, specs[:4]):
+            one = hashlib.sha256(xa.tobytes()).hexdigest()
+            digest.update(bytes.fromhex(one))
+            log(f"input sha256 {sp.name} {sp.M}x{sp.N} {one}")
+        del items, xa, qa, sa
+    log(f"cpu oracle: {len(specs)} tensors, {nel / 1e6:.1f} M values in {dt:.1f}s on {workers} processes")
+    what = "the whole benchmarked workload" if whole else "the first tensors of the benchmarked workload"
     return {
         "value": round(nbytes / dt / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"first {len(host)} tensors ({nel} values) of the benchmarked workload, "
-                  f"numpy oracle in one process, {dt:.1f} s",
+        "sample": f"{what}: {len(specs)} tensors, {nel} values; the numpy oracle in {workers} worker "
+                  f"processes (one per available host core, at most 16), {dt:.1f} s wall from BF16 bits "
+                  "in host memory to codes and scales",
         "sample_sha256": digest.hexdigest(),
+        "sample_sha256_covers": f"the first {min(4, len(specs))} inputs",
     }
 
 

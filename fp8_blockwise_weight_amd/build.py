@@ -26,7 +26,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "fp8bq.hip")
-KERNEL_SOURCES = [SRC, os.path.join(HERE, "csrc", "kernels.hpp"), os.path.join(HERE, "csrc", "div31.hpp")]
+KERNEL_SOURCES = [os.path.join(HERE, "csrc", "kernels.hpp"), SRC, os.path.join(HERE, "csrc", "div31.hpp")]
 DEPS = KERNEL_SOURCES + [os.path.join(ROOT, "include", "fp8bq.h")]
 LIB = os.path.join(HERE, "libfp8bq.so")
 ARCH = "gfx950"

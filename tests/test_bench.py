@@ -26,7 +26,7 @@ def test_bench_json_line(gpu_lib):
     record with every key the contract names, consistent with itself."""
     print("bench.py --workload dense-layer --steps 3 --warmup 1", flush=True)
     res = subprocess.run([sys.executable, BENCH, "--workload", "dense-layer", "--steps", "3",
-                          "--warmup", "1", "--no-cpu-baseline"],
+                          "--warmup", "1", "--cpu-values", "1"],
                          capture_output=True, text=True, timeout=240, cwd=ROOT)
     assert res.returncode == 0, res.stderr[-2000:]
     rec = json.loads(res.stdout.strip().splitlines()[-1])
@@ -43,6 +43,14 @@ def test_bench_json_line(gpu_lib):
     assert roof["bound"] == "hbm" and roof["peak"] == 8000.0
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert 0 < roof["frac"] < 1
+    cpu = rec["cpu_baseline"]
+    assert cpu["kind"] == "oracle" and cpu["unit"] == "GB/s" and cpu["value"] > 0
+    assert 1 <= cpu["cores"] <= 16 and "1 tensors" in cpu["sample"]
+    sys.path.insert(0, ROOT)
+    from fp8_blockwise_weight_amd import build
+
+    assert rec["lib_sha"] == build.built_sha() == build.source_sha()
+    assert "configs" not in rec          # only the default run measures the other sets
     # value = algorithmic bytes / wall time per step
     want = rec["config"]["algorithmic_bytes_per_step"] / (rec["ms_per_step"] * 1e-3) / 1e9
     assert abs(rec["value"] - want) / want < 1e-3

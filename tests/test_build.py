@@ -28,7 +28,7 @@ def sandbox(tmp_path, monkeypatch):
         return [sys.executable, "-c", f"open({out!r}, 'w').write('lib')"]
 
     monkeypatch.setattr(build, "DEPS", srcs)
-    monkeypatch.setattr(build, "KERNEL_SOURCES", srcs[:3])
+    monkeypatch.setattr(build, "KERNEL_SOURCES", [srcs[1], srcs[0], srcs[2]])
     monkeypatch.setattr(build, "LIB", lib)
     monkeypatch.setattr(build, "command", fake_command)
     return srcs, lib, calls
