@@ -29,12 +29,14 @@ ERR_HIP = 4
 
 E4M3_MAX = 448.0
 EPS = 1e-10
+NOALLOC_MAX_TENSORS = 16384   # FP8BQ_NOALLOC_MAX_TENSORS
 
 # Every symbol include/fp8bq.h declares.
 EXPORTS = (
     "fp8bq_quantize",
     "fp8bq_many_workspace_bytes",
     "fp8bq_quantize_many",
+    "fp8bq_quantize_many_noalloc",
     "fp8bq_encode_e4m3",
     "fp8bq_dequantize",
     "fp8bq_dequantize_many",
@@ -110,6 +112,8 @@ def load_library() -> ctypes.CDLL:
     lib.fp8bq_quantize_many.argtypes = [ctypes.POINTER(TensorEntry), c_i32, c_i32, c_i32, c_vp,
                                         ctypes.c_size_t, c_vp]
     lib.fp8bq_quantize_many.restype = ctypes.c_int
+    lib.fp8bq_quantize_many_noalloc.argtypes = [ctypes.POINTER(TensorEntry), c_i32, c_i32, c_i32, c_vp]
+    lib.fp8bq_quantize_many_noalloc.restype = ctypes.c_int
     lib.fp8bq_dequantize.argtypes = [c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_vp, c_i32, c_vp]
     lib.fp8bq_dequantize.restype = ctypes.c_int
     lib.fp8bq_dequantize_many.argtypes = [ctypes.POINTER(DqEntry), c_i32, c_i32, c_i32, c_i32, c_vp]
@@ -337,6 +341,35 @@ def quantize_many(tensors: Sequence, block_size=(128, 128), outputs: Optional[Se
         _check("fp8bq_quantize_many",
                lib.fp8bq_quantize_many(arr, n, bm, bn, ws_ptr, ws_bytes, _stream(dev)))
     return views() if views is not None else outputs
+
+
+def quantize_many_noalloc(tensors: Sequence, outputs: Sequence, block_size=(128, 128)) -> List:
+    """``quantize_many`` into caller-supplied outputs through
+    ``fp8bq_quantize_many_noalloc``: no device memory is allocated anywhere in
+    the call (lists beyond 512 tensors use the library's per-device table
+    block).  Calls that overlap on one GPU race on that block; order them on
+    one stream.  Returns ``outputs``."""
+    import torch
+
+    bm, bn = block_shape(block_size)
+    tensors, outputs = list(tensors), list(outputs)
+    if len(outputs) != len(tensors):
+        raise ValueError("outputs must hold one (q, scale_inv) pair per tensor")
+    if not tensors:
+        return outputs
+    if len(tensors) > NOALLOC_MAX_TENSORS:
+        raise ValueError(f"at most {NOALLOC_MAX_TENSORS} tensors per call, got {len(tensors)}")
+    dev = tensors[0].device
+    for x, out in zip(tensors, outputs):
+        _check_input(x)
+        if x.device != dev:
+            raise ValueError("all tensors of one grouped call must be on the same device")
+        _check_outputs(out, *x.shape, bm, bn, dev)
+    arr = make_entries(tensors, outputs)
+    with torch.cuda.device(dev):
+        _check("fp8bq_quantize_many_noalloc",
+               load_library().fp8bq_quantize_many_noalloc(arr, len(tensors), bm, bn, _stream(dev)))
+    return outputs
 
 
 def dequantize(q, scale_inv, block_size=(128, 128), out_dtype=None, out=None):
@@ -571,6 +604,7 @@ __all__ = [
     "dequantize_many", "encode_e4m3",
     "load_library", "local_grid", "quantize_with_amax", "quantize_with_amax_many", "tile_amax",
     "tile_amax_many", "ShardEntry",
-    "make_entries", "quantize", "quantize_many", "scale_shape", "set_resident_wait_us",
+    "make_entries", "quantize", "quantize_many", "quantize_many_noalloc", "scale_shape",
+    "set_resident_wait_us",
     "workspace_bytes",
 ]

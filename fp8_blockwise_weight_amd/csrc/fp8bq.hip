@@ -10,11 +10,25 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <utility>
 #include <vector>
 
 #include "fp8bq.h"
 #include "kernels.hpp"
+
+// Device memory of fp8bq_quantize_many_noalloc: the descriptor table of a
+// grouped call of more than FP8BQ_MANY_ARGS_MAX tensors (64-byte entries,
+// then the int64 unit prefix sums), laid out as in a caller's workspace.
+// Each device holds its own copy for the life of the process.  Host code
+// never passes this name to a kernel (on the host it is a stand-in, not a
+// device address): it uses the address hipGetSymbolAddress gives per device.
+constexpr size_t kScratchBytes =
+    (sizeof(fp8bq::Desc) * FP8BQ_NOALLOC_MAX_TENSORS + 255) / 256 * 256 +
+    (sizeof(int64_t) * (FP8BQ_NOALLOC_MAX_TENSORS + 1) + 255) / 256 * 256;
+static_assert(sizeof(fp8bq::Desc) == 64 && kScratchBytes == 1179904,
+              "include/fp8bq.h states the size of this block");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -653,6 +667,35 @@ thread_local std::vector<int64_t> g_starts;
 
 size_t descs_bytes(int32_t count) { return align_up(sizeof(Desc) * static_cast<size_t>(count), 256); }
 
+// Per device: the address of that device's copy of `scratch`, looked up once
+// with the device current (nullptr until then).
+std::atomic<unsigned char*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_pointer(unsigned char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_failed(e);
+  if (dev < 0 || dev >= kMaxDevices) return FP8BQ_ERR_UNSUPPORTED_DEVICE;
+  unsigned char* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_failed(e);
+      p = static_cast<unsigned char*>(addr);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return FP8BQ_OK;
+}
+
+int quantize_many_impl(const fp8bq_tensor* list, int32_t count, int32_t bm, int32_t bn,
+                       unsigned char* workspace, void* stream);
+
 // Host staging of one grouped call's descriptor table, reused per thread.
 thread_local std::vector<unsigned char> g_stage;
 
@@ -917,6 +960,30 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
                    (reinterpret_cast<uintptr_t>(workspace) & 15) != 0)) {
     return FP8BQ_ERR_WORKSPACE;
   }
+  return quantize_many_impl(list, count, bm, bn, static_cast<unsigned char*>(workspace), stream);
+}
+
+int fp8bq_quantize_many_noalloc(const fp8bq_tensor* list, int32_t count, int32_t bm, int32_t bn,
+                                void* stream) {
+  if (count < 0 || bm < 1 || bn < 1) return FP8BQ_ERR_INVALID_ARGUMENT;
+  if (count == 0) return FP8BQ_OK;
+  if (list == nullptr) return FP8BQ_ERR_INVALID_ARGUMENT;
+  if (count > FP8BQ_NOALLOC_MAX_TENSORS) return FP8BQ_ERR_WORKSPACE;
+  return quantize_many_impl(list, count, bm, bn, nullptr, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The body of both grouped entry points.  `workspace` receives the
+// descriptor table when it travels by copy; nullptr selects this device's
+// copy of `scratch` instead (fp8bq_quantize_many_noalloc; its count is
+// already bounded by FP8BQ_NOALLOC_MAX_TENSORS).  Every argument check runs
+// before the first HIP call.
+int quantize_many_impl(const fp8bq_tensor* list, int32_t count, int32_t bm, int32_t bn,
+                       unsigned char* workspace, void* stream) {
+  const size_t need = fp8bq_many_workspace_bytes(count);
   int kind = kind_of(bm, bn);
   if (kind == fp8bq::kT128 || kind == fp8bq::kT64) {
     const int64_t rows = kind == fp8bq::kT128 ? 128 : 64;
@@ -1057,7 +1124,11 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
     int64_t* start = reinterpret_cast<int64_t*>(g_stage.data() + descs_bytes(count));
     std::memcpy(start, g_starts.data(), sizeof(int64_t) * static_cast<size_t>(n));
     start[n] = total;
-    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    unsigned char* ws = workspace;
+    if (ws == nullptr) {
+      st = scratch_pointer(&ws);
+      if (st != FP8BQ_OK) return st;
+    }
     const size_t used = descs_bytes(count) + sizeof(int64_t) * (static_cast<size_t>(n) + 1);
     hipError_t e = hipMemcpyAsync(ws, g_stage.data(), used, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_failed(e);
@@ -1076,6 +1147,10 @@ int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
 }
+
+}  // namespace
+
+extern "C" {
 
 int fp8bq_tile_amax(const void* x, int64_t M, int64_t N, int32_t bm, int32_t bn, int32_t row_phase,
                     int32_t col_phase, float* amax, void* stream) {

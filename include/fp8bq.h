@@ -140,6 +140,33 @@ size_t fp8bq_many_workspace_bytes(int32_t count);
 int fp8bq_quantize_many(const fp8bq_tensor* list, int32_t count, int32_t bm, int32_t bn,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* Largest list fp8bq_quantize_many_noalloc takes. */
+#define FP8BQ_NOALLOC_MAX_TENSORS 16384
+
+/*
+ * fp8bq_quantize_many without a workspace, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, results and rules as
+ * fp8bq_quantize_many, whose kernels it launches; where that call copies the
+ * descriptor table of more than FP8BQ_MANY_ARGS_MAX tensors into the
+ * caller's workspace, this one copies it into device memory the library
+ * holds: one block of 1,179,904 bytes per GPU it runs on, kept until the
+ * process ends.  It calls no hipMalloc, hipFree or other allocating routine.
+ *   count  0 .. FP8BQ_NOALLOC_MAX_TENSORS; larger lists return
+ *          FP8BQ_ERR_WORKSPACE with nothing enqueued
+ * Every call on one GPU shares that block, and a call's copy and launch read
+ * it until the launch ends: calls that overlap on one GPU (other streams,
+ * other threads, without ordering between them) race.  Order them on one
+ * stream, or use fp8bq_quantize_many with a workspace per stream.  Lists of
+ * at most FP8BQ_MANY_ARGS_MAX tensors, and any list while `stream` is
+ * capturing a graph, carry their table in the kernel arguments and do not
+ * touch the block.  Nothing in it needs to start at zero: each call writes
+ * the whole table it reads.
+ * Returns an fp8bq_status; on an argument error nothing is enqueued.
+ */
+int fp8bq_quantize_many_noalloc(const fp8bq_tensor* list, int32_t count, int32_t bm, int32_t bn,
+                                void* stream);
+
 /*
  * Shards and large tiles.  A shard is an [M, N] sub-matrix of a larger
  * matrix whose element (0,0) sits at (row_phase, col_phase) inside a tile of

@@ -127,6 +127,31 @@ def test_quantize_many_rejects(lib):
     assert f(bad, 1, 128, 128, W, need, None) == INVALID
 
 
+def test_quantize_many_noalloc_rejects(lib):
+    """The workspace-free grouped call checks everything before any HIP call:
+    lists beyond FP8BQ_NOALLOC_MAX_TENSORS are refused (nothing read past the
+    count check), and the usual argument errors."""
+    f = lib.fp8bq_quantize_many_noalloc
+    good = _entries([(X, Q, S, 256, 256)])
+    assert fq.NOALLOC_MAX_TENSORS == 16384
+    assert f(good, fq.NOALLOC_MAX_TENSORS + 1, 128, 128, None) == WORKSPACE
+    assert f(good, -1, 128, 128, None) == INVALID
+    assert f(None, 1, 128, 128, None) == INVALID
+    assert f(good, 1, 0, 128, None) == INVALID
+    assert f(good, 1, 128, 0, None) == INVALID
+    assert f(None, 0, 128, 128, None) == fq.OK
+    empty = _entries([(None, None, None, 0, 4096), (None, None, None, 7, 0)])
+    assert f(empty, 2, 128, 128, None) == fq.OK
+    bad = _entries([(X, Q, S, 256, 256), (X + 0x1000000, None, S + 0x1000, 4, 4)])
+    assert f(bad, 2, 128, 128, None) == INVALID
+    many = _entries([(X + i * 0x100000, Q + i * 0x100000, S + i * 0x1000, 256, 256)
+                     for i in range(599)] + [(X, X + 64, S, 256, 256)])   # the last: q overlaps x
+    assert f(many, 600, 128, 128, None) == INVALID
+    with pytest.raises(ValueError):
+        fq.quantize_many_noalloc([None] * (fq.NOALLOC_MAX_TENSORS + 1),
+                                 [None] * (fq.NOALLOC_MAX_TENSORS + 1))
+
+
 def _shards(rows):
     arr = (fq.ShardEntry * len(rows))()
     for e, (x, q, a, sc, M, N, rp, cp) in zip(arr, rows):
