@@ -246,48 +246,87 @@ def make_entries(tensors: Sequence, outputs: Sequence) -> ctypes.Array:
     return (TensorEntry * len(tensors)).from_buffer(buf)
 
 
-def _group_outputs(tensors: Sequence, bm: int, bn: int, device, entries=None):
+def _plan_outputs(shapes: Sequence, ptrs: Sequence, bm: int, bn: int, device):
     """Outputs for a grouped call: one q buffer and one scale buffer per
     distinct row length N, holding the tensors' [M, N] / [TM, TN] outputs
     one after another in input order (contiguous and disjoint).  Two
     allocations per row length instead of two per tensor: for lists of
     thousands of small matrices the allocations, not the kernel, set the
-    pace.  Fills ``entries`` (a bytearray of the ``fp8bq_tensor`` array)
-    from the buffers' addresses when given.  Returns a function that cuts
-    the per-tensor views; calling it after the launch lets the device start
-    while the host builds them."""
+    pace.  ``shapes`` and ``ptrs`` are the inputs' (M, N) and data pointers.
+    Returns the ``fp8bq_tensor`` array (a bytearray) filled from the buffers'
+    addresses, and a function that cuts the per-tensor views as two lists
+    (q views, scale views) in input order; calling it after the launch lets
+    the device start while the host builds them."""
     import torch
 
+    n = len(shapes)
     by_n = {}
-    for i, x in enumerate(tensors):
-        M, N = x.shape
+    for i, (M, N) in enumerate(shapes):
         g = by_n.get(N)
         if g is None:
             by_n[N] = g = ([], [])
         g[0].append(i)
         g[1].append(M)
+    entries = bytearray(_ENTRY.size * n)
+    pack, size = _ENTRY.pack_into, _ENTRY.size
     plan = []
     for N, (idx, ms) in by_n.items():
         tms = [-(-m // bm) for m in ms]
         TN = -(-N // bn)
         qbuf = torch.empty((sum(ms), N), dtype=torch.float8_e4m3fn, device=device)
         sbuf = torch.empty((sum(tms), TN), dtype=torch.float32, device=device)
-        if entries is not None:
-            qp, sp = qbuf.data_ptr(), sbuf.data_ptr()
-            for i, m, tm in zip(idx, ms, tms):
-                _ENTRY.pack_into(entries, _ENTRY.size * i, tensors[i].data_ptr(), qp, sp, m, N)
-                qp += m * N
-                sp += 4 * tm * TN
+        qp, sp = qbuf.data_ptr(), sbuf.data_ptr()
+        for i, m, tm in zip(idx, ms, tms):
+            pack(entries, size * i, ptrs[i], qp, sp, m, N)
+            qp += m * N
+            sp += 4 * tm * TN
         plan.append((idx, qbuf, sbuf, ms, tms))
 
-    def views() -> List:
-        outs = [None] * len(tensors)
+    def views():
+        # outputs never require grad: views without autograd's view tracking
+        split = torch.unsafe_split_with_sizes
+        if len(plan) == 1:                 # one row length: the splits are in input order
+            _, qbuf, sbuf, ms, tms = plan[0]
+            return list(split(qbuf, ms)), list(split(sbuf, tms))
+        qs, ss = [None] * n, [None] * n
         for idx, qbuf, sbuf, ms, tms in plan:
-            for i, q, s in zip(idx, torch.split_with_sizes(qbuf, ms), torch.split_with_sizes(sbuf, tms)):
-                outs[i] = (q, s)
-        return outs
+            for i, q, sc in zip(idx, split(qbuf, ms), split(sbuf, tms)):
+                qs[i] = q
+                ss[i] = sc
+        return qs, ss
 
-    return views
+    return entries, views
+
+
+def _launch_many(arr, n: int, bm: int, bn: int, dev, workspace=None) -> None:
+    """fp8bq_quantize_many on ``dev``'s current stream (a workspace is made
+    when the table does not fit the kernel arguments and none is given)."""
+    import torch
+
+    lib = load_library()
+    need = int(lib.fp8bq_many_workspace_bytes(n))
+    if workspace is None:
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the tensors' device")
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    with torch.cuda.device(dev):
+        _check("fp8bq_quantize_many",
+               lib.fp8bq_quantize_many(arr, n, bm, bn, ws_ptr, ws_bytes, _stream(dev)))
+
+
+def _quantize_checked(xs: Sequence, shapes: Sequence, ptrs: Sequence, bm: int, bn: int, dev):
+    """One grouped call over inputs already checked (BF16, 2-D, contiguous,
+    all on ``dev``), given with their shapes and data pointers.  Returns the
+    q views and the scale views, two lists in input order."""
+    if dev.type != "cuda":
+        raise TypeError("x must be on a GPU (there is no CPU implementation)")
+    entries, views = _plan_outputs(shapes, ptrs, bm, bn, dev)
+    n = len(shapes)
+    _launch_many((TensorEntry * n).from_buffer(entries), n, bm, bn, dev)
+    return views()
 
 
 def quantize_many(tensors: Sequence, block_size=(128, 128), outputs: Optional[Sequence] = None,
@@ -308,6 +347,7 @@ def quantize_many(tensors: Sequence, block_size=(128, 128), outputs: Optional[Se
     dev = tensors[0].device
     index = tensors[0].get_device()
     bf16 = torch.bfloat16
+    shapes, ptrs = [], []
     for x in tensors:
         # the common case in one expression; _check_input names what is wrong
         if not (isinstance(x, torch.Tensor) and x.dtype is bf16 and x.dim() == 2 and x.is_cuda
@@ -315,32 +355,20 @@ def quantize_many(tensors: Sequence, block_size=(128, 128), outputs: Optional[Se
             _check_input(x)
         if x.get_device() != index:
             raise ValueError("all tensors of one grouped call must be on the same device")
+        shapes.append(tuple(x.shape))
+        ptrs.append(x.data_ptr())
     n = len(tensors)
     if outputs is None:
-        entries = bytearray(_ENTRY.size * n)
-        views = _group_outputs(tensors, bm, bn, dev, entries)
-        arr = (TensorEntry * n).from_buffer(entries)
-    else:
-        outputs = list(outputs)
-        if len(outputs) != n:
-            raise ValueError("outputs must hold one (q, scale_inv) pair per tensor")
-        for x, out in zip(tensors, outputs):
-            _check_outputs(out, *x.shape, bm, bn, dev)
-        views = None
-        arr = make_entries(tensors, outputs)
-    lib = load_library()
-    need = int(lib.fp8bq_many_workspace_bytes(n))
-    if workspace is None:
-        if need > 0:
-            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    elif workspace.device != dev or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous tensor on the tensors' device")
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    with torch.cuda.device(dev):
-        _check("fp8bq_quantize_many",
-               lib.fp8bq_quantize_many(arr, n, bm, bn, ws_ptr, ws_bytes, _stream(dev)))
-    return views() if views is not None else outputs
+        entries, views = _plan_outputs(shapes, ptrs, bm, bn, dev)
+        _launch_many((TensorEntry * n).from_buffer(entries), n, bm, bn, dev, workspace)
+        return list(zip(*views()))
+    outputs = list(outputs)
+    if len(outputs) != n:
+        raise ValueError("outputs must hold one (q, scale_inv) pair per tensor")
+    for (M, N), out in zip(shapes, outputs):
+        _check_outputs(out, M, N, bm, bn, dev)
+    _launch_many(make_entries(tensors, outputs), n, bm, bn, dev, workspace)
+    return outputs
 
 
 def quantize_many_noalloc(tensors: Sequence, outputs: Sequence, block_size=(128, 128)) -> List:

@@ -332,7 +332,12 @@ __device__ __forceinline__ void vec_unit(const Desc& d, int64_t ur, int64_t uc, 
 // 128x1024 units on 512-thread workgroups (single calls on 151937x4096 and
 // 32768x16384: 72-76% against 77-78%), and three-tile 128x384 units (48 of
 // 64 lanes active) for the MoE layers' 768-wide matrices beside four-tile
-// units for their 2048-wide ones (75.8% against 76.9%), and raw buffer loads
+// units for their 2048-wide ones (75.8% against 76.9%), and 256 x 256 units
+// of two by two tiles (32 loads per thread, all lanes active: each wave load
+// reads two 512-byte runs) for those 768-wide matrices beside four-tile
+// units, both layouts in one body switched by a per-tensor flag (MoE layers
+// 72.0% against 76.5%; the flag's extra arithmetic also cost the dense set
+// 81.4% -> 79.2%), and raw buffer loads
 // and stores for interior units, the row step in the scalar offset and no
 // per-load address arithmetic (dense set 75.6-76.5% against 81.1%: the
 // compiler's split of these global loads, 22 then 10, runs faster).

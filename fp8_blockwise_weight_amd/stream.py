@@ -17,14 +17,18 @@ group, so a decoder layer's projections share a launch.  Output order is
 the input order.  Which weights are FP8 is a caller predicate (the pages ask
 the inference engine's module types; this library has no engine, so the
 default is "a 2-D tensor whose name ends in ``weight``").
+
+The per-weight host work is what bounds a stream of small matrices (an MoE
+layer has hundreds), so each weight's shape, data pointer and device are read
+once, here, and the grouped launch takes them as they are (it checks once per
+group that the device is a GPU).
 """
 
 from typing import Callable, Iterable, Iterator, Tuple
 
-from . import block_shape, quantize_many
+from . import _quantize_checked, block_shape
 
 SCALE_SUFFIX = "_scale_inv"
-_FP8 = object()  # placeholder for a weight that is being quantized
 
 
 def default_is_fp8(name: str, tensor) -> bool:
@@ -41,44 +45,67 @@ def quant_weights(weights: Iterable[Tuple[str, object]], block_size=(128, 128),
     For an FP8 weight ``k`` the stream carries ``(k, q)`` and then
     ``(k + "_scale_inv", scale_inv)``; other pairs pass through unchanged.
     Weights are cast to ``dtype`` (default bfloat16) and made contiguous
-    first.  ``group_bytes=0`` quantizes one weight per launch (the pages'
-    one-at-a-time behaviour, lowest peak memory).  ``squeeze_scale`` drops
-    a trailing dimension of size 1 from the scale, as the SGLang loop does.
+    first; they must be 2-D and on one GPU.  ``group_bytes=0`` quantizes one
+    weight per launch (the pages' one-at-a-time behaviour, lowest peak
+    memory).  ``squeeze_scale`` drops a trailing dimension of size 1 from the
+    scale, as the SGLang loop does.
     """
     import torch
 
     bm, bn = block_shape(block_size)  # raises ValueError when the block size is missing
     dtype = dtype or torch.bfloat16
-    pending = []   # (name, tensor) in input order; _FP8 marks a weight in `xs`
-    xs = []        # the FP8 weights of the pending group, in order
+    if dtype is not torch.bfloat16:
+        raise TypeError("the quantizer takes BF16 input")
+    default = is_fp8 is default_is_fp8
+    pending = []   # (name, tensor) in input order; tensor None marks a queued FP8 weight
+    shapes = []    # (M, N) of the queued FP8 weights, in order
+    ptrs = []      # their data pointers
+    xs = []        # the BF16 inputs themselves, alive until their launch is enqueued
     nbytes = 0
+    device = None
+    index = None
 
     def flush():
-        nonlocal pending, xs, nbytes
+        nonlocal pending, shapes, ptrs, xs, nbytes
         if not pending:
             return
-        items, group = pending, xs
-        pending, xs, nbytes = [], [], 0
-        outs = iter(quantize_many(group, (bm, bn)) if group else ())
-        del group      # the BF16 inputs go once the launch is enqueued
+        items, sh, pt = pending, shapes, ptrs
+        pending, shapes, ptrs, nbytes = [], [], [], 0
+        qs, ss = _quantize_checked(xs, sh, pt, bm, bn, device) if sh else ((), ())
+        xs = []        # the BF16 inputs go once the launch is enqueued
+        if squeeze_scale:
+            ss = [s.squeeze(-1) if s.shape[-1] == 1 else s for s in ss]
+        k = 0
         for name, x in items:
-            if x is not _FP8:
+            if x is None:
+                yield name, qs[k]
+                yield name + SCALE_SUFFIX, ss[k]
+                k += 1
+            else:
                 yield name, x
-                continue
-            q, s = next(outs)
-            yield name, q
-            yield name + SCALE_SUFFIX, (s.squeeze(-1) if squeeze_scale and s.shape[-1] == 1 else s)
 
     for name, t in weights:
-        if not is_fp8(name, t):
+        if not ((name.endswith("weight") and t.ndim == 2) if default else is_fp8(name, t)):
             pending.append((name, t))
-            if not xs:
+            if not shapes:
                 yield from flush()   # nothing to wait for
             continue
-        x = t if (t.dtype is dtype and t.is_contiguous()) else t.to(dtype).contiguous()
-        pending.append((name, _FP8))
-        xs.append(x)
-        nbytes += x.numel() * x.element_size()
-        if len(xs) >= group_max or nbytes >= group_bytes:
+        if not (t.dtype is dtype and t.is_contiguous()):
+            t = t.to(dtype).contiguous()
+        d = t.get_device()           # -1 off the GPU; the grouped call refuses that device
+        if d != index:
+            if index is not None:
+                raise ValueError(f"{name}: FP8 weights must all be on one GPU ({t.device}, {device})")
+            index, device = d, t.device
+        try:
+            M, N = t.shape
+        except ValueError:
+            raise TypeError(f"{name}: FP8 weights must be 2-D, got shape {tuple(t.shape)}") from None
+        pending.append((name, None))
+        shapes.append((M, N))
+        ptrs.append(t.data_ptr())
+        xs.append(t)
+        nbytes += 2 * M * N
+        if nbytes >= group_bytes or len(shapes) >= group_max:
             yield from flush()
     yield from flush()

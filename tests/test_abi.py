@@ -346,10 +346,17 @@ def test_group_outputs_layout():
     shapes included (host logic, CPU tensors)."""
     import torch
 
-    shapes = [(5, 8), (3, 16), (0, 8), (7, 8), (2, 0), (130, 16), (1, 24)]
+    for shapes in ([(5, 8), (3, 16), (0, 8), (7, 8), (2, 0), (130, 16), (1, 24)],
+                   [(5, 16), (0, 16), (130, 16), (1, 16)]):      # several row lengths, or one
+        _check_group_outputs(torch, shapes)
+
+
+def _check_group_outputs(torch, shapes):
     xs = [torch.empty(sh, dtype=torch.bfloat16) for sh in shapes]
-    entries = bytearray(ctypes.sizeof(fq.TensorEntry) * len(xs))
-    outs = fq._group_outputs(xs, 4, 8, torch.device("cpu"), entries)()
+    entries, views = fq._plan_outputs([tuple(x.shape) for x in xs], [x.data_ptr() for x in xs],
+                                      4, 8, torch.device("cpu"))
+    assert len(entries) == ctypes.sizeof(fq.TensorEntry) * len(xs)
+    outs = list(zip(*views()))
     table = (fq.TensorEntry * len(xs)).from_buffer(entries)
     spans = []
     for x, (q, s), e in zip(xs, outs, table):

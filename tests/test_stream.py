@@ -11,14 +11,17 @@ from fp8_blockwise_weight_amd import stream
 
 
 class FakeGroup:
-    """Records grouped calls; returns (q, s) markers carrying the input name index."""
+    """Stands in for the grouped launch: records the group sizes, returns
+    marker outputs (the input's first value as q, a 1x1 scale)."""
 
     def __init__(self):
         self.calls = []
 
-    def __call__(self, xs, block):
+    def __call__(self, xs, shapes, ptrs, bm, bn, dev):
+        assert [tuple(x.shape) for x in xs] == list(shapes)
+        assert [x.data_ptr() for x in xs] == list(ptrs)
         self.calls.append(len(xs))
-        return [(("q", float(x[0, 0])), torch.ones(1, 1) * float(x[0, 0])) for x in xs]
+        return ([("q", float(x[0, 0])) for x in xs], [torch.ones(1, 1) * float(x[0, 0]) for x in xs])
 
 
 def _weights(n, bias_every=3):
@@ -32,7 +35,7 @@ def _weights(n, bias_every=3):
 
 def test_order_names_and_passthrough(monkeypatch):
     fake = FakeGroup()
-    monkeypatch.setattr(stream, "quantize_many", fake)
+    monkeypatch.setattr(stream, "_quantize_checked", fake)
     ws = _weights(7)
     got = list(stream.quant_weights(ws, (128, 128)))
     names = [n for n, _ in got]
@@ -49,7 +52,7 @@ def test_order_names_and_passthrough(monkeypatch):
 
 def test_grouping_limits(monkeypatch):
     fake = FakeGroup()
-    monkeypatch.setattr(stream, "quantize_many", fake)
+    monkeypatch.setattr(stream, "_quantize_checked", fake)
     ws = [(f"w{i}.weight", torch.zeros(4, 8, dtype=torch.bfloat16)) for i in range(10)]
     list(stream.quant_weights(ws, (128, 128), group_max=4))
     assert fake.calls == [4, 4, 2]
@@ -66,7 +69,7 @@ def test_passthrough_order_with_group_limits(monkeypatch):
     pair still comes out in input order, and a leading pass-through is not
     held back."""
     fake = FakeGroup()
-    monkeypatch.setattr(stream, "quantize_many", fake)
+    monkeypatch.setattr(stream, "_quantize_checked", fake)
     ws = [("embed.scale", torch.zeros(3))] + _weights(9, bias_every=2)
     it = stream.quant_weights(ws, (128, 128), group_max=4)
     assert next(it)[0] == "embed.scale"
@@ -80,7 +83,7 @@ def test_passthrough_order_with_group_limits(monkeypatch):
 
 
 def test_missing_block_size_raises(monkeypatch):
-    monkeypatch.setattr(stream, "quantize_many", FakeGroup())
+    monkeypatch.setattr(stream, "_quantize_checked", FakeGroup())
     with pytest.raises(ValueError):
         list(stream.quant_weights([("a.weight", torch.zeros(2, 2))], None))
 
@@ -88,11 +91,11 @@ def test_missing_block_size_raises(monkeypatch):
 def test_predicate_and_cast(monkeypatch):
     seen = []
 
-    def fake(xs, block):
+    def fake(xs, shapes, ptrs, bm, bn, dev):
         seen.extend((x.dtype, x.is_contiguous()) for x in xs)
-        return [(x, torch.ones(1, 1)) for x in xs]
+        return list(xs), [torch.ones(1, 1) for _ in xs]
 
-    monkeypatch.setattr(stream, "quantize_many", fake)
+    monkeypatch.setattr(stream, "_quantize_checked", fake)
     ws = [("a.weight", torch.zeros(8, 4).t()), ("b.kv_scale", torch.zeros(1)),
           ("c.weight", torch.zeros(3, 3, dtype=torch.float16))]
     got = list(stream.quant_weights(ws, (128, 128), is_fp8=lambda n, t: n.endswith("weight")))
@@ -101,9 +104,23 @@ def test_predicate_and_cast(monkeypatch):
     assert seen == [(torch.bfloat16, True), (torch.bfloat16, True)]
 
 
+def test_weights_must_be_2d(monkeypatch):
+    monkeypatch.setattr(stream, "_quantize_checked", FakeGroup())
+    with pytest.raises(TypeError, match="2-D"):
+        list(stream.quant_weights([("a.weight", torch.zeros(2, 2, 2))], (128, 128),
+                                  is_fp8=lambda n, t: True))
+
+
+def test_cpu_weights_are_refused():
+    """Without the stand-in: the grouped call refuses a group off the GPU
+    before anything reaches the library."""
+    with pytest.raises(TypeError, match="on a GPU"):
+        list(stream.quant_weights([("a.weight", torch.zeros(4, 8, dtype=torch.bfloat16))], (128, 128)))
+
+
 def test_squeeze_scale(monkeypatch):
-    monkeypatch.setattr(stream, "quantize_many",
-                        lambda xs, b: [(x, torch.ones(x.shape[0], 1)) for x in xs])
+    monkeypatch.setattr(stream, "_quantize_checked",
+                        lambda xs, sh, p, bm, bn, d: (list(xs), [torch.ones(x.shape[0], 1) for x in xs]))
     got = dict(stream.quant_weights([("a.weight", torch.zeros(5, 4))], (1, 128), squeeze_scale=True))
     assert got["a.weight_scale_inv"].shape == (5,)
 
