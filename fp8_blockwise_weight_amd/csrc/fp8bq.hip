@@ -1264,8 +1264,8 @@ int fp8bq_dequantize_many(const fp8bq_dq_tensor* list, int32_t count, int32_t bm
   (void)hipGetLastError();
   const int64_t G = out_dtype == FP8BQ_OUT_F32 ? 4 : 8;
   const int64_t per_block = static_cast<int64_t>(fp8bq::kThreads) * fp8bq::kDqUnroll;
-  // fp32 output over more than 8 entries: runs of 2 blocks and the counting
-  // table search; otherwise one block per unit and the binary search.
+  // fp32 output over more than 8 entries: runs of 2 blocks per unit;
+  // otherwise one block per unit.
   const bool f32 = out_dtype == FP8BQ_OUT_F32;
   int32_t vec_count = 0;
   for (int32_t i = 0; i < count; ++i) vec_count += vec[static_cast<size_t>(i)] && list[i].M > 0 && list[i].N > 0;
@@ -1280,11 +1280,11 @@ int fp8bq_dequantize_many(const fp8bq_dq_tensor* list, int32_t count, int32_t bm
     const int32_t tot = static_cast<int32_t>(total);
     constexpr int C = fp8bq::kDqArgsMax;
     if (f32 && run == 2) {
-      hipLaunchKernelGGL((fp8bq::dequant_group<fp8bq::kOutF32, C, 2, true>), grid, blk, 0, s, a, n, tot);
+      hipLaunchKernelGGL((fp8bq::dequant_group<fp8bq::kOutF32, C, 2>), grid, blk, 0, s, a, n, tot);
     } else if (f32) {
-      hipLaunchKernelGGL((fp8bq::dequant_group<fp8bq::kOutF32, C, 1, false>), grid, blk, 0, s, a, n, tot);
+      hipLaunchKernelGGL((fp8bq::dequant_group<fp8bq::kOutF32, C, 1>), grid, blk, 0, s, a, n, tot);
     } else {
-      hipLaunchKernelGGL((fp8bq::dequant_group<fp8bq::kOutBF16, C, 1, false>), grid, blk, 0, s, a, n, tot);
+      hipLaunchKernelGGL((fp8bq::dequant_group<fp8bq::kOutBF16, C, 1>), grid, blk, 0, s, a, n, tot);
     }
     n = 0;
     total = 0;

@@ -1620,15 +1620,24 @@ __global__ __launch_bounds__(kThreads) void dequant_vec(const uint8_t* __restric
 // rides in the kernel arguments.  A unit is a run of RUN consecutive blocks
 // of one tensor; unit u belongs to the entry whose first unit start[e] is
 // the largest <= u, found by a binary search over the table (eight
-// dependent scalar loads for 256 entries) or, with COUNT, by counting the
-// entries that start at or before u, one per thread, in one barrier.  The
-// run's first group is divided into (row, column) once (32-bit: the host
-// keeps every entry below 2^31 groups), then the position steps by whole
-// blocks.  Measured on MI355X (dense 36-layer set / 8 MoE layers / the
-// 151937x4096 matrix alone): fp32 output with RUN 1 and the search 70.4 /
-// 68.8 / 80.8% of peak, with RUN 2 and COUNT 73.8 / 75.4 / 72.0%; BF16 with
-// RUN 1 and the search 79.7 / 76.0 / 78.4%, with RUN 2 and COUNT 72.0 /
-// 75.3 / 74.8%; RUN 8 67 / 68 / 69%.
+// dependent scalar loads for 256 entries).  The run's first group is
+// divided into (row, column) once (32-bit: the host keeps every entry below
+// 2^31 groups), then the position steps by whole blocks.  Measured on
+// MI355X, % of the HBM peak (dense 36-layer set / 8 MoE layers / the
+// 151937x4096 matrix alone), one grouped call:
+//   fp32 out, RUN 1:                 68.6-70.4 / 68.8 / 80.6
+//   fp32 out, RUN 2:                 72.5 / 73.6 / 76.8     (taken for lists)
+//   fp32 out, RUN 4:                 69.3 / 70.0 / 71.1
+//   fp32 out, 4 groups per thread:   72.0 / 72.6 / 69.7  (RUN 2: 67.4 / 70.1 / 70.1)
+//   fp32 out, 8 groups per thread:   66.6 / 70.2 / 70.5
+//   BF16 out, RUN 1:                 79.0-79.7 / 79.3 / 76.8-78.4  (taken)
+//   BF16 out, RUN 2 / RUN 4:         71.2 / 73.8 / 74.1;  69.9 / 71.2 / 71.7
+// and, instead of the search, counting the entries that start at or before
+// u in one workgroup barrier: fp32 RUN 2 70.0-73.8 / 71.8-75.4 / 71.4,
+// BF16 RUN 2 72.0-72.2 / 75.3-76.1 / 74.8-75.6.  The same body over the
+// dense set as 252 single calls (no table) reached 72.9% for fp32 out: the
+// fp32 gap to the single large matrix follows the set's tensor sizes, not
+// the grouping.
 struct DqEntry {
   const uint8_t* q;
   const float* s;
@@ -1652,18 +1661,12 @@ struct DqGroupArgs {
   DqEntry e[CAP];
 };
 
-template <int OUT, int CAP, int RUN, bool COUNT>
+template <int OUT, int CAP, int RUN>
 __global__ __launch_bounds__(kThreads) void dequant_group(const DqGroupArgs<CAP> a, int32_t count,
                                                           int32_t total) {
-  static_assert(!COUNT || CAP <= kThreads, "one table entry per thread");
   const int64_t per_block = (int64_t)kThreads * kDqUnroll;
   for (int64_t u = blockIdx.x; u < total; u += gridDim.x) {
-    int i;
-    if constexpr (COUNT) {
-      i = __syncthreads_count((int)threadIdx.x < count && a.start[threadIdx.x] <= u) - 1;
-    } else {
-      i = find_tensor(a.start, count, u);
-    }
+    const int i = find_tensor(a.start, count, u);
     const DqEntry& e = a.e[i];
     int64_t b0 = (u - a.start[i]) * (per_block * RUN);
     int64_t row0 = div31((uint32_t)b0, e.by_gpr);
