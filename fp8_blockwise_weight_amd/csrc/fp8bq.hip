@@ -833,6 +833,27 @@ int shard_many(const fp8bq_shard* list, int32_t count, int32_t bm, int32_t bn, v
 }
 
 // Checks a dequantization call; *vec says whether it takes the vector body.
+// One grouped dequantization launch from a table filled up to entry n:
+// copied into a table of CAP entries, with the search's padding (INT32_MAX
+// past start[n], and in the coarse entries whose bucket lies past it).
+template <int CAP>
+void launch_dq_group(const fp8bq::DqGroupArgs<fp8bq::kDqArgsMax>& full, int32_t n, int32_t total,
+                     bool f32, dim3 grid, dim3 blk, hipStream_t s) {
+  fp8bq::DqGroupArgs<CAP> a;
+  std::memset(&a, 0, sizeof(a));
+  for (int k = 0; k <= n; ++k) a.start[k] = full.start[k];
+  for (int k = n + 1; k < CAP + fp8bq::kDqBucket; ++k) a.start[k] = INT32_MAX;
+  for (int k = 0; k < CAP / fp8bq::kDqBucket; ++k) {
+    a.coarse[k] = fp8bq::kDqBucket * k <= n ? a.start[fp8bq::kDqBucket * k] : INT32_MAX;
+  }
+  for (int k = 0; k < n; ++k) a.e[k] = full.e[k];
+  if (f32) {
+    hipLaunchKernelGGL((fp8bq::dequant_group<fp8bq::kOutF32, CAP>), grid, blk, 0, s, a, n, total);
+  } else {
+    hipLaunchKernelGGL((fp8bq::dequant_group<fp8bq::kOutBF16, CAP>), grid, blk, 0, s, a, n, total);
+  }
+}
+
 int check_dequant(const void* q, const float* scale_inv, int64_t M, int64_t N, int32_t bm,
                   int32_t bn, void* out, int32_t out_dtype, bool* vec) {
   *vec = false;
@@ -1264,13 +1285,9 @@ int fp8bq_dequantize_many(const fp8bq_dq_tensor* list, int32_t count, int32_t bm
   (void)hipGetLastError();
   const int64_t G = out_dtype == FP8BQ_OUT_F32 ? 4 : 8;
   const int64_t per_block = static_cast<int64_t>(fp8bq::kThreads) * fp8bq::kDqUnroll;
-  // fp32 output over more than 8 entries: runs of 2 blocks per unit;
-  // otherwise one block per unit.
   const bool f32 = out_dtype == FP8BQ_OUT_F32;
-  int32_t vec_count = 0;
-  for (int32_t i = 0; i < count; ++i) vec_count += vec[static_cast<size_t>(i)] && list[i].M > 0 && list[i].N > 0;
-  const int64_t run = f32 && vec_count > 8 ? 2 : 1;
-  fp8bq::DqGroupArgs<fp8bq::kDqArgsMax> a;
+  constexpr int C = fp8bq::kDqArgsMax;
+  fp8bq::DqGroupArgs<C> a;
   int32_t n = 0;
   int64_t total = 0;
   auto flush = [&]() {
@@ -1278,13 +1295,10 @@ int fp8bq_dequantize_many(const fp8bq_dq_tensor* list, int32_t count, int32_t bm
     a.start[n] = static_cast<int32_t>(total);
     const dim3 grid(grid_for(total)), blk(fp8bq::kThreads);
     const int32_t tot = static_cast<int32_t>(total);
-    constexpr int C = fp8bq::kDqArgsMax;
-    if (f32 && run == 2) {
-      hipLaunchKernelGGL((fp8bq::dequant_group<fp8bq::kOutF32, C, 2>), grid, blk, 0, s, a, n, tot);
-    } else if (f32) {
-      hipLaunchKernelGGL((fp8bq::dequant_group<fp8bq::kOutF32, C, 1>), grid, blk, 0, s, a, n, tot);
+    if (n <= fp8bq::kDqBucket) {
+      launch_dq_group<fp8bq::kDqBucket>(a, n, tot, f32, grid, blk, s);
     } else {
-      hipLaunchKernelGGL((fp8bq::dequant_group<fp8bq::kOutBF16, C, 1>), grid, blk, 0, s, a, n, tot);
+      launch_dq_group<C>(a, n, tot, f32, grid, blk, s);
     }
     n = 0;
     total = 0;
@@ -1297,8 +1311,8 @@ int fp8bq_dequantize_many(const fp8bq_dq_tensor* list, int32_t count, int32_t bm
       continue;
     }
     const int64_t groups = t.M * t.N / G;
-    const int64_t runs = ceil_div(groups, per_block * run);
-    if (groups >= (int64_t{1} << 31) - per_block * run) {  // beyond 32-bit group numbers: its own launch
+    const int64_t runs = ceil_div(groups, per_block);
+    if (groups >= (int64_t{1} << 31) - per_block) {  // beyond 32-bit group numbers: its own launch
       launch_dequant_vec(t.q, t.scale_inv, t.M, t.N, bm, bn, t.out, out_dtype, s);
       continue;
     }

@@ -742,7 +742,11 @@ __global__ __launch_bounds__(kThreads) void quantize_flat_one(Desc d, int64_t to
 // (start[0] = 0 <= u, non-decreasing).  start is uniform, so the search runs
 // on scalar loads.  For the quantize launches this beat counting the entries
 // at or before u in one workgroup barrier (dense 36-layer set 81.0% against
-// 73.4% of peak, MoE layers 76.7% against 74.4%).
+// 73.4% of peak, MoE layers 76.7% against 74.4%), and the two-level search
+// of the grouped dequantization (dense set 81.4% against 80.5%, MoE layers
+// 77.5% against 76.4%, ragged set at [64,64] 79.4% against 73.8%): a
+// quantize unit lives long enough to hide the search, and the extra scalar
+// registers cost more than its latency.
 template <typename T>
 __device__ __forceinline__ int find_tensor(const T* start, int count, int64_t u) {
   int lo = 0, hi = count - 1;
@@ -1617,27 +1621,30 @@ __global__ __launch_bounds__(kThreads) void dequant_vec(const uint8_t* __restric
 }
 
 // A list of tensors that take the vector body, in one launch: the table
-// rides in the kernel arguments.  A unit is a run of RUN consecutive blocks
-// of one tensor; unit u belongs to the entry whose first unit start[e] is
-// the largest <= u, found by a binary search over the table (eight
-// dependent scalar loads for 256 entries).  The run's first group is
-// divided into (row, column) once (32-bit: the host keeps every entry below
-// 2^31 groups), then the position steps by whole blocks.  Measured on
-// MI355X, % of the HBM peak (dense 36-layer set / 8 MoE layers / the
-// 151937x4096 matrix alone), one grouped call:
-//   fp32 out, RUN 1:                 68.6-70.4 / 68.8 / 80.6
-//   fp32 out, RUN 2:                 72.5 / 73.6 / 76.8     (taken for lists)
-//   fp32 out, RUN 4:                 69.3 / 70.0 / 71.1
-//   fp32 out, 4 groups per thread:   72.0 / 72.6 / 69.7  (RUN 2: 67.4 / 70.1 / 70.1)
-//   fp32 out, 8 groups per thread:   66.6 / 70.2 / 70.5
-//   BF16 out, RUN 1:                 79.0-79.7 / 79.3 / 76.8-78.4  (taken)
-//   BF16 out, RUN 2 / RUN 4:         71.2 / 73.8 / 74.1;  69.9 / 71.2 / 71.7
-// and, instead of the search, counting the entries that start at or before
-// u in one workgroup barrier: fp32 RUN 2 70.0-73.8 / 71.8-75.4 / 71.4,
-// BF16 RUN 2 72.0-72.2 / 75.3-76.1 / 74.8-75.6.  The same body over the
-// dense set as 252 single calls (no table) reached 72.9% for fp32 out: the
-// fp32 gap to the single large matrix follows the set's tensor sizes, not
-// the grouping.
+// rides in the kernel arguments.  Unit u is one block of one tensor: the
+// entry whose first unit start[e] is the largest <= u.  Dequantization
+// units are small (a few KB each), so the search that finds the entry is a
+// measurable share of a unit's life: it runs in two rounds of independent
+// uniform loads -- 15 entries of a contiguous coarse table (start[16 k])
+// pick a bucket of 16 entries, then those 15 entries pick the entry -- where
+// a binary search makes eight dependent loads.  Entries past the table hold
+// INT32_MAX, so neither round compares against the count.  The block's
+// first group is divided into (row, column) once (32-bit: the host keeps
+// every entry below 2^31 groups).  Lists of at most 16 entries use a table
+// of one bucket (one round of loads), and a list of one tensor no search at
+// all (151937x4096 alone, fp32 out: 75.5% with the two rounds).  Measured
+// on MI355X, % of the HBM peak
+// (dense 36-layer set / 8 MoE layers / the 151937x4096 matrix alone), one
+// grouped call, fp32 out | BF16 out:
+//   two-level search, 1 block per unit:       79.6 / 77.7 / 79.0 | 79.5 / 80.6 / 81.3  (taken)
+//   binary search, 1 block per unit:          68.5 / 70.1 / 80.6 | 79.8 / 79.1 / 77.8
+//   binary search, runs of 2 blocks per unit: 73.9 / 74.2 / 75.9 | 71.7 / 73.5 / 74.0
+//   two-level, 4 or 8 groups per thread:      68.5, 66.2 on the dense set (fp32)
+//   two-level, runs of 2 (2 / 4 groups):      73.7 / 70.2 on the dense set (fp32)
+// Also slower: the first two-level form, whose rounds the compiler split
+// into five dependent batches of loads (55% fp32 on the dense set), and
+// counting the entries with one ballot per four table entries per lane
+// (vector loads of the kernel-argument table: 55-61%).
 struct DqEntry {
   const uint8_t* q;
   const float* s;
@@ -1654,40 +1661,50 @@ struct DqEntry {
 };
 
 constexpr int kDqArgsMax = 256;
+constexpr int kDqBucket = 16;   // table entries per bucket of the two-level search
 
 template <int CAP>
 struct DqGroupArgs {
-  int32_t start[CAP + 1];
+  int32_t coarse[CAP / kDqBucket];  // start[16 k]; INT32_MAX past the table
+  int32_t start[CAP + kDqBucket];   // first unit of each entry, start[count] = total, then INT32_MAX
   DqEntry e[CAP];
 };
 
-template <int OUT, int CAP, int RUN>
+// Entry owning unit u (start[0] = 0 <= u < start[count]; start strictly
+// increasing, INT32_MAX past start[count]; units < 2^31).  A table of one
+// bucket (CAP 16) takes one round of loads.
+template <int CAP>
+__device__ __forceinline__ int find_entry_2level(const int32_t* coarse, const int32_t* start,
+                                                 int32_t u) {
+  static_assert(CAP % kDqBucket == 0 && CAP <= kDqBucket * kDqBucket, "at most 16 buckets");
+  int j = 0;
+#pragma unroll
+  for (int k = 1; k < CAP / kDqBucket; ++k) j += (int)(coarse[k] <= u);
+  const int b = kDqBucket * j;
+  int i = b;
+#pragma unroll
+  for (int k = 1; k < kDqBucket; ++k) i += (int)(start[b + k] <= u);
+  return i;
+}
+
+// Lists of up to 16 entries take CAP 16, longer ones CAP 256; a list of one
+// tensor skips the search.
+template <int OUT, int CAP>
 __global__ __launch_bounds__(kThreads) void dequant_group(const DqGroupArgs<CAP> a, int32_t count,
                                                           int32_t total) {
   const int64_t per_block = (int64_t)kThreads * kDqUnroll;
   for (int64_t u = blockIdx.x; u < total; u += gridDim.x) {
-    const int i = find_tensor(a.start, count, u);
+    const int i = count == 1 ? 0 : find_entry_2level<CAP>(a.coarse, a.start, (int32_t)u);
     const DqEntry& e = a.e[i];
-    int64_t b0 = (u - a.start[i]) * (per_block * RUN);
-    int64_t row0 = div31((uint32_t)b0, e.by_gpr);
-    int32_t col0 = (int32_t)(b0 - row0 * e.gpr);
-#pragma unroll
-    for (int r = 0; r < RUN; ++r) {
-      if (b0 >= e.groups) break;
-      if (b0 + per_block <= e.groups) {
-        dequant_block<OUT, false>(e.q, e.s, e.gpr, e.TN, e.by_gpr, e.by_bm, e.by_bn, e.out,
-                                  e.groups, e.last_row, b0, row0, col0);
-      } else {
-        dequant_block<OUT, true>(e.q, e.s, e.gpr, e.TN, e.by_gpr, e.by_bm, e.by_bn, e.out,
-                                 e.groups, e.last_row, b0, row0, col0);
-      }
-      b0 += per_block;
-      row0 += e.step_rows;
-      col0 += e.step_cols;
-      if (col0 >= e.gpr) {
-        col0 -= e.gpr;
-        ++row0;
-      }
+    const int64_t b0 = (u - a.start[i]) * per_block;
+    const int64_t row0 = div31((uint32_t)b0, e.by_gpr);
+    const int32_t col0 = (int32_t)(b0 - row0 * e.gpr);
+    if (b0 + per_block <= e.groups) {
+      dequant_block<OUT, false>(e.q, e.s, e.gpr, e.TN, e.by_gpr, e.by_bm, e.by_bn, e.out,
+                                e.groups, e.last_row, b0, row0, col0);
+    } else {
+      dequant_block<OUT, true>(e.q, e.s, e.gpr, e.TN, e.by_gpr, e.by_bm, e.by_bn, e.out,
+                               e.groups, e.last_row, b0, row0, col0);
     }
   }
 }
