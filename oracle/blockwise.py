@@ -218,9 +218,15 @@ def tile_amax(x_bits: np.ndarray, bm: int, bn: int, row_phase: int = 0, col_phas
     a = np.abs(bf16_bits_to_f64(x_bits))
     if not np.all(np.isfinite(a)):
         raise ValueError("non-finite input is outside the quantizer's contract")
-    padded = np.zeros((TM * bm, TN * bn), dtype=np.float64)
-    padded[row_phase:row_phase + M, col_phase:col_phase + N] = a
-    return padded.reshape(TM, bm, TN, bn).max(axis=(1, 3))
+    # local tile (ti, tj) covers rows [ti*bm - row_phase, (ti+1)*bm - row_phase)
+    # and columns [tj*bn - col_phase, (tj+1)*bn - col_phase) of the sub-matrix,
+    # clipped to it; every local tile holds at least one element
+    for ti in range(TM):
+        r0, r1 = max(0, ti * bm - row_phase), min(M, (ti + 1) * bm - row_phase)
+        for tj in range(TN):
+            c0, c1 = max(0, tj * bn - col_phase), min(N, (tj + 1) * bn - col_phase)
+            out[ti, tj] = a[r0:r1, c0:c1].max()
+    return out
 
 
 def quantize_with_amax(x_bits: np.ndarray, bm: int, bn: int, amax: np.ndarray,
