@@ -12,6 +12,15 @@ that tile's elements alone, and ``quantize`` walks the tensor one tile row at
 a time; a slab that starts and ends on tile-row boundaries therefore holds
 exactly the tiles, bytes and scales of those rows of the whole tensor.
 
+Tiles too large for one slab (one scale over a whole tensor, say) take two
+passes over pieces of the tile: ``oracle.tile_amax`` gives each piece's
+partial maxima, which combine by max into the tiles' maxima, and
+``oracle.quantize_with_amax`` quantizes each piece with them.  The pages'
+cast takes one maximum per tile, so cutting a tile, taking the max of the
+pieces' maxima and scaling every piece by the tile's reciprocal reproduces
+the whole tile (the oracle's own pins check that equivalence on shards cut
+anywhere).
+
 Data sits in one block of shared host memory (an anonymous memory file that
 the workers map through /proc): the main process copies inputs and outputs
 into arrays carved from it, workers map the same block and read and write
@@ -26,7 +35,7 @@ import time
 
 import numpy as np
 
-from .blockwise import quantize, tile_grid
+from .blockwise import local_grid, quantize, quantize_with_amax, tile_amax, tile_grid
 
 MAX_WORKERS = 16          # one GPU's share of a host's cores
 _ALIGN = 256
@@ -129,6 +138,32 @@ def _quantize_slab(task):
     return key
 
 
+def _piece(path, xd, c0, c1):
+    return _view(path, xd)[:, c0:c1]
+
+
+def _amax_piece(task):
+    """Partial tile maxima of one piece (rows of a slab, columns c0..c1) at
+    its tile phase.  Returns (key, first tile row, first tile column, maxima)."""
+    path, key, xd, c0, c1, bm, bn, rp, cp, t0, u0 = task
+    return key, t0, u0, tile_amax(_piece(path, xd, c0, c1), bm, bn, rp, cp)
+
+
+def _compare_piece_amax(task):
+    """One piece quantized with its tiles' full maxima, compared with the
+    given bytes.  Returns (key, (row, col) of the piece in the tensor,
+    mismatches, first (row, col, got, want) inside the piece)."""
+    path, key, xd, qd, c0, c1, bm, bn, rp, cp, origin, amax = task
+    q_ref, _ = quantize_with_amax(_piece(path, xd, c0, c1), bm, bn, amax, rp, cp)
+    q = _view(path, qd)[:, c0:c1]
+    bad = np.nonzero(q != q_ref)
+    first = None
+    if bad[0].size:
+        r, c = int(bad[0][0]), int(bad[1][0])
+        first = (r, c, int(q[r, c]), int(q_ref[r, c]))
+    return key, origin, int(bad[0].size), first
+
+
 def _ping(path):
     return _view(path, (0, (1,), "|u1")).shape
 
@@ -202,6 +237,57 @@ class OraclePool:
         first mismatch in the item's own row / tile-row numbering."""
         return self.compare_async(items, bm, bn, arena).get()
 
+    def _pieces(self, arena, x, r0, c0, bm, bn):
+        """Pieces of an array holding rows r0.. and columns c0.. of a tensor:
+        row groups of whole rows of the array, or column runs of single rows
+        when a row alone exceeds the piece size.  Yields (descriptor of the
+        row group, first and last column in the array, row phase, column
+        phase, first tile row, first tile column, row offset in the array)."""
+        M, N = x.shape
+        target = self.slab_values or min(max(x.size // (8 * self.workers), 1 << 20), 1 << 24)
+        rows = max(1, target // max(N, 1))
+        cols = N if rows > 1 or N <= target else target
+        for a in range(0, M, rows):
+            b = min(M, a + rows)
+            desc = arena.descriptor(x, a, b)
+            for ca in range(0, N, cols):
+                cb = min(N, ca + cols)
+                g, h = r0 + a, c0 + ca
+                yield desc, ca, cb, g % bm, h % bn, g // bm, h // bn, a
+
+    def tile_maxima_async(self, items, bm: int, bn: int, arena=None):
+        """Start the partial tile maxima of every item, where an item is
+        (key, x, r0, c0, TM, TN): the part of a tensor from row r0 and column
+        c0 on, whose full tile grid is TM x TN.  ``.get()`` gives {key:
+        float64 [TM, TN]} with the maxima over the items' elements (zero
+        where an item holds none of a tile)."""
+        arena = arena or self.arena
+        tasks, shapes = [], {}
+        for key, x, r0, c0, TM, TN in items:
+            shapes[key] = (TM, TN)
+            for desc, ca, cb, rp, cp, t0, u0, _ in self._pieces(arena, x, r0, c0, bm, bn):
+                tasks.append((arena.path, key, desc, ca, cb, bm, bn, rp, cp, t0, u0))
+        res = self.pool.map_async(_amax_piece, tasks, chunksize=1)
+        return _Maxima(shapes, res)
+
+    def compare_with_maxima_async(self, items, bm: int, bn: int, arena=None):
+        """Start comparing the bytes of every item, (key, x, q, r0, c0, amax):
+        the part of a tensor from row r0 and column c0 on and its codes,
+        quantized with the tensor's full tile maxima ``amax`` [TM, TN].
+        ``.get()`` gives {key: (byte mismatches, first (row, col, got, want)
+        in the tensor's coordinates)}."""
+        arena = arena or self.arena
+        tasks = []
+        for key, x, q, r0, c0, amax in items:
+            for desc, ca, cb, rp, cp, t0, u0, a in self._pieces(arena, x, r0, c0, bm, bn):
+                rows = desc[1][0]
+                TMl, TNl = local_grid(rows, cb - ca, bm, bn, rp, cp)
+                tasks.append((arena.path, key, desc, arena.descriptor(q, a, a + rows), ca, cb, bm, bn,
+                              rp, cp, (r0 + a, c0 + ca),
+                              np.ascontiguousarray(amax[t0:t0 + TMl, u0:u0 + TNl])))
+        res = self.pool.map_async(_compare_piece_amax, tasks, chunksize=1)
+        return _PieceComparison([key for key, *_ in items], res)
+
     def quantize(self, items, bm: int, bn: int, arena=None) -> float:
         """Quantize every item with the oracle into its q and s arrays;
         returns the wall time in seconds (the pool's work alone)."""
@@ -230,4 +316,35 @@ class _Comparison:
                 rec[2] += ns
                 cand = (first_s[0] + t0, first_s[1])
                 rec[3] = cand if rec[3] is None or cand < rec[3] else rec[3]
+        return {k: tuple(v) for k, v in out.items()}
+
+
+class _Maxima:
+    """Partial maxima of pieces, combined per item by max on ``get``."""
+
+    def __init__(self, shapes, res):
+        self.shapes, self.res = shapes, res
+
+    def get(self):
+        out = {key: np.zeros(shape, dtype=np.float64) for key, shape in self.shapes.items()}
+        for key, t0, u0, m in self.res.get():
+            dst = out[key][t0:t0 + m.shape[0], u0:u0 + m.shape[1]]
+            np.maximum(dst, m, out=dst)
+        return out
+
+
+class _PieceComparison:
+    """Byte mismatches of pieces, merged per item on ``get``."""
+
+    def __init__(self, keys, res):
+        self.keys, self.res = keys, res
+
+    def get(self):
+        out = {key: [0, None] for key in self.keys}
+        for key, (r0, c0), nb, first in self.res.get():
+            if nb:
+                rec = out[key]
+                rec[0] += nb
+                cand = (first[0] + r0, first[1] + c0) + first[2:]
+                rec[1] = cand if rec[1] is None or cand < rec[1] else rec[1]
         return {k: tuple(v) for k, v in out.items()}

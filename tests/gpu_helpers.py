@@ -122,9 +122,17 @@ class FullOracleCheck:
     ``add(name, x, q, s)`` copies the tensor's BF16 bits, codes and scales
     into the current shared block; when a block is full its comparison starts
     in the pool's workers while the next block is filled (the pool holds two
-    blocks).  ``finish()`` waits for every comparison and raises on the
-    first tensor that differs, naming its first differing byte or scale.
+    blocks).  A tensor larger than a block is cut into chunks of whole tile
+    rows, which the oracle quantizes independently.  A tensor whose tile rows
+    hold more than ``TILE_ROW_VALUES`` values (one scale over a whole tensor,
+    say) is compared in two streamed passes: its pieces' partial tile maxima,
+    combined by max, then every piece quantized with the full maxima; its
+    scales are the oracle's scales of those maxima.  ``finish()`` waits for
+    every comparison and raises on the first tensor that differs, naming its
+    first differing byte or scale.
     """
+
+    TILE_ROW_VALUES = 1 << 24
 
     def __init__(self, pool, bm: int, bn: int, what: str = ""):
         self.pool, self.bm, self.bn, self.what = pool, bm, bn, what
@@ -135,6 +143,10 @@ class FullOracleCheck:
         self.values = 0
         self.tensors = 0
         pool.arenas[0].reset()
+        # values of one chunk: 2 B of x and 1 B of q each, scales and alignment aside
+        nbytes = pool.arenas[0].nbytes
+        self.capacity = (nbytes - min(64 << 20, nbytes // 8)) // 3
+        self.origin = {}    # chunk key -> (tensor name, first row, first tile row)
 
     def _stage(self, name, x, q, s):
         """Copy one tensor's data into the current block; False if it is full."""
@@ -147,7 +159,7 @@ class FullOracleCheck:
         for a, t, view_np, view_torch in ((xa, x, np.int16, torch.int16), (qa, q, np.uint8, torch.uint8),
                                           (sa, s, np.float32, torch.float32)):
             if a.size:
-                torch.from_numpy(a.view(view_np)).copy_(t.detach().view(view_torch))
+                torch.from_numpy(a.view(view_np)).copy_(t.detach().contiguous().view(view_torch))
         self.items.append((name, xa, qa, sa))
         return True
 
@@ -162,26 +174,116 @@ class FullOracleCheck:
 
     def _collect(self, k):
         if self.pending[k] is not None:
-            for name, rec in self.pending[k].get().items():
-                if rec[0] or rec[2]:
-                    self.failures.append((name, rec))
+            for key, (nb, first, ns, first_s) in self.pending[k].get().items():
+                if nb or ns:
+                    name, r0, t0 = self.origin.get(key, (key, 0, 0))
+                    if first is not None:
+                        first = (first[0] + r0,) + first[1:]
+                    if first_s is not None:
+                        first_s = (first_s[0] + t0, first_s[1])
+                    self.failures.append((name, (nb, first, ns, first_s)))
             self.pending[k] = None
 
-    def add(self, name, x, q, s):
-        assert tuple(q.shape) == tuple(x.shape)
-        need = 3 * x.numel() + 4 * s.numel() + 1024
-        if need > self.pool.arenas[0].nbytes:
-            raise ValueError(f"{name}: {need} bytes do not fit one shared block")
+    def _drain(self):
+        """Finish everything in flight; both blocks free, block 0 current."""
+        if self.items:
+            self._submit()
+        for k in range(len(self.pool.arenas)):
+            self._collect(k)
+            self.pool.arenas[k].reset()
+        self.cur = 0
+
+    def _add_one(self, name, x, q, s):
         if not self._stage(name, x, q, s):
             self._submit()
             assert self._stage(name, x, q, s)
-        self.values += x.numel()
+
+    def add(self, name, x, q, s):
+        assert tuple(q.shape) == tuple(x.shape)
+        M, N = x.shape
+        bm, bn = self.bm, self.bn
+        self.values += M * N
         self.tensors += 1
+        if min(bm, M) * N > self.TILE_ROW_VALUES:
+            self._two_pass(name, x, q, s)
+            return
+        if 3 * M * N + 4 * s.numel() + 1024 <= self.capacity * 3:
+            self._add_one(name, x, q, s)
+            return
+        rows = max(bm, (self.capacity // max(N, 1)) // bm * bm)   # whole tile rows per chunk
+        for r0 in range(0, M, rows):
+            r1 = min(M, r0 + rows)
+            key = f"{name} rows {r0}..{r1 - 1}"
+            self.origin[key] = (name, r0, r0 // bm)
+            self._add_one(key, x[r0:r1], q[r0:r1], s[r0 // bm:-(-r1 // bm)])
+
+    def _chunks(self, M, N):
+        """(r0, r1, c0, c1) chunks of at most ``capacity`` values: whole rows,
+        or column runs of one row when a row alone is larger."""
+        cap = self.capacity
+        if N <= cap:
+            rows = cap // N
+            return [(r0, min(M, r0 + rows), 0, N) for r0 in range(0, M, rows)]
+        return [(r, r + 1, c0, min(N, c0 + cap)) for r in range(M) for c0 in range(0, N, cap)]
+
+    def _two_pass(self, name, x, q, s):
+        self._drain()
+        bm, bn = self.bm, self.bn
+        M, N = x.shape
+        TM, TN = -(-M // bm), -(-N // bn)
+        chunks = self._chunks(M, N)
+        arenas = self.pool.arenas
+        amax = np.zeros((TM, TN), dtype=np.float64)
+        handles = [None] * len(arenas)
+
+        def copy(arena, t, np_dtype, view_np, view_torch):
+            a = arena.array(tuple(t.shape), np_dtype)
+            torch.from_numpy(a.view(view_np)).copy_(t.detach().contiguous().view(view_torch))
+            return a
+
+        def merge(h):
+            if h is not None:
+                np.maximum(amax, h.get()[name], out=amax)
+
+        for i, (r0, r1, c0, c1) in enumerate(chunks):      # pass 1: tile maxima
+            k = i % len(arenas)
+            merge(handles[k])
+            arenas[k].reset()
+            xa = copy(arenas[k], x[r0:r1, c0:c1], np.uint16, np.int16, torch.int16)
+            handles[k] = self.pool.tile_maxima_async([(name, xa, r0, c0, TM, TN)], bm, bn, arenas[k])
+        for k in range(len(arenas)):
+            merge(handles[k])
+            handles[k] = None
+        nb, first = 0, None
+
+        def count(h):
+            nonlocal nb, first
+            if h is not None:
+                n1, f1 = h.get()[name]
+                nb += n1
+                if f1 is not None and (first is None or f1 < first):
+                    first = f1
+
+        for i, (r0, r1, c0, c1) in enumerate(chunks):      # pass 2: bytes with the full maxima
+            k = i % len(arenas)
+            count(handles[k])
+            arenas[k].reset()
+            xa = copy(arenas[k], x[r0:r1, c0:c1], np.uint16, np.int16, torch.int16)
+            qa = copy(arenas[k], q[r0:r1, c0:c1], np.uint8, np.uint8, torch.uint8)
+            handles[k] = self.pool.compare_with_maxima_async([(name, xa, qa, r0, c0, amax)], bm, bn,
+                                                             arenas[k])
+        for k in range(len(arenas)):
+            count(handles[k])
+            arenas[k].reset()
+        s_ref, _ = oracle.blockwise.tile_scales_np(amax)
+        bad_s = np.nonzero(scales_bits(s) != scales_bits(s_ref.astype(np.float32)))
+        ns = int(bad_s[0].size)
+        first_s = (int(bad_s[0][0]), int(bad_s[1][0])) if ns else None
+        if nb or ns:
+            self.failures.append((name, (nb, first, ns, first_s)))
 
     def finish(self):
-        self._submit()
-        for k in range(len(self.pool.arenas)):
-            self._collect(k)
+        self._drain()
         if self.failures:
             name, (nb, first, ns, first_s) = self.failures[0]
             msg = (f"{self.what}: {len(self.failures)} tensor(s) differ from the oracle; first {name}: "

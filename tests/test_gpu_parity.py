@@ -3,11 +3,11 @@
 Bit-exact in both outputs: every fp8 byte and every fp32 scale.  Small and
 medium tensors are compared whole in this process; the full-size weight sets
 (the 36-layer dense stack in the one grouped launch the benchmark times,
-all 48 MoE layers, the 151937x4096 matrix at every block size) are compared
-whole too, every byte and scale, by the oracle running on the host's cores
-(``oracle.pool``).  A few tests of shapes beyond the five configurations
-(2^31+ elements, one scale over a whole tensor) compare sampled tiles or
-rows plus every scale and size-independent invariants; each says so.
+all 48 MoE layers, the 151937x4096 matrix at every block size), the 2^31+
+element matrices and the one-scale-per-tensor cases are compared whole too,
+every byte and scale, by the oracle running on the host's cores
+(``oracle.pool``: slabs of whole tile rows, or two passes over pieces of
+tiles too large for a slab).
 """
 
 import numpy as np
@@ -17,8 +17,7 @@ import torch
 import fp8_blockwise_weight_amd as fq
 import oracle
 from fp8_blockwise_weight_amd import workloads as wl
-from gpu_helpers import (FullOracleCheck, assert_matches_oracle, assert_properties_gpu,
-                         assert_scales_match_oracle, assert_tiles_match_oracle, bits_np,
+from gpu_helpers import (FullOracleCheck, assert_matches_oracle, assert_properties_gpu, bits_np,
                          codes_np, scales_bits, tile_amax_gpu)
 
 pytestmark = pytest.mark.gpu
@@ -953,11 +952,11 @@ def test_grouped_large_tiles_many_tensors(gpu_lib):
 @pytest.mark.parametrize("M,N,bm,bn", [(6145, 16384, 6145, 16384),    # 3 chunks per pass-1 item, last item 1
                                       (4096, 16384, 4096, 16384),    # 2 chunks per item
                                       (8192, 8192, 4096, 2048)])     # 8 tiles of row runs, 2 per item
-def test_large_tiles_chunk_grouping(gpu_lib, M, N, bm, bn):
+def test_large_tiles_chunk_grouping(gpu_lib, oracle_pool, M, N, bm, bn):
     """Large tiles where pass-1 workgroups take several chunks each (the
-    host's chunks-per-workgroup above 1): single and grouped calls agree,
-    every scale comes from the exact tile maximum, and sampled row bands of
-    each tile match the oracle given that maximum."""
+    host's chunks-per-workgroup above 1): single and grouped calls agree, and
+    every byte and scale equals the oracle's (its two passes over pieces of
+    the tiles)."""
     say("chunk grouping", M, N, bm, bn)
     g = torch.Generator(device=DEV).manual_seed(M + N)
     x = (torch.randn((M, N), generator=g, device=DEV) * 0.03).to(torch.bfloat16)
@@ -966,31 +965,24 @@ def test_large_tiles_chunk_grouping(gpu_lib, M, N, bm, bn):
     ((qg, sg),) = fq.quantize_many([x], (bm, bn))
     assert torch.equal(q.view(torch.uint8), qg.view(torch.uint8))
     assert torch.equal(s.view(torch.int32), sg.view(torch.int32))
-    assert_scales_match_oracle(x, s, bm, bn, f"chunk grouping {M}x{N}")
-    amax = x.abs().float().view(-(-M // bm), bm, -(-N // bn), bn).amax(dim=(1, 3)).double().cpu().numpy()
-    for ti in range(amax.shape[0]):
-        for tj in range(amax.shape[1]):
-            for r0 in (ti * bm, ti * bm + bm // 2, (ti + 1) * bm - 8):
-                band = x[r0:r0 + 8, tj * bn:(tj + 1) * bn].contiguous()
-                q_ref, _ = oracle.quantize_with_amax(bits_np(band), 8, band.shape[1],
-                                                     np.array([[amax[ti, tj]]]))
-                got = codes_np(q[r0:r0 + 8, tj * bn:(tj + 1) * bn].contiguous())
-                assert np.array_equal(got, q_ref), (ti, tj, r0)
+    chk = FullOracleCheck(oracle_pool, bm, bn, f"chunk grouping {M}x{N} [{bm},{bn}]")
+    chk.add("x", x, q, s)
+    chk.finish()
 
 
-def test_per_tensor_vocab_matrix(gpu_lib):
-    """One scale for the whole 151937x4096 matrix (1.2 GB): the scale from the
-    exact maximum, sampled rows against the oracle, invariants everywhere."""
+def test_per_tensor_vocab_matrix(gpu_lib, oracle_pool):
+    """One scale for the whole 151937x4096 matrix (1.2 GB, one tile of 622M
+    values, the two-pass kernels): every byte and the scale against the
+    oracle (its two passes over pieces of the tile), invariants everywhere."""
     sp = [t for t in wl.c5() if t.M == 151937][0]
     x = wl.materialize(sp, DEV)
     q, s = fq.quantize(x, (sp.M, sp.N))
     amax = float(x.abs().max().float())
     assert float(s[0, 0]) == float(np.float32(max(amax, np.float32(1e-10)) / 448.0))
-    for r0 in (0, 1, 77777, sp.M - 300):
-        xs = x[r0:r0 + 300].contiguous()
-        q_ref, _ = oracle.quantize_with_amax(bits_np(xs), sp.M, sp.N, np.array([[amax]]))
-        assert np.array_equal(codes_np(q[r0:r0 + 300].contiguous()), q_ref), r0
     assert_properties_gpu(x, q, s, sp.M, sp.N, "vocab per-tensor")
+    chk = FullOracleCheck(oracle_pool, sp.M, sp.N, "vocab per-tensor")
+    chk.add(sp.name, x, q, s)
+    chk.finish()
 
 
 @pytest.mark.parametrize("M,N", [(1024, 1024),      # 2^20 values: 128 workgroups x 4 chunks
@@ -1026,15 +1018,16 @@ def test_per_tensor_held_in_registers(gpu_lib, M, N):
     assert torch.equal(q0.view(torch.uint8), q) and torch.equal(s0.view(torch.int32), s.view(torch.int32))
 
 
-def test_per_tensor_register_capacity(gpu_lib):
+def test_per_tensor_register_capacity(gpu_lib, oracle_pool):
     """12288x4096, the largest tensor the register-resident kernel holds on an
     MI355X (512 workgroups x 256 threads x 48 chunks), and 12289x4096, one
-    row more, which takes the two-pass path: exact scales, sampled rows
-    against the oracle, invariants everywhere; a grouped call mixing both
-    with a misaligned and a small tensor equals the single calls."""
+    row more, which takes the two-pass path: every byte and the scale against
+    the oracle, invariants everywhere; a grouped call mixing both with a
+    misaligned and a small tensor equals the single calls."""
     g = torch.Generator(device=DEV).manual_seed(83)
     outs = []
     xs = []
+    chk = FullOracleCheck(oracle_pool, 16384, 16384, "resident capacity")
     for M in (12288, 12289):
         say("resident capacity", M)
         x = (torch.randn((M, 4096), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
@@ -1043,13 +1036,11 @@ def test_per_tensor_register_capacity(gpu_lib):
         amax = float(x.abs().max().float())
         assert amax == 2.25
         assert float(s[0, 0]) == float(np.float32(np.float32(amax) / np.float32(448.0)))
-        for r0 in (0, 3001, M - 64):
-            band = x[r0:r0 + 64].contiguous()
-            q_ref, _ = oracle.quantize_with_amax(bits_np(band), 16384, 16384, np.array([[amax]]))
-            assert np.array_equal(codes_np(q[r0:r0 + 64].contiguous()), q_ref), (M, r0)
         assert_properties_gpu(x, q, s, 16384, 16384, f"capacity {M}")
+        chk.add(f"{M}x4096", x, q, s)
         xs.append(x)
         outs.append((q, s))
+    chk.finish()
     raw = (torch.randn(1500 * 1200 + 8, generator=g, device=DEV) * 0.1).to(torch.bfloat16)
     mis = raw[1:1 + 1500 * 1200].view(1500, 1200)   # x not 16-byte aligned: two-pass path
     small = (torch.randn((100, 200), generator=g, device=DEV)).to(torch.bfloat16)
@@ -1100,11 +1091,13 @@ def test_per_tensor_resident_groups(gpu_lib):
 
 # ------------------------------------------------------------------ maximum sizes
 
-def test_beyond_2_31_elements(gpu_lib):
+def test_beyond_2_31_elements(gpu_lib, oracle_pool):
     """A 33000x65536 matrix (2.16e9 elements, 4.3 GB) through the [128,128],
     [1,128] and register-tile kernels and a 1 x (2^31 - 1) row through the
-    general kernel: scales everywhere, tiles past element 2^31 against the
-    oracle, and the dequantized tail."""
+    general kernel, grouped [1,4096] tiles and one scale for the whole row:
+    every byte and scale against the oracle (chunks of whole tile rows, or
+    its two passes over pieces where a tile row is longer than a piece), and
+    the dequantized tail."""
     M, N = 33000, 65536
     g = torch.Generator(device=DEV).manual_seed(59)
     x = (torch.randn((M, N), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
@@ -1113,10 +1106,9 @@ def test_beyond_2_31_elements(gpu_lib):
         bm, bn = block
         say("2^31+", block)
         q, s = fq.quantize(x, block)
-        assert_scales_match_oracle(x, s, bm, bn, f"2^31+ {block}")
-        TM, TN = fq.scale_shape(M, N, bm, bn)
-        tiles = [(TM - 1, TN - 1), (TM - 1, 0), ((2 ** 31 // N) // bm + 1, TN // 2), (0, 0)]
-        assert_tiles_match_oracle(x, q, s, bm, bn, tiles, f"2^31+ {block}")
+        chk = FullOracleCheck(oracle_pool, bm, bn, f"2^31+ {block}")
+        chk.add(f"{M}x{N}", x, q, s)
+        chk.finish()
         tail = fq.dequantize(q[-bm:].contiguous(), s[-1:].contiguous(), block,
                              out_dtype=torch.bfloat16)
         want = oracle.dequantize(codes_np(q[-bm:].contiguous()), s[-1:].cpu().numpy(), bm, bn, "bf16")
@@ -1127,11 +1119,13 @@ def test_beyond_2_31_elements(gpu_lib):
     n = 2 ** 31 - 1
     row = (torch.randn((1, n), generator=g, device=DEV) * 0.02).to(torch.bfloat16)   # N odd: general kernel
     row[0, n - 1] = -7.0
+    say("1 x 2^31-1 [1,128]")
     q, s = fq.quantize(row, (1, 128))
     assert s.shape == (1, -(-n // 128))
-    assert_tiles_match_oracle(row, q, s, 1, 128, [(0, 0), (0, s.shape[1] - 1), (0, s.shape[1] // 2)],
-                              "1 x 2^31-1")
     assert int(q.view(torch.uint8)[0, n - 1]) == 0xFE
+    chk = FullOracleCheck(oracle_pool, 1, 128, "1 x 2^31-1 [1,128]")
+    chk.add("row", row, q, s)
+    chk.finish()
     del q, s
     # the same row in grouped calls: [1,4096] tiles from the kernel-argument
     # table (N + bn - 1 exceeds 2^31), then one scale for the whole row
@@ -1139,8 +1133,9 @@ def test_beyond_2_31_elements(gpu_lib):
     say("1 x 2^31-1 grouped [1,4096]")
     ((q, s),) = fq.quantize_many([row], (1, 4096))
     assert s.shape == (1, -(-n // 4096))
-    assert_tiles_match_oracle(row, q, s, 1, 4096, [(0, 0), (0, s.shape[1] - 1), (0, s.shape[1] // 2)],
-                              "grouped 1 x 2^31-1")
+    chk = FullOracleCheck(oracle_pool, 1, 4096, "grouped 1 x 2^31-1 [1,4096]")
+    chk.add("row", row, q, s)
+    chk.finish()
     del q, s
     s_ref, _ = oracle.blockwise.tile_scales_np(np.array([[7.0]]))
     for how in ("grouped", "single"):
@@ -1150,8 +1145,7 @@ def test_beyond_2_31_elements(gpu_lib):
         else:
             q, s = fq.quantize(row, (1, n))
         assert np.array_equal(scales_bits(s), scales_bits(s_ref.astype(np.float32))), how
-        for c0 in (0, n // 2 + 5, n - 4099):
-            q_ref, _ = oracle.quantize_with_amax(bits_np(row[:, c0:c0 + 4099].contiguous()), 1, n,
-                                                 np.array([[7.0]]), 0, c0)
-            assert np.array_equal(codes_np(q[:, c0:c0 + 4099].contiguous()), q_ref), (how, c0)
+        chk = FullOracleCheck(oracle_pool, 1, n, f"1 x 2^31-1 one scale, {how}")
+        chk.add("row", row, q, s)
+        chk.finish()
         del q, s

@@ -106,3 +106,65 @@ def test_full_check_streams_blocks_and_reports():
             chk.add(f"t{i}", x, bad_q if i == 5 else q, s)
         with pytest.raises(AssertionError, match=r"t5: 1 byte mismatches \(first \(row, col, got, want\) = \(499, 7"):
             chk.finish()
+
+
+@pytest.mark.parametrize("shape,block,arena", [((300, 520), (300, 520), 60_000),  # one tile, row chunks
+                                               ((1, 5000), (1, 5000), 12_000),    # one tile, column chunks
+                                               ((37, 700), (16, 300), 60_000),    # tiles larger than pieces
+                                               ((3, 4000), (1, 4000), 30_000)])   # one tile per row
+def test_two_pass_equals_whole_tensor_oracle(shape, block, arena):
+    """Tensors whose tiles exceed a piece go through the two passes (partial
+    maxima of pieces combined by max, then quantize with the full maxima):
+    equal to the oracle on the whole tensor, and planted wrong bytes and
+    scales are found and placed in the tensor's coordinates."""
+    import torch
+
+    from gpu_helpers import FullOracleCheck
+
+    rng = np.random.default_rng(sum(shape))
+    M, N = shape
+    bm, bn = block
+    bits = _bits(rng, M, N)
+    q_ref, s_ref = oracle.quantize(bits, bm, bn)
+    x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    with OraclePool(arena, workers=2, slab_values=700, arenas=2) as pool:
+        chk = FullOracleCheck(pool, bm, bn, "two-pass")
+        chk.TILE_ROW_VALUES = 600
+        assert chk.capacity < M * N           # several chunks as well
+        chk.add("t", x, torch.from_numpy(q_ref.copy()), torch.from_numpy(s_ref.copy()))
+        assert chk.finish() == (1, M * N)
+        bad_q = torch.from_numpy(q_ref.copy())
+        bad_q[M - 1, N - 3] ^= 0x01
+        bad_s = torch.from_numpy(s_ref.copy())
+        bad_s[-1, -1] = bad_s[-1, -1] * 2
+        chk = FullOracleCheck(pool, bm, bn, "two-pass")
+        chk.TILE_ROW_VALUES = 600
+        chk.add("t", x, bad_q, bad_s)
+        want = int(bad_q[M - 1, N - 3])
+        tm, tn = s_ref.shape
+        with pytest.raises(AssertionError, match=rf"t: 1 byte mismatches \(first \(row, col, got, want\) = "
+                                                 rf"\({M - 1}, {N - 3}, {want}, {int(q_ref[M - 1, N - 3])}\)\), "
+                                                 rf"1 scale mismatches \(first tile \({tm - 1}, {tn - 1}\)\)"):
+            chk.finish()
+
+
+def test_tensors_larger_than_a_block_are_cut_into_tile_rows():
+    """A tensor larger than one shared block is compared in chunks of whole
+    tile rows; a wrong byte in a later chunk is reported at its tensor row."""
+    import torch
+
+    from gpu_helpers import FullOracleCheck
+
+    rng = np.random.default_rng(9)
+    M, N, bm, bn = 700, 256, 64, 128
+    bits = _bits(rng, M, N)
+    q_ref, s_ref = oracle.quantize(bits, bm, bn)
+    x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    with OraclePool(120_000, workers=2, slab_values=5000, arenas=2) as pool:
+        chk = FullOracleCheck(pool, bm, bn, "chunks")
+        assert chk.capacity < M * N
+        q = torch.from_numpy(q_ref.copy())
+        q[650, 100] ^= 0x04
+        chk.add("big", x, q, torch.from_numpy(s_ref.copy()))
+        with pytest.raises(AssertionError, match=r"big: 1 byte mismatches \(first \(row, col, got, want\) = \(650, 100"):
+            chk.finish()
