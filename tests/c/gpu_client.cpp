@@ -5,9 +5,13 @@
 //      graph and replays it twice, refilling those outputs with a pattern
 //      before each replay (eagerly, outside the graph);
 //   3. dequantizes the result of step 1 to fp32 with fp8bq_dequantize, and
-//      both results again with one fp8bq_dequantize_many call.
-// It checks that both quantizations, and all three dequantizations, agree
-// byte for byte and writes
+//      both results again with one fp8bq_dequantize_many call;
+//   4. quantizes the first tile row of the input as 520 and then 515 entries
+//      of fp8bq_quantize_many_noalloc (more than 512: the library's own
+//      device table), each into outputs of its own.
+// It checks that the quantizations, and all three dequantizations, agree
+// byte for byte (every entry of step 4 with the first tile row of step 1)
+// and writes
 // <prefix>.q (uint8 [M, N]), <prefix>.s (fp32 [TM, TN]) and <prefix>.deq
 // (fp32 [M, N]) for the caller to compare with the CPU oracle.
 //
@@ -122,6 +126,39 @@ int main(int argc, char** argv) {
     return 4;
   }
 
+  // 4. the first tile row as many entries of the call that allocates nothing
+  const int64_t R = M < bm ? M : bm;
+  const size_t rn = static_cast<size_t>(R) * static_cast<size_t>(N);
+  const size_t rs = static_cast<size_t>((N + bn - 1) / bn);
+  const int kEntries = 520;
+  void* dq3 = nullptr;
+  float* ds3 = nullptr;
+  HIP_OK(hipMalloc(&dq3, kEntries * rn));
+  HIP_OK(hipMalloc(reinterpret_cast<void**>(&ds3), 4 * kEntries * rs));
+  std::vector<fp8bq_tensor> list(kEntries);
+  for (int i = 0; i < kEntries; ++i) {
+    list[i] = {dx, static_cast<uint8_t*>(dq3) + i * rn, ds3 + i * rs, R, N};
+  }
+  std::vector<uint8_t> q3(kEntries * rn);
+  std::vector<float> s3(kEntries * rs);
+  for (const int count : {kEntries, kEntries - 5}) {
+    HIP_OK(hipMemsetAsync(dq3, 0x5A, kEntries * rn, st));
+    HIP_OK(hipMemsetAsync(ds3, 0xFF, 4 * kEntries * rs, st));
+    FP8BQ_OK_(fp8bq_quantize_many_noalloc(list.data(), count, bm, bn, st));
+    HIP_OK(hipStreamSynchronize(st));
+    HIP_OK(hipMemcpy(q3.data(), dq3, kEntries * rn, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(s3.data(), ds3, 4 * kEntries * rs, hipMemcpyDeviceToHost));
+    for (int i = 0; i < count; ++i) {
+      if (std::memcmp(q3.data() + i * rn, q.data(), rn) != 0 ||
+          std::memcmp(s3.data() + i * rs, s.data(), 4 * rs) != 0) {
+        std::fprintf(stderr, "no-alloc entry %d of %d differs from the direct call\n", i, count);
+        return 6;
+      }
+    }
+  }
+  HIP_OK(hipFree(dq3));
+  HIP_OK(hipFree(ds3));
+
   const std::string prefix = argv[6];
   if (!write_file((prefix + ".q").c_str(), q.data(), n) ||
       !write_file((prefix + ".s").c_str(), s.data(), 4 * ns) ||
@@ -139,7 +176,7 @@ int main(int argc, char** argv) {
   HIP_OK(hipFree(ds2));
   HIP_OK(hipFree(ddeq));
   HIP_OK(hipFree(ddeq2));
-  std::printf("gpu client ok: %lldx%lld at [%d,%d], graph replays equal\n",
+  std::printf("gpu client ok: %lldx%lld at [%d,%d], graph replays and no-alloc entries equal\n",
               static_cast<long long>(M), static_cast<long long>(N), bm, bn);
   return 0;
 }
