@@ -276,15 +276,19 @@ def main():
     ap.add_argument("--workload", default="dense")
     ap.add_argument("--block", default=None, help="bm,bn for the ragged/vocab workloads")
     ap.add_argument("--op", default="quantize",
-                    choices=["quantize", "dequant-f32", "dequant-bf16", "stream", "shard"],
+                    choices=["quantize", "dequant-f32", "dequant-bf16", "stream", "shard",
+                             "shard-rows"],
                     help="quantize (default); time fp8bq_dequantize on the quantized workload; "
                          "time the streaming quant_weights loop over the workload in model "
-                         "order with norm weights passed through; or treat every tensor as a "
+                         "order with norm weights passed through; treat every tensor as a "
                          "shard at --phase and time fp8bq_tile_amax_many + "
-                         "fp8bq_quantize_amax_many per group")
+                         "fp8bq_quantize_amax_many per group; or treat every tensor as a row "
+                         "shard at the --phase row phase and time fp8bq_row_shards_begin + "
+                         "fp8bq_row_shards_finish per group")
     ap.add_argument("--phase", default=None,
-                    help="row,col tile phase of each shard for --op shard (default bm/2,0: "
-                         "row cuts in the middle of a tile row)")
+                    help="row,col tile phase of each shard for --op shard / shard-rows (default "
+                         "bm/2,0: row cuts in the middle of a tile row; shard-rows takes the row "
+                         "phase only)")
     ap.add_argument("--per-tensor", action="store_true",
                     help="also time one fp8bq_quantize call per tensor (HIP events per call)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -358,6 +362,9 @@ def main():
         return
     if args.op == "shard":
         time_shard(lib, keep, groups, bm, bn, args, stream, sptr, desc)
+        return
+    if args.op == "shard-rows":
+        time_row_shards(lib, keep, groups, bm, bn, args, sptr, desc)
         return
     if args.op != "quantize":
         time_dequant(lib, keep, groups, bm, bn, args, stream, sptr, desc)
@@ -547,6 +554,69 @@ def time_shard(lib, keep, groups, bm, bn, args, stream, sptr, desc):
                       "GBps_moved": round(gbs, 1), "pct_of_hbm_peak_moved": round(100 * gbs / HBM_PEAK_GBS, 2),
                       "GBps_algorithmic": round(alg, 1),
                       "pct_of_hbm_peak_algorithmic": round(100 * alg / HBM_PEAK_GBS, 2)}), flush=True)
+
+
+def time_row_shards(lib, keep, groups, bm, bn, args, sptr, desc):
+    """Every tensor as a row shard (whole rows) at a tile-row phase: per
+    group of the workload, fp8bq_row_shards_begin (the edge rows' partial
+    maxima, then the whole tile rows between them in one pass; the exchange
+    between shards would follow) and fp8bq_row_shards_finish (the edge rows
+    with their maxima).  Reports GB/s of the quantizer's algorithmic bytes
+    and of the bytes the calls move (edge rows read twice)."""
+    import torch
+
+    import fp8_blockwise_weight_amd as fq
+
+    rp = int(args.phase.split(",")[0]) if args.phase else bm // 2
+    tables = []
+    hold = []
+    moved = algorithmic = 0
+    for (xs, outs), specs in zip(keep, groups):
+        arr = (fq.RowShardEntry * len(xs))()
+        for e, x, (q, _), sp in zip(arr, xs, outs, specs):
+            tm, tn = fq.local_grid(sp.M, sp.N, bm, bn, (rp, 0))
+            s = torch.empty((tm, tn), dtype=torch.float32, device=x.device)
+            hold.append(s)
+            top, bottom = fq.row_shard_edges(sp.M, bm, rp)
+            e.x, e.q, e.scale_inv, e.M, e.N, e.row_phase = x.data_ptr(), q.data_ptr(), s.data_ptr(), sp.M, sp.N, rp
+            e.top_amax = s[0].data_ptr() if top else None
+            e.bottom_amax = s[tm - 1].data_ptr() if bottom else None
+            edge = (top + bottom) * sp.N
+            moved += 3 * sp.M * sp.N + 2 * edge + 4 * tm * tn + 8 * ((top > 0) + (bottom > 0)) * tn
+            algorithmic += 3 * sp.M * sp.N + 4 * tm * tn
+        need = int(lib.fp8bq_many_workspace_bytes(len(xs)))
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=keep[0][0][0].device)
+        hold.append(ws)
+        tables.append((arr, len(xs), ws, need))
+
+    def step():
+        for arr, n, ws, need in tables:
+            st = lib.fp8bq_row_shards_begin(arr, n, bm, bn, ws.data_ptr(), need, None, sptr)
+            if st == 0:
+                st = lib.fp8bq_row_shards_finish(arr, n, bm, bn, sptr)
+            if st != 0:
+                raise RuntimeError(f"row-shard path failed: {st}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - w0) * 1e3 / args.steps
+    gbs = moved / (ms * 1e-3) / 1e9
+    alg = algorithmic / (ms * 1e-3) / 1e9
+    log(f"row shards at row phase {rp}: {2 * len(tables)} calls/step, wall {ms:.3f} ms/step; "
+        f"{alg:.1f} GB/s algorithmic = {100 * alg / HBM_PEAK_GBS:.1f}% of peak, "
+        f"{gbs:.1f} GB/s moved = {100 * gbs / HBM_PEAK_GBS:.1f}%")
+    print(json.dumps({"op": "shard-rows", "workload": desc, "row_phase": rp,
+                      "calls_per_step": 2 * len(tables), "bytes_moved_per_step": moved,
+                      "algorithmic_bytes_per_step": algorithmic, "ms_per_step": round(ms, 4),
+                      "GBps_algorithmic": round(alg, 1),
+                      "pct_of_hbm_peak_algorithmic": round(100 * alg / HBM_PEAK_GBS, 2),
+                      "GBps_moved": round(gbs, 1),
+                      "pct_of_hbm_peak_moved": round(100 * gbs / HBM_PEAK_GBS, 2)}), flush=True)
 
 
 def time_stream(keep, groups, bm, bn, args, desc):

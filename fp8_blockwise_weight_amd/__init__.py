@@ -44,6 +44,9 @@ EXPORTS = (
     "fp8bq_quantize_amax",
     "fp8bq_tile_amax_many",
     "fp8bq_quantize_amax_many",
+    "fp8bq_row_shard_edges",
+    "fp8bq_row_shards_begin",
+    "fp8bq_row_shards_finish",
     "fp8bq_set_resident_wait_us",
     "fp8bq_status_string",
     "fp8bq_last_hip_error",
@@ -91,6 +94,22 @@ class ShardEntry(ctypes.Structure):
     ]
 
 
+class RowShardEntry(ctypes.Structure):
+    """``fp8bq_row_shard`` of include/fp8bq.h (64 bytes, no padding)."""
+
+    _fields_ = [
+        ("x", ctypes.c_void_p),
+        ("q", ctypes.c_void_p),
+        ("scale_inv", ctypes.c_void_p),
+        ("top_amax", ctypes.c_void_p),
+        ("bottom_amax", ctypes.c_void_p),
+        ("M", ctypes.c_int64),
+        ("N", ctypes.c_int64),
+        ("row_phase", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -126,6 +145,14 @@ def load_library() -> ctypes.CDLL:
     for name in ("fp8bq_tile_amax_many", "fp8bq_quantize_amax_many"):
         getattr(lib, name).argtypes = [ctypes.POINTER(ShardEntry), c_i32, c_i32, c_i32, c_vp]
         getattr(lib, name).restype = ctypes.c_int
+    lib.fp8bq_row_shard_edges.argtypes = [c_i64, c_i32, c_i32, ctypes.POINTER(c_i64),
+                                          ctypes.POINTER(c_i64)]
+    lib.fp8bq_row_shard_edges.restype = ctypes.c_int
+    lib.fp8bq_row_shards_begin.argtypes = [ctypes.POINTER(RowShardEntry), c_i32, c_i32, c_i32, c_vp,
+                                           ctypes.c_size_t, c_vp, c_vp]
+    lib.fp8bq_row_shards_begin.restype = ctypes.c_int
+    lib.fp8bq_row_shards_finish.argtypes = [ctypes.POINTER(RowShardEntry), c_i32, c_i32, c_i32, c_vp]
+    lib.fp8bq_row_shards_finish.restype = ctypes.c_int
     lib.fp8bq_encode_e4m3.argtypes = [c_vp, c_vp, c_i64, c_vp]
     lib.fp8bq_encode_e4m3.restype = ctypes.c_int
     lib.fp8bq_set_resident_wait_us.argtypes = [c_i64]
@@ -604,6 +631,110 @@ def quantize_with_amax_many(xs: Sequence, amaxs: Sequence, block_size=(128, 128)
         _check("fp8bq_quantize_amax_many",
                load_library().fp8bq_quantize_amax_many(arr, len(xs), bm, bn, _stream(dev)))
     return list(zip(qs, scales))
+
+
+def row_shard_edges(M: int, bm: int, row_phase: int) -> Tuple[int, int]:
+    """(top, bottom): how many of a row shard's first and last rows lie in
+    tile rows that shards above and below may hold too
+    (``fp8bq_row_shard_edges``); the rows between are whole tile rows."""
+    top, bottom = ctypes.c_int64(), ctypes.c_int64()
+    _check("fp8bq_row_shard_edges",
+           load_library().fp8bq_row_shard_edges(int(M), int(bm), int(row_phase), ctypes.byref(top),
+                                                ctypes.byref(bottom)))
+    return top.value, bottom.value
+
+
+class RowShards:
+    """One quantize-before-gather of row shards in flight, between
+    ``row_shards_begin`` and ``row_shards_finish``.
+
+    ``outputs`` holds (q, scale_inv) per shard.  ``edges`` holds, per shard,
+    (top, bottom): the fp32 [TN] maxima of the tile rows its first and last
+    rows share with other shards, or None where it has no such rows.  They
+    are the first and last rows of its ``scale_inv``, which the finishing
+    call converts to scales in place; between the two calls they hold the
+    shard's partial maxima, for the caller's exchange to replace with the
+    full ones."""
+
+    def __init__(self, table, outputs, edges, bm, bn, device, keep):
+        self.table, self.outputs, self.edges = table, outputs, edges
+        self.bm, self.bn, self.device, self._keep = bm, bn, device, keep
+
+
+def row_shards_begin(xs: Sequence, block_size=(128, 128), row_phases=None, maxima_event=None,
+                     workspace=None) -> RowShards:
+    """Partial maxima of the shards' edge rows, then the whole tile rows
+    between them quantized in one pass (``fp8bq_row_shards_begin``).  Each
+    shard is a BF16 [M, N] GPU tensor of whole rows whose first row sits at
+    ``row_phases[i]`` inside a tile row (default 0).  ``maxima_event``
+    (a ``torch.cuda.Event``) is recorded on the current stream once the
+    maxima are enqueued.  An empty shard gets a [0, TN] scale_inv."""
+    import torch
+
+    bm, bn = block_shape(block_size)
+    xs = list(xs)
+    phases = [int(p) for p in (row_phases if row_phases is not None else [0] * len(xs))]
+    if len(phases) != len(xs):
+        raise ValueError("row_phases must hold one row phase per shard")
+    dev = xs[0].device if xs else None
+    table = (RowShardEntry * len(xs))()
+    outputs, edges = [], []
+    for e, x, rp in zip(table, xs, phases):
+        _check_input(x)
+        if x.device != dev:
+            raise ValueError("all shards of one call must be on the same device")
+        M, N = x.shape
+        TMl, TN = local_grid(M, N, bm, bn, (rp, 0)) if M else (0, -(-N // bn))
+        top, bottom = row_shard_edges(M, bm, rp)
+        q = torch.empty((M, N), dtype=torch.float8_e4m3fn, device=dev)
+        s = torch.empty((TMl, TN), dtype=torch.float32, device=dev)
+        ta = s[0] if top and N else None
+        ba = s[TMl - 1] if bottom and N else None
+        e.x, e.q, e.scale_inv, e.M, e.N, e.row_phase = x.data_ptr(), q.data_ptr(), s.data_ptr(), M, N, rp
+        e.top_amax = ta.data_ptr() if ta is not None else None
+        e.bottom_amax = ba.data_ptr() if ba is not None else None
+        outputs.append((q, s))
+        edges.append((ta, ba))
+    if not xs:
+        return RowShards(table, [], [], bm, bn, dev, ())
+    lib = load_library()
+    need = int(lib.fp8bq_many_workspace_bytes(len(xs)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    with torch.cuda.device(dev):
+        ev = maxima_event.cuda_event if maxima_event is not None else None
+        if maxima_event is not None and ev == 0:   # torch creates its event on first record
+            maxima_event.record()
+            ev = maxima_event.cuda_event
+        _check("fp8bq_row_shards_begin",
+               lib.fp8bq_row_shards_begin(table, len(xs), bm, bn, ws_ptr, ws_bytes, ev, _stream(dev)))
+    return RowShards(table, outputs, edges, bm, bn, dev, (xs, workspace))
+
+
+def row_shards_finish(state: RowShards) -> List:
+    """The edge rows quantized with the maxima now in ``state.edges``
+    (``fp8bq_row_shards_finish``).  Returns (q, scale_inv) per shard."""
+    import torch
+
+    if state.outputs:
+        with torch.cuda.device(state.device):
+            _check("fp8bq_row_shards_finish",
+                   load_library().fp8bq_row_shards_finish(state.table, len(state.outputs), state.bm,
+                                                          state.bn, _stream(state.device)))
+    return state.outputs
+
+
+def quantize_row_shards(xs: Sequence, block_size=(128, 128), row_phases=None, exchange=None) -> List:
+    """Quantize-before-gather of row shards: ``row_shards_begin``, then
+    ``exchange(edges)`` (which replaces, in place, each edge's maxima by the
+    max over the shards sharing that tile row; default: nothing, each shard
+    alone), then ``row_shards_finish``.  Returns (q, scale_inv) per shard."""
+    state = row_shards_begin(xs, block_size, row_phases)
+    if exchange is not None:
+        exchange(state.edges)
+    return row_shards_finish(state)
 
 
 def set_resident_wait_us(microseconds: int) -> None:

@@ -1169,6 +1169,100 @@ int quantize_many_impl(const fp8bq_tensor* list, int32_t count, int32_t bm, int3
   return e == hipSuccess ? FP8BQ_OK : hip_failed(e);
 }
 
+// Rows of a row shard: the first `top` rows share a tile row with the
+// shards above, the last `bottom` rows one with the shards below; the rows
+// between are whole tile rows of this shard alone.
+struct RowParts {
+  int64_t top = 0;
+  int64_t bottom = 0;
+  int64_t TMl = 0;  // local tile rows
+  int64_t TN = 0;   // tile columns
+};
+
+int row_parts(int64_t M, int32_t bm, int32_t row_phase, RowParts* p) {
+  if (M < 0 || M > INT32_MAX || bm < 1 || row_phase < 0 || row_phase >= bm) {
+    return FP8BQ_ERR_INVALID_ARGUMENT;
+  }
+  p->top = std::min<int64_t>(M, (bm - row_phase) % bm);
+  p->bottom = (M - p->top) % bm;
+  p->TMl = ceil_div(row_phase + M, bm);
+  return FP8BQ_OK;
+}
+
+// Checks one row-shard entry as a whole: ranges, pointers, alignment and
+// the overlaps of x, q, scale_inv and the two edge maxima (each edge's
+// maxima may be its own scale row, converted in place).  Fills *p.
+int check_row_shard(const fp8bq_row_shard& r, int32_t bm, int32_t bn, RowParts* p) {
+  int st = row_parts(r.M, bm, r.row_phase, p);
+  if (st != FP8BQ_OK || r.N < 0 || r.N > INT32_MAX || bn < 1) return FP8BQ_ERR_INVALID_ARGUMENT;
+  p->TN = ceil_div(r.N, bn);
+  if (r.M == 0 || r.N == 0) return FP8BQ_OK;
+  if (r.x == nullptr || r.q == nullptr || r.scale_inv == nullptr) return FP8BQ_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(r.x) & 1) != 0 || (reinterpret_cast<uintptr_t>(r.scale_inv) & 3) != 0) {
+    return FP8BQ_ERR_INVALID_ARGUMENT;
+  }
+  const uint64_t n = static_cast<uint64_t>(r.M) * static_cast<uint64_t>(r.N);
+  const uint64_t ns = 4 * static_cast<uint64_t>(p->TMl) * static_cast<uint64_t>(p->TN);
+  const uint64_t na = 4 * static_cast<uint64_t>(p->TN);
+  if (overlap(r.x, 2 * n, r.q, n) || overlap(r.x, 2 * n, r.scale_inv, ns) || overlap(r.q, n, r.scale_inv, ns)) {
+    return FP8BQ_ERR_INVALID_ARGUMENT;
+  }
+  const float* rows[2] = {r.scale_inv, r.scale_inv + (p->TMl - 1) * p->TN};  // first, last scale row
+  const float* am[2] = {r.top_amax, r.bottom_amax};
+  const bool used[2] = {p->top > 0, p->bottom > 0};
+  for (int k = 0; k < 2; ++k) {
+    if (!used[k]) continue;
+    if (am[k] == nullptr || (reinterpret_cast<uintptr_t>(am[k]) & 3) != 0) return FP8BQ_ERR_INVALID_ARGUMENT;
+    if (overlap(am[k], na, r.x, 2 * n) || overlap(am[k], na, r.q, n) ||
+        (am[k] != rows[k] && overlap(am[k], na, r.scale_inv, ns))) {
+      return FP8BQ_ERR_INVALID_ARGUMENT;
+    }
+  }
+  if (used[0] && used[1] && overlap(am[0], na, am[1], na)) return FP8BQ_ERR_INVALID_ARGUMENT;
+  return FP8BQ_OK;
+}
+
+// Host lists of a row-shard call, reused per thread.
+thread_local std::vector<fp8bq_shard> g_row_edges;
+thread_local std::vector<fp8bq_tensor> g_row_inner;
+
+// The edge slabs of every entry as shard entries: pass 0 writes their
+// partial maxima to top_amax / bottom_amax, pass 1 quantizes them with
+// those maxima into their q rows and first / last scale row.
+void row_edges(const fp8bq_row_shard* list, int32_t count, int32_t bm, int32_t bn, int pass) {
+  g_row_edges.clear();
+  for (int32_t i = 0; i < count; ++i) {
+    const fp8bq_row_shard& r = list[i];
+    RowParts p;
+    (void)check_row_shard(r, bm, bn, &p);  // already checked: fills p
+    if (r.M == 0 || r.N == 0) continue;
+    const bool quant = pass == 1;
+    if (p.top > 0) {
+      g_row_edges.push_back(fp8bq_shard{r.x, quant ? r.q : nullptr, r.top_amax,
+                                        quant ? r.scale_inv : nullptr, p.top, r.N, r.row_phase, 0});
+    }
+    if (p.bottom > 0) {
+      const int64_t r0 = r.M - p.bottom;
+      g_row_edges.push_back(fp8bq_shard{
+          static_cast<const uint16_t*>(r.x) + r0 * r.N,
+          quant ? static_cast<void*>(static_cast<uint8_t*>(r.q) + r0 * r.N) : nullptr, r.bottom_amax,
+          quant ? r.scale_inv + (p.TMl - 1) * p.TN : nullptr, p.bottom, r.N, 0, 0});
+    }
+  }
+}
+
+// The edge slabs through the grouped shard calls, in lists of at most
+// INT32_MAX entries.
+int run_row_edges(int32_t bm, int32_t bn, void* stream, int pass) {
+  const size_t n = g_row_edges.size();
+  for (size_t i = 0; i < n; i += INT32_MAX) {
+    const int32_t c = static_cast<int32_t>(std::min<size_t>(n - i, INT32_MAX));
+    const int st = shard_many(g_row_edges.data() + i, c, bm, bn, stream, pass);
+    if (st != FP8BQ_OK) return st;
+  }
+  return FP8BQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1221,6 +1315,66 @@ int fp8bq_tile_amax_many(const fp8bq_shard* list, int32_t count, int32_t bm, int
 int fp8bq_quantize_amax_many(const fp8bq_shard* list, int32_t count, int32_t bm, int32_t bn,
                              void* stream) {
   return shard_many(list, count, bm, bn, stream, 1);
+}
+
+int fp8bq_row_shard_edges(int64_t M, int32_t bm, int32_t row_phase, int64_t* top, int64_t* bottom) {
+  RowParts p;
+  if (top == nullptr || bottom == nullptr) return FP8BQ_ERR_INVALID_ARGUMENT;
+  const int st = row_parts(M, bm, row_phase, &p);
+  if (st != FP8BQ_OK) return st;
+  *top = p.top;
+  *bottom = p.bottom;
+  return FP8BQ_OK;
+}
+
+int fp8bq_row_shards_begin(const fp8bq_row_shard* list, int32_t count, int32_t bm, int32_t bn,
+                           void* workspace, size_t workspace_bytes, void* maxima_event,
+                           void* stream) {
+  if (count < 0 || bm < 1 || bn < 1) return FP8BQ_ERR_INVALID_ARGUMENT;
+  if (count > 0 && list == nullptr) return FP8BQ_ERR_INVALID_ARGUMENT;
+  g_row_inner.clear();
+  for (int32_t i = 0; i < count; ++i) {
+    const fp8bq_row_shard& r = list[i];
+    RowParts p;
+    const int st = check_row_shard(r, bm, bn, &p);
+    if (st != FP8BQ_OK) return st;
+    const int64_t inner = r.M - p.top - p.bottom;
+    if (r.N == 0 || inner == 0) continue;
+    g_row_inner.push_back(fp8bq_tensor{static_cast<const uint16_t*>(r.x) + p.top * r.N,
+                                       static_cast<uint8_t*>(r.q) + p.top * r.N,
+                                       r.scale_inv + (p.top > 0 ? p.TN : 0), inner, r.N});
+  }
+  const int32_t n_inner = static_cast<int32_t>(g_row_inner.size());
+  const size_t need = fp8bq_many_workspace_bytes(n_inner);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need ||
+                   (reinterpret_cast<uintptr_t>(workspace) & 15) != 0)) {
+    return FP8BQ_ERR_WORKSPACE;
+  }
+  // 1. partial maxima of the edge rows, then the event the exchange waits for
+  row_edges(list, count, bm, bn, 0);
+  int st = run_row_edges(bm, bn, stream, 0);
+  if (st != FP8BQ_OK) return st;
+  if (maxima_event != nullptr) {
+    const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(maxima_event), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_failed(e);
+  }
+  // 2. the whole tile rows between the edges, in one pass
+  if (n_inner == 0) return FP8BQ_OK;
+  return quantize_many_impl(g_row_inner.data(), n_inner, bm, bn, static_cast<unsigned char*>(workspace),
+                            stream);
+}
+
+int fp8bq_row_shards_finish(const fp8bq_row_shard* list, int32_t count, int32_t bm, int32_t bn,
+                            void* stream) {
+  if (count < 0 || bm < 1 || bn < 1) return FP8BQ_ERR_INVALID_ARGUMENT;
+  if (count > 0 && list == nullptr) return FP8BQ_ERR_INVALID_ARGUMENT;
+  for (int32_t i = 0; i < count; ++i) {
+    RowParts p;
+    const int st = check_row_shard(list[i], bm, bn, &p);
+    if (st != FP8BQ_OK) return st;
+  }
+  row_edges(list, count, bm, bn, 1);
+  return run_row_edges(bm, bn, stream, 1);
 }
 
 int fp8bq_encode_e4m3(const float* y, void* q, int64_t n, void* stream) {

@@ -240,6 +240,73 @@ int fp8bq_tile_amax_many(const fp8bq_shard* list, int32_t count, int32_t bm, int
 int fp8bq_quantize_amax_many(const fp8bq_shard* list, int32_t count, int32_t bm, int32_t bn,
                              void* stream);
 
+/*
+ * Row shards, with the exchange confined to the tile rows that shards share.
+ * A row shard holds whole rows of a matrix (the full width N, column phase
+ * 0), its first row at row_phase inside a tile row: the weights split
+ * across ranks by rows before the gather (the sharding discussion of the
+ * page "Using FP8 inference in long response vllm rollouts").  Only its
+ * first `top` and last `bottom` rows (fp8bq_row_shard_edges) lie in tile
+ * rows that other shards may hold too; the tile rows between them are whole
+ * and need no exchange.  The quantize-before-gather of such shards runs as
+ *   1. fp8bq_row_shards_begin: the partial maxima of each shard's edge rows
+ *      (top_amax, bottom_amax; the tile maxima of fp8bq_tile_amax), then
+ *      the whole tile rows between them quantized in one pass (their q rows
+ *      and scale rows, as fp8bq_quantize_many);
+ *   2. the caller's exchange: each edge's maxima replaced, element by
+ *      element, by the max over every shard that holds part of that tile
+ *      row (left as they are where no other shard does).  It may run on
+ *      another stream once `maxima_event` has completed, beside the
+ *      whole-tile-row work of step 1;
+ *   3. fp8bq_row_shards_finish: the edge rows quantized with those maxima
+ *      (their q rows and the first / last scale row, as
+ *      fp8bq_quantize_amax), on a stream ordered after the exchange.
+ * Every byte and scale then equals quantizing the whole matrix.  Whole tile
+ * rows are read once and edge rows twice, where fp8bq_tile_amax_many and
+ * fp8bq_quantize_amax_many read every row twice.
+ */
+typedef struct fp8bq_row_shard {
+  const void* x;       /* BF16 [M, N] row-major */
+  void* q;             /* e4m3fn [M, N] */
+  float* scale_inv;    /* fp32 [TMl, TN]: TMl = ceil((row_phase + M) / bm), TN = ceil(N / bn) */
+  float* top_amax;     /* fp32 [TN], the tile row of the first `top` rows (unused when
+                          top == 0); may be scale_inv's first row, converted in place */
+  float* bottom_amax;  /* fp32 [TN], the tile row of the last `bottom` rows (unused when
+                          bottom == 0); may be scale_inv's last row */
+  int64_t M;
+  int64_t N;
+  int32_t row_phase;   /* 0 <= row_phase < bm */
+  int32_t reserved;    /* ignored */
+} fp8bq_row_shard;
+
+/* The edge rows of a row shard of M rows at row_phase:
+ * *top = min(M, (bm - row_phase) % bm) rows at its start and
+ * *bottom = (M - *top) % bm rows at its end.  Host arithmetic only; returns
+ * FP8BQ_ERR_INVALID_ARGUMENT unless 0 <= M <= INT32_MAX, bm >= 1 and
+ * 0 <= row_phase < bm. */
+int fp8bq_row_shard_edges(int64_t M, int32_t bm, int32_t row_phase, int64_t* top, int64_t* bottom);
+
+/*
+ *   list          HOST array of `count` entries, read before the call returns
+ *   count         number of entries (>= 0); entries with M == 0 or N == 0 are skipped
+ *   bm, bn        block size shared by every entry
+ *   workspace     device memory for the table of the shards' whole-tile parts, as
+ *   workspace_bytes  in fp8bq_quantize_many: fp8bq_many_workspace_bytes(count)
+ *                 bytes are always enough (NULL / 0 for count <= FP8BQ_MANY_ARGS_MAX)
+ *   maxima_event  hipEvent_t recorded on `stream` after the edge maxima, before the
+ *                 whole-tile-row launches (NULL: none)
+ *   stream        hipStream_t (NULL = null stream)
+ * Every entry is checked before anything is enqueued: ranges, null pointers,
+ * alignment (x 2-byte, scale_inv and the maxima 4-byte), and the overlaps of
+ * x, q, scale_inv, top_amax and bottom_amax within the entry (not across
+ * entries).  Returns an fp8bq_status.
+ */
+int fp8bq_row_shards_begin(const fp8bq_row_shard* list, int32_t count, int32_t bm, int32_t bn,
+                           void* workspace, size_t workspace_bytes, void* maxima_event,
+                           void* stream);
+int fp8bq_row_shards_finish(const fp8bq_row_shard* list, int32_t count, int32_t bm, int32_t bn,
+                            void* stream);
+
 /* Output element type of fp8bq_dequantize. */
 enum fp8bq_out_dtype {
   FP8BQ_OUT_F32 = 0,  /* float32 */

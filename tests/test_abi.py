@@ -192,6 +192,82 @@ def test_shard_many_rejects(lib):
                 assert f(_shards(good + [bad]), 2, 128, 128, None) == INVALID, bad
 
 
+def _rows(rows):
+    arr = (fq.RowShardEntry * len(rows))()
+    for e, (x, q, sc, ta, ba, M, N, rp) in zip(arr, rows):
+        e.x, e.q, e.scale_inv, e.top_amax, e.bottom_amax, e.M, e.N, e.row_phase = x, q, sc, ta, ba, M, N, rp
+    return arr
+
+
+def test_row_shard_entry_layout_matches_header():
+    # fp8bq_row_shard: five pointers, two int64, two int32 -> 64 bytes on LP64
+    assert ctypes.sizeof(fq.RowShardEntry) == 64
+
+
+def test_row_shards_reject(lib):
+    """Both row-shard calls check every entry as a whole before anything is
+    enqueued: ranges, null pointers, alignment, overlaps within an entry
+    (an edge's maxima may be its own scale row), and the workspace of the
+    whole-tile parts."""
+    # 300 x 256 rows at row phase 64 of [128,128]: 64 top rows, 108 bottom
+    # rows, 3 local tile rows x 2 tile columns; maxima in their scale rows
+    first, last = S, S + 4 * 2 * 2
+    good = (X, Q, S, first, last, 300, 256, 64)
+    A = S + 0x100000
+    begin = lambda arr, n, bm=128, bn=128, ws=None, wsb=0: lib.fp8bq_row_shards_begin(
+        arr, n, bm, bn, ws, wsb, None, None)
+    finish = lambda arr, n, bm=128, bn=128: lib.fp8bq_row_shards_finish(arr, n, bm, bn, None)
+    for f in (begin, finish):
+        assert f(_rows([good]), -1) == INVALID                          # count < 0
+        assert f(None, 1) == INVALID                                     # null list
+        assert f(_rows([good]), 1, bm=0) == INVALID                      # bm < 1
+        assert f(_rows([good]), 1, bn=0) == INVALID                      # bn < 1
+        assert f(None, 0) == fq.OK
+        for bad in [(X, Q, S, first, last, -1, 256, 64),                 # negative M
+                    (X, Q, S, first, last, 300, 1 << 31, 64),            # N beyond 32 bits
+                    (X, Q, S, first, last, 300, 256, 128),               # row phase >= bm
+                    (X, Q, S, first, last, 300, 256, -1),                # negative row phase
+                    (None, Q, S, first, last, 300, 256, 64),             # null x
+                    (X, None, S, first, last, 300, 256, 64),             # null q
+                    (X, Q, None, first, last, 300, 256, 64),             # null scale_inv
+                    (X + 1, Q, S, first, last, 300, 256, 64),            # x not 2-byte aligned
+                    (X, Q, S + 2, first, last, 300, 256, 64),            # scale_inv not 4-byte aligned
+                    (X, Q, S, None, last, 300, 256, 64),                 # top rows, no top maxima
+                    (X, Q, S, first, None, 300, 256, 64),                # bottom rows, no bottom maxima
+                    (X, Q, S, A + 2, last, 300, 256, 64),                # maxima not 4-byte aligned
+                    (X, X + 64, S, first, last, 300, 256, 64),           # q overlaps x
+                    (X, Q, X + 8, first, last, 300, 256, 64),            # scale_inv overlaps x
+                    (X, Q, S, Q + 16, last, 300, 256, 64),               # top maxima overlap q
+                    (X, Q, S, X, last, 300, 256, 64),                    # top maxima overlap x
+                    (X, Q, S, S + 4, last, 300, 256, 64),                # inside scale_inv, not its row
+                    (X, Q, S, first, first, 300, 256, 64),               # bottom maxima in the first row
+                    (X, Q, S, A, A + 4, 300, 256, 64)]:                  # the two maxima overlap
+            assert f(_rows([good, bad]), 2) == INVALID, bad
+    # maxima beside scale_inv, and a shard with no edges (phase 0, whole tile
+    # rows): no maxima needed -- still refused here only through the workspace
+    many = _rows([good] * 600)
+    assert begin(many, 600) == WORKSPACE                                 # > 512 whole-tile parts
+    need = lib.fp8bq_many_workspace_bytes(600)
+    assert begin(many, 600, ws=W, wsb=need - 1) == WORKSPACE
+    assert begin(many, 600, ws=W + 8, wsb=need) == WORKSPACE             # not 16-byte aligned
+    # entries with M == 0 or N == 0 (any maxima) and lists of them need no device
+    empty = _rows([(None, None, None, None, None, 0, 256, 5), (None, None, None, None, None, 300, 0, 7)])
+    assert begin(empty, 2) == fq.OK
+    assert finish(empty, 2) == fq.OK
+
+
+def test_row_shard_edges_rejects(lib):
+    t, b = ctypes.c_int64(), ctypes.c_int64()
+    f = lib.fp8bq_row_shard_edges
+    assert f(10, 128, 0, ctypes.byref(t), ctypes.byref(b)) == fq.OK
+    assert f(-1, 128, 0, ctypes.byref(t), ctypes.byref(b)) == INVALID
+    assert f(1 << 31, 128, 0, ctypes.byref(t), ctypes.byref(b)) == INVALID
+    assert f(10, 0, 0, ctypes.byref(t), ctypes.byref(b)) == INVALID
+    assert f(10, 128, 128, ctypes.byref(t), ctypes.byref(b)) == INVALID
+    assert f(10, 128, -1, ctypes.byref(t), ctypes.byref(b)) == INVALID
+    assert f(10, 128, 0, None, ctypes.byref(b)) == INVALID
+
+
 def test_shard_many_empty_is_ok_without_device(lib):
     empty = _shards([(None, None, None, None, 0, 8, 0, 0), (None, None, None, None, 8, 0, 0, 0)])
     assert lib.fp8bq_tile_amax_many(empty, 2, 128, 128, None) == fq.OK

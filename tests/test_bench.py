@@ -80,6 +80,31 @@ def test_bench_shard_mode(gpu_lib):
     assert 0 < rec["pct_of_hbm_peak_moved"] < 100
 
 
+@pytest.mark.gpu
+def test_bench_row_shard_mode(gpu_lib):
+    """--op shard-rows on one dense layer: every tensor as a row shard at row
+    phase 64 through fp8bq_row_shards_begin / _finish; the record's byte
+    counts follow the edge-rows formula."""
+    print("bench.py --workload dense-layer --op shard-rows --phase 64", flush=True)
+    res = subprocess.run([sys.executable, BENCH, "--workload", "dense-layer", "--op", "shard-rows",
+                          "--phase", "64", "--steps", "2", "--warmup", "1", "--no-cpu-baseline"],
+                         capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert res.returncode == 0, res.stderr[-2000:]
+    rec = json.loads(res.stdout.strip().splitlines()[-1])
+    assert rec["op"] == "shard-rows" and rec["row_phase"] == 64 and rec["calls_per_step"] == 2
+    sys.path.insert(0, ROOT)
+    from fp8_blockwise_weight_amd import workloads as wl
+
+    moved = alg = 0
+    for sp in wl.c2():
+        tm, tn = -(-(64 + sp.M) // 128), -(-sp.N // 128)
+        edge = 64 + (sp.M - 64) % 128                      # 64 top rows, the rest of the last tile row
+        moved += 3 * sp.M * sp.N + 2 * edge * sp.N + 4 * tm * tn + 16 * tn
+        alg += 3 * sp.M * sp.N + 4 * tm * tn
+    assert rec["bytes_moved_per_step"] == moved and rec["algorithmic_bytes_per_step"] == alg
+    assert 0 < rec["pct_of_hbm_peak_algorithmic"] < 100
+
+
 def test_kernel_fingerprint_ignores_comments_only():
     """The counter record is tied to the kernels' code: comment and layout
     edits keep the fingerprint, code edits change it."""
