@@ -8,16 +8,22 @@
 //      both results again with one fp8bq_dequantize_many call;
 //   4. quantizes the first tile row of the input as 520 and then 515 entries
 //      of fp8bq_quantize_many_noalloc (more than 512: the library's own
-//      device table), each into outputs of its own.
+//      device table), each into outputs of its own;
+//   5. quantizes the input as two row shards cut at row M/2 + 1 (inside a
+//      tile row unless that row is a multiple of bm): fp8bq_row_shards_begin
+//      records an event after the edge rows' maxima, a second stream waits
+//      for it and exchanges the shared tile row's maxima (through the host),
+//      and fp8bq_row_shards_finish runs once that stream is done.
 // It checks that the quantizations, and all three dequantizations, agree
-// byte for byte (every entry of step 4 with the first tile row of step 1)
-// and writes
+// byte for byte (every entry of step 4 with the first tile row of step 1,
+// the shards of step 5 with the rows and scale rows of step 1) and writes
 // <prefix>.q (uint8 [M, N]), <prefix>.s (fp32 [TM, TN]) and <prefix>.deq
 // (fp32 [M, N]) for the caller to compare with the CPU oracle.
 //
 // usage: gpu_client <in.bf16> M N bm bn <prefix>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -159,6 +165,68 @@ int main(int argc, char** argv) {
   HIP_OK(hipFree(dq3));
   HIP_OK(hipFree(ds3));
 
+  // 5. two row shards, the exchange of their shared tile row on a second stream
+  const int64_t cut = M / 2 + 1 < M ? M / 2 + 1 : M;
+  const int64_t TN = (N + bn - 1) / bn;
+  const int64_t r0s[2] = {0, cut};
+  int64_t tml[2], tops[2], bots[2];
+  fp8bq_row_shard rsh[2];
+  void* dq5 = nullptr;
+  float* ds5[2] = {nullptr, nullptr};
+  HIP_OK(hipMalloc(&dq5, n));
+  for (int k = 0; k < 2; ++k) {
+    const int64_t rows = k == 0 ? cut : M - cut;
+    const int32_t rp = static_cast<int32_t>(r0s[k] % bm);
+    FP8BQ_OK_(fp8bq_row_shard_edges(rows, bm, rp, &tops[k], &bots[k]));
+    tml[k] = rows == 0 ? 0 : (rp + rows + bm - 1) / bm;
+    HIP_OK(hipMalloc(reinterpret_cast<void**>(&ds5[k]), 4 * static_cast<size_t>(std::max<int64_t>(tml[k], 1) * TN)));
+    rsh[k] = {static_cast<const uint16_t*>(dx) + r0s[k] * N, static_cast<uint8_t*>(dq5) + r0s[k] * N,
+              ds5[k], tops[k] > 0 ? ds5[k] : nullptr, bots[k] > 0 ? ds5[k] + (tml[k] - 1) * TN : nullptr,
+              rows, N, rp, 0};
+  }
+  hipStream_t side;
+  hipEvent_t maxima, exchanged;
+  HIP_OK(hipStreamCreate(&side));
+  HIP_OK(hipEventCreateWithFlags(&maxima, hipEventDisableTiming));
+  HIP_OK(hipEventCreateWithFlags(&exchanged, hipEventDisableTiming));
+  HIP_OK(hipMemsetAsync(dq5, 0x5A, n, st));
+  FP8BQ_OK_(fp8bq_row_shards_begin(rsh, 2, bm, bn, nullptr, 0, maxima, st));
+  HIP_OK(hipStreamWaitEvent(side, maxima, 0));
+  if (bots[0] > 0 && tops[1] > 0) {  // the first shard's last rows share a tile row with the second's first
+    std::vector<float> a(TN), b(TN);
+    HIP_OK(hipMemcpyAsync(a.data(), rsh[0].bottom_amax, 4 * TN, hipMemcpyDeviceToHost, side));
+    HIP_OK(hipMemcpyAsync(b.data(), rsh[1].top_amax, 4 * TN, hipMemcpyDeviceToHost, side));
+    HIP_OK(hipStreamSynchronize(side));
+    for (int64_t j = 0; j < TN; ++j) a[j] = std::max(a[j], b[j]);
+    HIP_OK(hipMemcpyAsync(rsh[0].bottom_amax, a.data(), 4 * TN, hipMemcpyHostToDevice, side));
+    HIP_OK(hipMemcpyAsync(rsh[1].top_amax, a.data(), 4 * TN, hipMemcpyHostToDevice, side));
+    HIP_OK(hipStreamSynchronize(side));
+  }
+  HIP_OK(hipEventRecord(exchanged, side));
+  HIP_OK(hipStreamWaitEvent(st, exchanged, 0));
+  FP8BQ_OK_(fp8bq_row_shards_finish(rsh, 2, bm, bn, st));
+  HIP_OK(hipStreamSynchronize(st));
+  std::vector<uint8_t> q5(n);
+  HIP_OK(hipMemcpy(q5.data(), dq5, n, hipMemcpyDeviceToHost));
+  if (std::memcmp(q5.data(), q.data(), n) != 0) {
+    std::fprintf(stderr, "row shards cut at %lld differ from the direct call\n", static_cast<long long>(cut));
+    return 7;
+  }
+  for (int k = 0; k < 2; ++k) {
+    std::vector<float> s5(static_cast<size_t>(tml[k] * TN));
+    HIP_OK(hipMemcpy(s5.data(), ds5[k], 4 * s5.size(), hipMemcpyDeviceToHost));
+    if (std::memcmp(s5.data(), s.data() + (r0s[k] / bm) * TN, 4 * s5.size()) != 0) {
+      std::fprintf(stderr, "row shard %d's scales differ from the direct call's\n", k);
+      return 7;
+    }
+  }
+  HIP_OK(hipEventDestroy(maxima));
+  HIP_OK(hipEventDestroy(exchanged));
+  HIP_OK(hipStreamDestroy(side));
+  HIP_OK(hipFree(dq5));
+  HIP_OK(hipFree(ds5[0]));
+  HIP_OK(hipFree(ds5[1]));
+
   const std::string prefix = argv[6];
   if (!write_file((prefix + ".q").c_str(), q.data(), n) ||
       !write_file((prefix + ".s").c_str(), s.data(), 4 * ns) ||
@@ -176,7 +244,7 @@ int main(int argc, char** argv) {
   HIP_OK(hipFree(ds2));
   HIP_OK(hipFree(ddeq));
   HIP_OK(hipFree(ddeq2));
-  std::printf("gpu client ok: %lldx%lld at [%d,%d], graph replays and no-alloc entries equal\n",
+  std::printf("gpu client ok: %lldx%lld at [%d,%d], graph replays, no-alloc entries and row shards equal\n",
               static_cast<long long>(M), static_cast<long long>(N), bm, bn);
   return 0;
 }

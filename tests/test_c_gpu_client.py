@@ -1,8 +1,10 @@
 """The library from a native C++ program on the GPU, with no Python in the
 process (tests/c/gpu_client.cpp): a direct quantize, a grouped call captured
 in a HIP graph and replayed, two grouped calls of the entry point that
-allocates nothing (over 512 entries), and a dequantization, checked here
-against the CPU oracle.  The client is host code only and builds with g++ in seconds."""
+allocates nothing (over 512 entries), two row shards whose shared tile row's
+maxima are exchanged on a second stream between the two row-shard calls,
+and a dequantization, checked here against the CPU oracle.  The client is
+host code only and builds with g++ in seconds."""
 
 import os
 import shutil
