@@ -338,6 +338,17 @@ def main():
             for x, sp in zip(xs, specs):
                 log(f"input sha256 {sp.name} {sp.M}x{sp.N} {tensor_sha256(x)}")
 
+    # the shard and stream operations time their own calls on the inputs alone
+    if args.op == "shard":
+        time_shard(lib, keep, groups, bm, bn, args, stream, sptr, desc)
+        return
+    if args.op == "shard-rows":
+        time_row_shards(lib, keep, groups, bm, bn, args, sptr, desc)
+        return
+    if args.op == "stream":
+        time_stream(keep, groups, bm, bn, args, desc)
+        return
+
     ms_per_step, ev_ms = prep.time(args.steps, args.warmup, stream)
     launches = prep.launches
     mean_launch_ms = sum(ev_ms) / len(ev_ms) / launches
@@ -357,15 +368,6 @@ def main():
         torch.cuda.synchronize()
         log("calibration copy: 3 x 1 GiB device-to-device")
 
-    if args.op == "stream":
-        time_stream(keep, groups, bm, bn, args, desc)
-        return
-    if args.op == "shard":
-        time_shard(lib, keep, groups, bm, bn, args, stream, sptr, desc)
-        return
-    if args.op == "shard-rows":
-        time_row_shards(lib, keep, groups, bm, bn, args, sptr, desc)
-        return
     if args.op != "quantize":
         time_dequant(lib, keep, groups, bm, bn, args, stream, sptr, desc)
         return

@@ -1871,9 +1871,51 @@ __device__ __forceinline__ void shard_wide_quant(const Big& b, int64_t ti, int64
   if (wave == 0 && (lane & 15) == 0) ((FP8BQ_GLOBAL float*)out)[tile0 + sub] = s;
 }
 
+// The same unit when some of its 128 rows lie outside the shard (the first
+// or last local tile row of a shard at a row phase, or of a shard shorter
+// than a tile row) but its 512 columns lie inside: rows outside [0, M) are
+// neither read nor written, and the four given maxima scale the others.
+// Edge slabs of row shards (64 of 128 rows at phase 64) went from one tile
+// at a time to this body.
+__device__ __forceinline__ void shard_wide_quant_rows(const Big& b, int64_t ti, int64_t g,
+                                                      const float* amax, float* out,
+                                                      uint32_t* red) {
+  constexpr int L = 32;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int sub = lane >> 4;
+  const int64_t N = b.N;
+  const int64_t r0 = ti * 128 - b.row_phase;
+  const int64_t col = g * 512 - b.col_phase + lane * 8;
+  const int64_t tile0 = ti * b.TNl + g * 4;
+  if (t < 4) red[8 + t] = __float_as_uint(((const FP8BQ_GLOBAL float*)amax)[tile0 + t]);
+  u32x4 v[L];
+#pragma unroll
+  for (int k = 0; k < L; ++k) {
+    const int64_t row = r0 + wave + 4 * k;
+    v[k] = u32x4{0u, 0u, 0u, 0u};
+    if (row >= 0 && row < b.M) {
+      v[k] = __builtin_nontemporal_load((const FP8BQ_GLOBAL u32x4*)(b.x + row * N + col));
+    }
+  }
+  __syncthreads();
+  float s, r;
+  tile_scale_f(__uint_as_float(red[8 + sub]), s, r);
+#pragma unroll
+  for (int k = 0; k < L; ++k) {
+    const int64_t row = r0 + wave + 4 * k;
+    if (row >= 0 && row < b.M) {
+      __builtin_nontemporal_store(quant8(v[k], r), (FP8BQ_GLOBAL u32x2*)(b.q + row * N + col));
+    }
+  }
+  if (wave == 0 && (lane & 15) == 0) ((FP8BQ_GLOBAL float*)out)[tile0 + sub] = s;
+}
+
 // Quantize pass of grouped [128,128] shards in four-tile units: unit (ti, g)
 // covers local tiles (ti, 4g..4g+3); units whose four tiles lie whole inside
-// the shard take shard_wide_quant, the others their tiles one by one.  At 2
+// the shard take shard_wide_quant, units whose columns do take
+// shard_wide_quant_rows, the others their tiles one by one.  At 2
 // workgroups per CU, against one tile per workgroup at 4: the 151937x4096
 // shard at phase (64, 0) 77.0% -> 78.5% of peak, at (0, 64) 65.5% -> 72.9%,
 // 70 dense-set shards at (64, 0) 76.9% -> 79.0% (3 per CU: 77.2 / 70.5 / 77.9%).
@@ -1909,6 +1951,8 @@ __global__ __launch_bounds__(kThreads) void shard_group_wide(const ShardGroupArg
     const int64_t c0 = g * 512 - b.col_phase;
     if (r0 >= 0 && r0 + 128 <= b.M && c0 >= 0 && c0 + 512 <= b.N) {
       shard_wide_quant(b, ti, g, en.amax, en.out, red);
+    } else if (c0 >= 0 && c0 + 512 <= b.N) {
+      shard_wide_quant_rows(b, ti, g, en.amax, en.out, red);
     } else {
       for (int64_t tj = g * 4; tj < g * 4 + 4 && tj < b.TNl; ++tj) {
         if (tj > g * 4) __syncthreads();  // red[] of the previous tile is read
