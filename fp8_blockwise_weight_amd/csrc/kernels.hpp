@@ -1787,7 +1787,7 @@ __global__ __launch_bounds__(kThreads) void quantize_group_args(const GroupArgs<
 // unit start[e] is the largest <= u (units: local tiles, or 64-row units
 // for one-row tiles).
 
-constexpr int kShardArgsMax = 256;
+constexpr int kShardArgsMax = 512;
 
 struct ShardEntry {
   const uint16_t* x;

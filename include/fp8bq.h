@@ -229,7 +229,7 @@ typedef struct fp8bq_shard {
  * Every entry is checked as the single call checks it before anything is
  * enqueued.  Entries whose tiles hold at most 16,384 elements, with tile
  * columns on 8-element boundaries (x 16-byte and q 8-byte aligned; N, bn and
- * col_phase multiples of 8), share launches of up to 256 entries with the
+ * col_phase multiples of 8), share launches of up to 512 entries with the
  * table in the kernel arguments (graph-capturable, no workspace); other
  * entries take their own two-pass launches.  Outputs of different entries
  * must not overlap each other or any entry's x (not checked across entries).

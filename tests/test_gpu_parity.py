@@ -794,7 +794,7 @@ def test_shard_many_four_tile_units(gpu_lib):
 
 @pytest.mark.parametrize("block", [(128, 128), (64, 64), (1, 128), (32, 96)])
 def test_shard_many_matches_single_calls(gpu_lib, block):
-    """Grouped shard calls over 300 shards (more than one 256-entry launch)
+    """Grouped shard calls over 600 shards (more than one 512-entry launch)
     mixing small aligned tiles with entries that take their own launches
     (N % 8 != 0, a misaligned x, odd column phases) and empty shards: every
     maximum, code and scale equals the single calls' and the oracle's; maxima
@@ -805,7 +805,7 @@ def test_shard_many_matches_single_calls(gpu_lib, block):
     g = torch.Generator(device=DEV).manual_seed(53)
     rng = np.random.default_rng(53)
     xs, phases = [], []
-    for i in range(300):
+    for i in range(600):
         M = int(rng.integers(0 if i % 97 == 0 else 1, 300))
         N = int(rng.choice([8, 64, 128, 136, 256, 520, 77]))
         cp = 8 * int(rng.integers(max(1, bn // 8))) if i % 5 else int(rng.integers(bn))

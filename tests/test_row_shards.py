@@ -159,3 +159,68 @@ def test_row_shards_many_and_side_stream(gpu_lib):
     assert torch.equal(q, q_ref.view(torch.uint8))
     assert torch.equal(s.view(torch.int32), s_ref.view(torch.int32))
     assert_matches_oracle(x, q_ref, s_ref, bm, bn, "600 row shards")
+
+
+@pytest.mark.gpu
+def test_row_shards_graph_capture(gpu_lib):
+    """fp8bq_row_shards_begin, a max-exchange in torch and
+    fp8bq_row_shards_finish captured in one HIP graph over 600 row shards
+    (the whole-tile parts take launches with the table in the kernel
+    arguments under capture): every replay, with the input rescaled eagerly
+    in between, equals the eager whole-matrix quantization."""
+    import ctypes
+
+    bm, bn = 128, 128
+    M, N = 600 * 150, 256
+    g = torch.Generator(device=DEV).manual_seed(17)
+    rng = np.random.default_rng(17)
+    x = (torch.randn((M, N), generator=g, device=DEV) * 0.03).to(torch.bfloat16)
+    spans = _cut(M, [int(c) for c in rng.integers(1, M, 599)])
+    n = len(spans)
+    table = (fq.RowShardEntry * n)()
+    outs, edges = [], []
+    for e, (r0, rows) in zip(table, spans):
+        rp = r0 % bm
+        TMl, TN = fq.local_grid(rows, N, bm, bn, (rp, 0))
+        top, bottom = fq.row_shard_edges(rows, bm, rp)
+        q = torch.empty((rows, N), dtype=torch.uint8, device=DEV)
+        s = torch.empty((TMl, TN), dtype=torch.float32, device=DEV)
+        e.x, e.q, e.scale_inv, e.M, e.N, e.row_phase = x[r0].data_ptr(), q.data_ptr(), s.data_ptr(), rows, N, rp
+        e.top_amax = s[0].data_ptr() if top else None
+        e.bottom_amax = s[TMl - 1].data_ptr() if bottom else None
+        outs.append((q, s))
+        edges.append((s[0] if top else None, s[TMl - 1] if bottom else None))
+    lib = gpu_lib.load_library()
+    need = int(lib.fp8bq_many_workspace_bytes(n))
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    exchange = _exchange(spans, bm)
+
+    def calls():
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        assert lib.fp8bq_row_shards_begin(table, n, bm, bn, ws.data_ptr(), need, None, st) == 0
+        exchange(edges)
+        assert lib.fp8bq_row_shards_finish(table, n, bm, bn, st) == 0
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()                                            # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        print("row-shard graph replay", rep, flush=True)
+        x.mul_(2.0 if rep % 2 else 0.5)                    # exact: powers of two
+        for q, s in outs:
+            q.fill_(0xA5)
+            s.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        q_ref, s_ref = fq.quantize(x, (bm, bn))
+        q, s = _assemble(x, [(q.view(torch.float8_e4m3fn), s) for q, s in outs], spans, bm, bn)
+        assert torch.equal(q, q_ref.view(torch.uint8)), rep
+        assert torch.equal(s.view(torch.int32), s_ref.view(torch.int32)), rep
