@@ -105,6 +105,29 @@ def test_bench_row_shard_mode(gpu_lib):
     assert 0 < rec["pct_of_hbm_peak_algorithmic"] < 100
 
 
+@pytest.mark.gpu
+def test_bench_stream_mode(gpu_lib):
+    """--op stream on one dense layer: every weight and the norms in model
+    order through quant_weights; the record counts the pairs in and out
+    (two out per FP8 weight) and the weights' algorithmic bytes."""
+    print("bench.py --workload dense-layer --op stream", flush=True)
+    res = subprocess.run([sys.executable, BENCH, "--workload", "dense-layer", "--op", "stream",
+                          "--steps", "2", "--warmup", "1", "--no-cpu-baseline"],
+                         capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert res.returncode == 0, res.stderr[-2000:]
+    rec = json.loads(res.stdout.strip().splitlines()[-1])
+    assert rec["op"] == "stream"
+    sys.path.insert(0, ROOT)
+    from fp8_blockwise_weight_amd import workloads as wl
+
+    specs = wl.c2()
+    n_fp8 = len(specs)
+    assert rec["pairs_out"] == rec["pairs_in"] + n_fp8
+    assert rec["bytes_per_step"] == sum(3 * sp.M * sp.N + 4 * (-(-sp.M // 128)) * (-(-sp.N // 128))
+                                        for sp in specs)
+    assert 0 < rec["pct_of_hbm_peak"] < 100
+
+
 def test_kernel_fingerprint_ignores_comments_only():
     """The counter record is tied to the kernels' code: comment and layout
     edits keep the fingerprint, code edits change it."""
