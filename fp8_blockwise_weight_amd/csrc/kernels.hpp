@@ -1917,7 +1917,10 @@ __device__ __forceinline__ void shard_wide_quant_rows(const Big& b, int64_t ti, 
 // Quantize pass of grouped [128,128] shards in four-tile units: unit (ti, g)
 // covers local tiles (ti, 4g..4g+3); units whose four tiles lie whole inside
 // the shard take shard_wide_quant, units whose columns do take
-// shard_wide_quant_rows, the others their tiles one by one.  At 2
+// shard_wide_quant_rows, the others their tiles one by one.  The maxima pass
+// keeps one tile per unit even for shards one tile row deep: the same
+// four-tile units with rows masked measured slower there (MoE row shards
+// 68.3% -> 67.7%, dense set unchanged).  At 2
 // workgroups per CU, against one tile per workgroup at 4: the 151937x4096
 // shard at phase (64, 0) 77.0% -> 78.5% of peak, at (0, 64) 65.5% -> 72.9%,
 // 70 dense-set shards at (64, 0) 76.9% -> 79.0% (3 per CU: 77.2 / 70.5 / 77.9%).
