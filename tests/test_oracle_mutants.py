@@ -193,6 +193,25 @@ def m_phase_ignored(mp):
     mp.setattr(oracle, "tile_amax", ta)
 
 
+def m_reciprocal_not_rounded(mp):
+    """The reciprocal 1/s kept in float64 instead of rounded to float32."""
+    def scalar(amax, eps=oracle.EPS):
+        a = max(amax, fl32(eps))
+        s = fl32(a / 448.0)
+        return s, 1.0 / s
+
+    def vector(amax, eps=oracle.EPS):
+        a = np.maximum(amax, fl32(eps))
+        s = (a / 448.0).astype(np.float32).astype(np.float64)
+        return s, 1.0 / s
+    _patch_scales(mp, scalar, vector)
+
+
+def m_grid_floor(mp):
+    """Tile counts rounded down: a ragged last tile row or column is dropped."""
+    mp.setattr(blockwise, "tile_grid", lambda M, N, bm, bn: (M // bm, N // bn))
+
+
 MUTANTS = [
     m_single_division,
     m_no_eps_floor,
@@ -208,6 +227,8 @@ MUTANTS = [
     m_dequant_divides,
     m_bf16_truncates,
     m_phase_ignored,
+    m_reciprocal_not_rounded,
+    m_grid_floor,
 ]
 
 
