@@ -93,8 +93,12 @@ def _cut(M, cuts):
     return [(a, b - a) for a, b in zip(bounds, bounds[1:])]
 
 
+# the last three: rows not 16-byte aligned (N % 8 != 0) and tile columns off
+# 8-element boundaries, so edges and whole tile rows take the element-wise
+# and two-pass kernels
 CASES = [(1000, 3000, (128, 128)), (1536, 2048, (128, 128)), (4097, 1024, (64, 64)),
-         (300, 640, (1, 128)), (777, 520, (32, 96)), (99, 37, (5, 3)), (3000, 2000, (1024, 1024))]
+         (300, 640, (1, 128)), (777, 520, (32, 96)), (99, 37, (5, 3)), (3000, 2000, (1024, 1024)),
+         (300, 77, (16, 16)), (500, 1000, (100, 100)), (700, 1200, (256, 300))]
 
 
 @pytest.mark.gpu
